@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA forward hot path on one MI355X.
+
+Headline: the Kimi K2-shaped MLA prefill (B=1, T=2048, d=7168, 64 heads,
+q latent 1536, kv latent 512, 128+64 query/key and 128 value widths, causal,
+bf16 with fp32 softmax/accumulation), reported as algorithmic TFLOP/s of the
+whole step and, for the dominant kernel, against the bf16 MFMA peak.
+
+One step = one mla_prefill call (down-projections + norms + RoPE, up-
+projections, flash attention, o_proj) on inputs already resident in HBM.
+Secondary lines (same JSON object, key "secondary") time the full-cache
+decode (B=64, P=1000), the absorbed latent-cache decode (B=32, P=8192) and
+the dense block (B=1, T=4096) with the same weights, against the HBM or MFMA
+roofline.  The CPU baseline times the float32 oracle on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+KIMI = dict(d_model=7168, n_heads=64, q_lora_rank=1536, kv_lora_rank=512, qk_nope_dim=128,
+            qk_rope_dim=64, v_head_dim=128, d_ff=18432)
+
+
+def prefill_kernel_flops(B, T, k=KIMI):
+    """Algorithmic FLOPs per launch of each prefill kernel (2 per multiply-add;
+    attention counts only the visible (causal) query/key pairs)."""
+    M = B * T
+    H = k["n_heads"]
+    dqk = k["qk_nope_dim"] + k["qk_rope_dim"]
+    n1 = k["q_lora_rank"] + k["kv_lora_rank"] + k["qk_rope_dim"]
+    return {
+        "gemm_down": 2.0 * M * n1 * k["d_model"],
+        "gemm_q_up_rope": 2.0 * M * H * dqk * k["q_lora_rank"],
+        "gemm_kv_up": 2.0 * M * H * (k["qk_nope_dim"] + k["v_head_dim"]) * k["kv_lora_rank"],
+        "flash_prefill": 2.0 * H * B * (T * (T + 1) / 2) * (dqk + k["v_head_dim"]),
+        "gemm_o_proj": 2.0 * M * k["d_model"] * H * k["v_head_dim"],
+    }
+
+
+def mla_param_count(k=KIMI):
+    H = k["n_heads"]
+    dqk = k["qk_nope_dim"] + k["qk_rope_dim"]
+    return (k["q_lora_rank"] * k["d_model"] + k["q_lora_rank"] + H * dqk * k["q_lora_rank"]
+            + (k["kv_lora_rank"] + k["qk_rope_dim"]) * k["d_model"] + k["kv_lora_rank"]
+            + H * (k["qk_nope_dim"] + k["v_head_dim"]) * k["kv_lora_rank"]
+            + k["d_model"] * H * k["v_head_dim"])
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_weights(torch, dev, k, seed):
+    """Synthetic N(0, 0.02^2) weights with unit gains, drawn on the device."""
+    import head_latent_attention_fwd_amd as mla
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    d = mla.make_dims(k["d_model"], k["n_heads"], k["q_lora_rank"], k["kv_lora_rank"],
+                      k["qk_nope_dim"], k["qk_rope_dim"], k["v_head_dim"], d_ff=k["d_ff"],
+                      dtype="bf16")
+    w = {}
+    for name, shape in mla.weight_shapes(d).items():
+        if name.startswith("g_"):
+            w[name] = torch.ones(shape, dtype=torch.bfloat16, device=dev)
+        else:
+            w[name] = (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    return d, w, g
+
+
+def timed(torch, fn, steps, warmup, flush=None):
+    """Warm up, then time `steps` calls with HIP events on the current stream
+    (per-step events when a cache flush runs between steps)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    if flush is None:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record(st)
+        for _ in range(steps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return a.elapsed_time(b) / steps, wall
+    tot = 0.0
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        tot += a.elapsed_time(b)
+    return tot / steps, time.perf_counter() - t0
+
+
+def kernel_table(mla, steps):
+    prof = mla.mla_profile_summary()
+    return {n: {"launches": c, "avg_ms": ms / c} for n, (c, ms) in prof.items()}
+
+
+def bench_prefill(torch, mla, dev, steps, warmup, k=KIMI, B=1, T=2048):
+    d, w, g = make_weights(torch, dev, k, 1002)
+    x = torch.randn(B, T, k["d_model"], generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    rope = mla.mla_rope_table(T, k["qk_rope_dim"], 10000.0, dev)
+    out = torch.empty_like(x)
+    ws = torch.empty(mla.prefill_workspace_size(d, B, T), dtype=torch.uint8, device=dev)
+    fn = lambda: mla.mla_prefill(d, w, x, rope, out=out, workspace=ws)  # noqa: E731
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    mla.mla_profile_summary()                  # drop anything recorded so far
+    mla.mla_profile_enable(True)
+    ms, wall = timed(torch, fn, steps, 0)
+    mla.mla_profile_enable(False)
+    kern = kernel_table(mla, steps)
+    flops = prefill_kernel_flops(B, T, k)
+    for n, v in kern.items():
+        if n in flops:
+            v["gflop"] = flops[n] / 1e9
+            v["tflops"] = flops[n] / (v["avg_ms"] * 1e-3) / 1e12
+    total = sum(flops.values())
+    return {"ms": ms, "wall_s": wall, "flops": total, "kernels": kern, "w": w, "d": d}
+
+
+def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000):
+    k = KIMI
+    L_cap = P + 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(1003)
+    H = k["n_heads"]
+    kc = torch.randn(B, H, L_cap, 192, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    vc = torch.randn(B, H, L_cap, 128, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    x = torch.randn(B, k["d_model"], generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    rope = mla.mla_rope_table(L_cap, 64, 10000.0, dev)
+    out = torch.empty_like(x)
+    ws = torch.empty(mla.decode_workspace_size(d, B, L_cap), dtype=torch.uint8, device=dev)
+    fn = lambda: mla.mla_decode_fullcache(d, w, x, P, kc, vc, rope, out=out, workspace=ws)  # noqa: E731
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    mla.mla_profile_summary()
+    mla.mla_profile_enable(True)
+    ms, _ = timed(torch, fn, steps, 0, flush)
+    mla.mla_profile_enable(False)
+    kern = kernel_table(mla, steps)
+    L = P + 1
+    cache_bytes = B * H * L * (192 + 128) * 2
+    nbytes = cache_bytes + mla_param_count() * 2 + B * H * 320 * 2 + 2 * B * k["d_model"] * 2
+    if "decode_full" in kern:
+        kern["decode_full"]["gbs"] = cache_bytes / (kern["decode_full"]["avg_ms"] * 1e-3) / 1e9
+    del kc, vc
+    return {"workload": f"MLA decode, full cache, bf16, B={B}, P={P} (L={L} keys)",
+            "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3),
+            "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None}
+
+
+def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=8192):
+    k = KIMI
+    L_cap = P + 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(1004)
+    cc = torch.randn(B, L_cap, 576, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    x = torch.randn(B, k["d_model"], generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    rope = mla.mla_rope_table(L_cap, 64, 10000.0, dev)
+    out = torch.empty_like(x)
+    ws = torch.empty(mla.decode_workspace_size(d, B, L_cap), dtype=torch.uint8, device=dev)
+    fn = lambda: mla.mla_decode_latentcache(d, w, x, P, cc, rope, out=out, workspace=ws)  # noqa: E731
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    mla.mla_profile_summary()
+    mla.mla_profile_enable(True)
+    ms, _ = timed(torch, fn, steps, 0, flush)
+    mla.mla_profile_enable(False)
+    kern = kernel_table(mla, steps)
+    L = P + 1
+    cache_bytes = B * L * 576 * 2
+    nbytes = cache_bytes + mla_param_count() * 2 + B * 576 * 2 + 2 * B * k["d_model"] * 2
+    if "decode_latent" in kern:
+        kern["decode_latent"]["gbs"] = cache_bytes / (kern["decode_latent"]["avg_ms"] * 1e-3) / 1e9
+    return {"workload": f"MLA decode, absorbed latent cache, bf16, B={B}, P={P} (L={L} keys)",
+            "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3),
+            "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None}
+
+
+def bench_block(torch, mla, dev, d, w, steps, warmup, B=1, T=4096):
+    k = KIMI
+    g = torch.Generator(device=dev)
+    g.manual_seed(1005)
+    F, D = k["d_ff"], k["d_model"]
+    blk = {"g_attn": torch.ones(D, dtype=torch.bfloat16, device=dev),
+           "g_ffn": torch.ones(D, dtype=torch.bfloat16, device=dev)}
+    for n, shp in (("w1", (F, D)), ("w3", (F, D)), ("w2", (D, F))):
+        blk[n] = (torch.randn(shp, generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    x = torch.randn(B, T, D, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    rope = mla.mla_rope_table(T, 64, 10000.0, dev)
+    out = torch.empty_like(x)
+    ws = torch.empty(mla.block_workspace_size(d, B, T), dtype=torch.uint8, device=dev)
+    fn = lambda: mla.dense_block_fwd(d, w, blk, x, rope, out=out, workspace=ws)  # noqa: E731
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    mla.mla_profile_summary()
+    mla.mla_profile_enable(True)
+    ms, _ = timed(torch, fn, steps, 0)
+    mla.mla_profile_enable(False)
+    kern = kernel_table(mla, steps)
+    fl = prefill_kernel_flops(B, T)
+    flops = sum(fl.values()) + 2.0 * B * T * D * F * 3
+    fl["gemm_swiglu"] = 2.0 * B * T * D * F * 2
+    fl["gemm_w2_resid"] = 2.0 * B * T * D * F
+    for n, v in kern.items():
+        if n in fl:
+            v["tflops"] = fl[n] / (v["avg_ms"] * 1e-3) / 1e12
+    return {"workload": f"dense block (RMSNorm, MLA, residual, RMSNorm, SwiGLU 18432, residual), bf16, B={B}, T={T}",
+            "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, "gflop": flops / 1e9,
+            "kernels": kern}
+
+
+def cpu_baseline(k=KIMI, B=1, T=2048):
+    """The float32 oracle on the host cores, on the headline workload."""
+    import numpy as np
+    from oracle import mla_ref as ref
+    from tests import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 0) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:  # threadpoolctl missing: report the visible cores
+        threads = os.cpu_count() or 1
+    dims = ref.KIMI_K2
+    x, w = synth.prefill_inputs(dims, B, T, 1002, bf16=True)
+    mw = ref.MLAWeights(**w)
+    t0 = time.perf_counter()
+    ref.mla_prefill(dims, mw, x, dtype=np.float32)
+    dt = time.perf_counter() - t0
+    flops = sum(prefill_kernel_flops(B, T, k).values())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"one whole step of the headline workload (B={B}, T={T}) by the NumPy oracle in float32"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode_full", "decode_latent", "block"])
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_latent_attention_fwd_amd as mla
+    mla.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def flush():
+        flush_buf.fill_(1)   # 1 GiB write evicts the 256 MB Infinity Cache
+
+    if args.only and args.only != "prefill":
+        d, w, _ = make_weights(torch, dev, KIMI, 1002)
+        fn = {"decode_full": lambda: bench_decode_full(torch, mla, dev, d, w, args.steps, args.warmup, flush),
+              "decode_latent": lambda: bench_decode_latent(torch, mla, dev, d, w, args.steps, args.warmup, flush),
+              "block": lambda: bench_block(torch, mla, dev, d, w, args.steps, args.warmup)}[args.only]
+        print(json.dumps(fn()))
+        return
+
+    log(f"[bench] prefill B=1 T=2048 steps={args.steps} warmup={args.warmup}")
+    r = bench_prefill(torch, mla, dev, args.steps, args.warmup)
+    kern = r["kernels"]
+    gemmlike = {n: v for n, v in kern.items() if "tflops" in v}
+    dom = max(gemmlike, key=lambda n: gemmlike[n]["avg_ms"])
+    dv = gemmlike[dom]
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": dv["tflops"], "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": dv["tflops"] / MFMA_BF16_PEAK_TFS, "traffic": None,
+                "avg_ms": dv["avg_ms"], "gflop_per_launch": dv["gflop"]}
+    value = r["flops"] / (r["ms"] * 1e-3) / 1e12
+    line = {
+        "metric": "MLA prefill TFLOP/s (% MFMA peak); decode tokens/s & HBM GB/s (% peak)",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (N(0,1) activations, N(0,0.02^2) weights, unit gains)",
+        "config": {"workload": "Kimi K2-shaped MLA prefill, bf16 (fp32 softmax/accumulate), causal",
+                   "global_batch": 1, "seq_len": 2048, "d_model": 7168, "heads": 64,
+                   "q_lora": 1536, "kv_lora": 512, "qk_dims": "128 nope + 64 rope", "v_dim": 128,
+                   "parallelism": "none (1 GPU)"},
+        "mfma_frac_step": value / MFMA_BF16_PEAK_TFS,
+        "roofline": roofline,
+        "kernels": kern,
+    }
+    if not args.no_secondary:
+        sec = {}
+        for name, fn in (("decode_fullcache", lambda: bench_decode_full(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
+                         ("decode_latentcache", lambda: bench_decode_latent(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
+                         ("dense_block", lambda: bench_block(torch, mla, dev, r["d"], r["w"], max(3, args.steps // 4), 2))):
+            log(f"[bench] {name}")
+            try:
+                sec[name] = fn()
+            except Exception as e:  # a secondary failure must not hide the headline
+                sec[name] = {"error": repr(e)}
+            torch.cuda.empty_cache()
+        line["secondary"] = sec
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle, float32)")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

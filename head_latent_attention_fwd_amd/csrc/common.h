@@ -1,0 +1,66 @@
+// Device-side helpers shared by the gfx950 kernels of the MLA library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bfloat16 storage (upper half of an fp32 word)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define MLA_DEV __device__ __forceinline__
+
+MLA_DEV float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even float -> bf16 (NaN stays NaN).
+MLA_DEV bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Two floats -> packed bf16 pair (lo in bits 0..15).
+MLA_DEV uint32_t pack2bf(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+MLA_DEV float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+MLA_DEV float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Generic element conversion used by the kernels templated on storage type.
+template <typename T> MLA_DEV float to_f(T v);
+template <> MLA_DEV float to_f<float>(float v) { return v; }
+template <> MLA_DEV float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+template <typename T> MLA_DEV T from_f(float v);
+template <> MLA_DEV float from_f<float>(float v) { return v; }
+template <> MLA_DEV bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+MLA_DEV float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+MLA_DEV float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Logical block index -> block index remapped so that consecutive logical
+// ids land on the same XCD.  The dispatcher hands workgroup b to XCD b % 8,
+// so logical tile ranges [start_x, start_x + count_x) are assigned to XCD x.
+MLA_DEV int xcd_remap(int b, int nblocks) {
+  const int nx = 8;
+  int x = b % nx, slot = b / nx;
+  int base = nblocks / nx, rem = nblocks % nx;
+  int start = x * base + (x < rem ? x : rem);
+  return start + slot;
+}
+
+#define MLA_LDS __attribute__((address_space(3)))

@@ -1,0 +1,213 @@
+// Causal flash attention for the MLA prefill, bf16 with fp32 softmax, gfx950.
+//
+// What it computes ("Kimi K2 · Mix and project", code excerpt, and the
+// query/key assembly of "Kimi K2 · Dense transformer block"): for every
+// sequence b, head h and query i, scores s_ij = scale * [Q^C ; Q^R]_i .
+// [K^C_h ; k^R]_j over keys j <= i, a float32 softmax over j, and
+// O_i = sum_j p_ij V_h,j, written straight into the head-merged layout
+// [B*T, H*128] (column h*128 + c) that o_proj reads.
+//
+// Design (CDNA4):
+//  * 256 threads, 4 waves, 128 queries per workgroup (32 per wave), key
+//    tiles of 64.  Scores are formed transposed, S^T = K . Q^T, with
+//    v_mfma_f32_32x32x16_bf16: K rows are the A operand (K-contiguous rows in
+//    LDS) and the wave's queries are the B operand, held in registers for the
+//    whole loop.  Each lane then owns one query column, so the softmax
+//    statistics are lane-local (plus one cross-half shuffle).
+//  * O^T = V^T . P^T reuses the score accumulator directly as the B operand
+//    (8 consecutive accumulator values = 8 keys of one query).  V^T is the A
+//    operand: V tiles are stored transposed in LDS, with keys permuted inside
+//    each group of 16 so that a lane's 8 keys are one 16-byte read.
+//  * The shared rotary key k^R is loaded once per key into the 64 rotary
+//    columns of the K tile (never replicated per head in memory).
+//  * Two LDS stages (K 24 KB + V^T 16 KB each): the next tile's global loads
+//    are in flight during the MFMAs.  Query tiles are issued longest-first;
+//    heads map to XCD h % 8, so all query tiles of a head share one L2.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+constexpr int KCH = 24;  // 16-byte chunks per K row (192 bf16)
+
+MLA_DEV int kphys(int c, int row) { return (c & ~7) | ((c ^ row) & 7); }
+
+// position of key offset k (0..63) inside a V^T row (see header comment)
+MLA_DEV int vpos(int k) {
+  int g16 = k >> 4, kk = k & 15;
+  return g16 * 16 + 8 * ((kk >> 2) & 1) + 4 * (kk >> 3) + (kk & 3);
+}
+}  // namespace
+
+__global__ __launch_bounds__(256) void flash_prefill_kernel(FlashParams p) {
+  __shared__ u32x4 Ks[2][64 * KCH];
+  __shared__ u32x4 Vt[2][128 * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int nqt = (p.T + 127) / 128;
+  const int HB = p.H * p.B;
+  const int qt = nqt - 1 - (int)(blockIdx.x / HB);
+  const int rem = blockIdx.x % HB;
+  const int h = rem % p.H, b = rem / p.H;
+  const int q0 = qt * 128;
+  const long rowbase = (long)b * p.T;
+  const long HS = p.H;
+
+  // this wave's queries as MFMA B fragments: features 16 s + 8 lg .. +8
+  bf16x8 qf[12];
+  {
+    const int qrow = min(q0 + 32 * w + lr, p.T - 1);
+    const bf16_t* qp = p.q + ((rowbase + qrow) * HS + h) * 192 + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 12; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 16 * s));
+  }
+
+  const int qlast = min(q0 + 127, p.T - 1);
+  const int n_kv = qlast / 64 + 1;
+
+  u32x4 rk[6], rv[4];
+#define FP_LOAD(kv0)                                                                      \
+  do {                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < 6; ++i) {                                       \
+      const int e = tid + 256 * i, row = e / KCH, c = e % KCH;                            \
+      const long key = rowbase + min((kv0) + row, p.T - 1);                               \
+      const bf16_t* src = c < 16 ? p.kv + (key * HS + h) * 256 + 8 * c                    \
+                                 : p.kr + key * 64 + 8 * (c - 16);                        \
+      rk[i] = *(const u32x4*)src;                                                         \
+    }                                                                                     \
+    _Pragma("unroll") for (int it = 0; it < 2; ++it) {                                    \
+      const int kp = tid & 31, c = (tid >> 5) + 8 * it;                                   \
+      const long k0 = rowbase + min((kv0) + 2 * kp, p.T - 1);                             \
+      const long k1 = rowbase + min((kv0) + 2 * kp + 1, p.T - 1);                         \
+      rv[2 * it] = *(const u32x4*)(p.kv + (k0 * HS + h) * 256 + 128 + 8 * c);             \
+      rv[2 * it + 1] = *(const u32x4*)(p.kv + (k1 * HS + h) * 256 + 128 + 8 * c);         \
+    }                                                                                     \
+  } while (0)
+#define FP_STORE(buf)                                                                     \
+  do {                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < 6; ++i) {                                       \
+      const int e = tid + 256 * i, row = e / KCH, c = e % KCH;                            \
+      Ks[buf][row * KCH + kphys(c, row)] = rk[i];                                         \
+    }                                                                                     \
+    uint32_t* vt32 = (uint32_t*)&Vt[buf][0];                                              \
+    _Pragma("unroll") for (int it = 0; it < 2; ++it) {                                    \
+      const int kp = tid & 31, c = (tid >> 5) + 8 * it;                                   \
+      const int pos = vpos(2 * kp);                                                       \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
+        const int dv = 8 * c + i;                                                         \
+        const uint32_t w0 = rv[2 * it][i >> 1], w1 = rv[2 * it + 1][i >> 1];              \
+        const uint32_t val = (i & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))                  \
+                                     : ((w0 & 0xffffu) | (w1 << 16));                     \
+        const int ph = (((pos >> 3) ^ (dv & 7)) << 3) | (pos & 7);                        \
+        vt32[(dv * 64 + ph) >> 1] = val;                                                  \
+      }                                                                                   \
+    }                                                                                     \
+  } while (0)
+
+  floatx16 O[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) O[d][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int qi = q0 + 32 * w + lr;
+  const int wq_first = q0 + 32 * w, wq_last = wq_first + 31;
+
+  FP_LOAD(0);
+  FP_STORE(0);
+  __syncthreads();
+  for (int t = 0; t < n_kv; ++t) {
+    const int cur = t & 1, kv0 = t * 64;
+    if (t + 1 < n_kv) FP_LOAD(kv0 + 64);
+    if (kv0 <= wq_last) {  // wave-uniform: some key of the tile is visible
+      floatx16 S[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) S[mb][e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 12; ++s) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int row = 32 * mb + lr;
+          const bf16x8 a = __builtin_bit_cast(bf16x8, Ks[cur][row * KCH + kphys(2 * s + lg, row)]);
+          S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], S[mb], 0, 0, 0);
+        }
+      }
+      const bool diag = kv0 + 63 > wq_first;
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float v = S[mb][e] * p.scale_log2;
+          const int key = kv0 + 32 * mb + 8 * (e >> 2) + 4 * lg + (e & 3);
+          if (diag && key > qi) v = -INFINITY;
+          S[mb][e] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = exp2f(m_run - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float pv = exp2f(S[mb][e] - m_new);
+          S[mb][e] = pv;
+          psum += pv;
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) O[d][e] *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int ih = 0; ih < 2; ++ih) {
+          bf16x8 pf;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) pf[m] = (__bf16)S[mb][8 * ih + m];
+          const int ks = 2 * mb + ih;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const int dv = 32 * d + lr;
+            const bf16x8 a = __builtin_bit_cast(bf16x8, Vt[cur][dv * 8 + ((2 * ks + lg) ^ (dv & 7))]);
+            O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, O[d], 0, 0, 0);
+          }
+        }
+    }
+    if (t + 1 < n_kv) FP_STORE(cur ^ 1);
+    __syncthreads();
+  }
+#undef FP_LOAD
+#undef FP_STORE
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (qi < p.T) {
+    const float inv = 1.f / l_tot;
+    bf16_t* op = p.out + (rowbase + qi) * (HS * 128) + (long)h * 128 + 4 * lg;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 v;
+        v[0] = pack2bf(O[d][4 * i + 0] * inv, O[d][4 * i + 1] * inv);
+        v[1] = pack2bf(O[d][4 * i + 2] * inv, O[d][4 * i + 3] * inv);
+        *(u32x2*)(op + 32 * d + 8 * i) = v;
+      }
+  }
+}
+
+hipError_t flash_prefill_bf16(const FlashParams& p, hipStream_t s) {
+  const int nqt = (p.T + 127) / 128;
+  hipLaunchKernelGGL(flash_prefill_kernel, dim3(nqt * p.H * p.B), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,279 @@
+// bf16 MFMA GEMM for gfx950: C[M,N] = A[M,K] . B[N,K]^T with fp32 accumulate.
+//
+// Every projection of the MLA forward is an nn.Linear product y = x W^T with
+// W stored [out, in] (the module layout shown on the "Kimi K2 · Key-value
+// compression" page).  Both operands are therefore K-contiguous, which is
+// exactly the per-lane operand shape of v_mfma_f32_32x32x16_bf16 (each lane
+// holds 8 consecutive K values of one row), so tiles go global -> registers
+// -> LDS (XOR-swizzled 16-byte chunks, conflict-free ds_read_b128) -> MFMA
+// with no transposition anywhere.
+//
+// Tile: BM x BN x 64, WM x WN waves, each wave (BM/WM) x (BN/WN) built from
+// 32x32 MFMA blocks.  Two LDS stages: the next K tile's global loads are in
+// flight while the current one is multiplied.  Split-K writes fp32 partials
+// whose consumer sums them in a fixed order (deterministic).
+//
+// Epilogues (fused, lane-local):
+//   EPI_F32    fp32 store (split-K partial or fp32 result)
+//   EPI_BF16   bf16 store
+//   EPI_ROPE   bf16 store; the rotary columns of each head are rotated by the
+//              RoPE table row of the token's position (pair partner read with
+//              a lane shuffle: pair (2i, 2i+1) sits in adjacent lanes)
+//   EPI_RESID  bf16 store of R + acc (residual add of the dense block)
+//   EPI_SWIGLU dual-B product: 32-column blocks alternate W1 / W3 rows, so a
+//              lane holds g and u of the same output column and writes
+//              silu(g) * u (the SwiGLU steps of the dense block)
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int ROWS_PER_PASS = NT / 8;               // 8 threads x 16 B cover one 64-wide K row
+  constexpr int A_CH = BM / ROWS_PER_PASS;
+  constexpr int B_CH = BN / ROWS_PER_PASS;
+  static_assert(FM >= 1 && FN >= 1, "wave tile");
+  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small for the block");
+  static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU pairs 32-column blocks inside a wave");
+
+  __shared__ u32x4 lds[2][(BM + BN) * 8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+
+  // ---- tile coordinates (XCD-aware, grouped along M) ----
+  const int ntiles = p.tiles_m * p.tiles_n;
+  const int lin = xcd_remap(blockIdx.x, ntiles);
+  constexpr int GM = 8;
+  const int group = lin / (GM * p.tiles_n);
+  const int first_m = group * GM;
+  const int gm = min(p.tiles_m - first_m, GM);
+  const int within = lin - group * GM * p.tiles_n;
+  const int tm = first_m + within % gm;
+  const int tn = within / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int bidx = blockIdx.y / p.ksplit;
+  const int split = blockIdx.y % p.ksplit;
+  const bf16_t* __restrict__ A = p.A + (long)bidx * p.sA;
+  const bf16_t* __restrict__ B = p.B + (long)bidx * p.sB;
+  const bf16_t* __restrict__ B2 = p.B2;
+  const int k_begin = split * p.kchunk;
+  const int k_end = min(p.K, k_begin + p.kchunk);
+  const int nk = (k_end - k_begin) / 64;
+
+  // ---- per-thread global source rows as 32-bit element offsets (rows past
+  //      the edge are clamped: loaded from a valid row and never stored) ----
+  const int ch = tid & 7;
+  int a_off[A_CH], b_off[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    int r = tid / 8 + i * ROWS_PER_PASS;
+    int gr = min(m0 + r, p.M - 1);
+    a_off[i] = gr * (int)p.lda + ch * 8 + k_begin;
+  }
+  unsigned b2mask = 0;  // bit i: chunk row i comes from B2
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    int r = tid / 8 + i * ROWS_PER_PASS;
+    int src;
+    if (EPI == EPI_SWIGLU) {
+      int rb = r >> 5;
+      src = min(n0 / 2 + (rb >> 1) * 32 + (r & 31), p.N / 2 - 1);
+      if (rb & 1) b2mask |= 1u << i;
+    } else {
+      src = min(n0 + r, p.N - 1);
+      if (p.b_split > 0 && src >= p.b_split) {
+        src -= p.b_split;
+        b2mask |= 1u << i;
+      }
+    }
+    b_off[i] = src * (int)p.ldb + ch * 8 + k_begin;
+  }
+
+  u32x4 ra[A_CH], rb[B_CH];
+#define GEMM_GLOAD(koff)                                                              \
+  do {                                                                                \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                  \
+        ra[i] = *(const u32x4*)(A + a_off[i] + (koff));                                \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                \
+      const bf16_t* src_ = ((b2mask >> i) & 1) ? B2 : B;                               \
+      rb[i] = *(const u32x4*)(src_ + b_off[i] + (koff));                               \
+    }                                                                                 \
+  } while (0)
+#define GEMM_SSTORE(buf)                                                              \
+  do {                                                                                \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                \
+      const int r_ = tid / 8 + i * ROWS_PER_PASS;                                      \
+      lds[buf][r_ * 8 + (ch ^ (r_ & 7))] = ra[i];                                      \
+    }                                                                                 \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                \
+      const int r_ = tid / 8 + i * ROWS_PER_PASS;                                      \
+      lds[buf][(BM + r_) * 8 + (ch ^ (r_ & 7))] = rb[i];                               \
+    }                                                                                 \
+  } while (0)
+
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int lr = lane & 31, lg = lane >> 5;
+  if (nk > 0) {
+    GEMM_GLOAD(0);
+    GEMM_SSTORE(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) GEMM_GLOAD((kt + 1) * 64);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        int r = wm * WTM + i * 32 + lr;
+        u32x4 v = lds[cur][r * 8 + ((2 * s + lg) ^ (r & 7))];
+        af[i] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        int r = wn * WTN + j * 32 + lr;
+        u32x4 v = lds[cur][(BM + r) * 8 + ((2 * s + lg) ^ (r & 7))];
+        bfr[j] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) GEMM_SSTORE(cur ^ 1);
+    __syncthreads();
+  }
+
+#undef GEMM_GLOAD
+#undef GEMM_SSTORE
+
+  // ---- epilogue: lane holds column (lane & 31) of each 32x32 block and rows
+  //      8*i + 4*(lane >> 5) + j in acc[...][4*i + j] ----
+  if (EPI == EPI_SWIGLU) {
+    bf16_t* C = (bf16_t*)p.C + (long)bidx * p.sC;
+#pragma unroll
+    for (int j = 0; j < FN; j += 2) {
+      int rbk = (wn * WTN) / 32 + j;                 // even: W1 block, +1: W3 block
+      int col = n0 / 2 + (rbk >> 1) * 32 + lr;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          int row = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + lg * 4 + (e & 3);
+          float g = acc[i][j][e], u = acc[i][j + 1][e];
+          float h = g / (1.f + __expf(-g)) * u;
+          if (row < p.M && col < p.N / 2) C[(long)row * p.ldc + col] = f2bf(h);
+        }
+    }
+    return;
+  }
+
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int col = n0 + wn * WTN + j * 32 + lr;
+    // RoPE pair index of this column (-1 if not a rotary column)
+    int pair = -1;
+    if (EPI == EPI_ROPE) {
+      int cin = col % p.head_dim - p.rope_start;
+      pair = cin >= 0 ? (cin >> 1) : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + lg * 4 + (e & 3);
+        float v = acc[i][j][e];
+        if (EPI == EPI_ROPE) {
+          float partner = __shfl_xor(v, 1, 64);
+          if (pair >= 0 && row < p.M) {
+            int pos = row % p.rope_T + p.rope_pos0;
+            float c = p.rcos[(long)pos * p.n_pairs + pair];
+            float sn = p.rsin[(long)pos * p.n_pairs + pair];
+            // even lane holds x_{2i}, odd lane holds x_{2i+1}
+            v = (lr & 1) ? (partner * sn + v * c) : (v * c - partner * sn);
+          }
+        }
+        if (row < p.M && col < p.N) {
+          if (EPI == EPI_F32) {
+            float* C = (float*)p.C + (long)bidx * p.sC + (long)split * p.split_stride;
+            C[(long)row * p.ldc + col] = v;
+          } else if (EPI == EPI_RESID) {
+            bf16_t* C = (bf16_t*)p.C + (long)bidx * p.sC;
+            C[(long)row * p.ldc + col] = f2bf(bf2f(p.R[(long)row * p.ldr + col]) + v);
+          } else {
+            bf16_t* C = (bf16_t*)p.C + (long)bidx * p.sC;
+            C[(long)row * p.ldc + col] = f2bf(v);
+          }
+        }
+      }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+static hipError_t launch_cfg(GemmParams p, hipStream_t s) {
+  p.tiles_m = (p.M + BM - 1) / BM;
+  p.tiles_n = (p.N + BN - 1) / BN;  // SwiGLU: N counts both W1 and W3 columns
+  dim3 grid(p.tiles_m * p.tiles_n, p.batch * p.ksplit);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), grid, dim3(WM * WN * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t launch_epi(GemmParams p, int cfg, hipStream_t s) {
+  switch (cfg) {
+    case GEMM_CFG_256x256:
+      if (EPI == EPI_ROPE) return hipErrorInvalidValue;
+      return launch_cfg<256, 256, 2, 2, (EPI == EPI_ROPE ? EPI_BF16 : EPI)>(p, s);
+    case GEMM_CFG_128x128: return launch_cfg<128, 128, 2, 2, EPI>(p, s);
+    case GEMM_CFG_64x128: return launch_cfg<64, 128, 1, 2, EPI>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Tile choice: the largest tile that still gives every CU work; small-M
+// (decode) products use a 64-row tile whose B stream dominates.
+int gemm_pick_cfg(int M, int N, int batch) {
+  if (M <= 64) return GEMM_CFG_64x128;
+  long t256 = (long)((M + 255) / 256) * ((N + 255) / 256) * batch;
+  if (t256 >= 200) return GEMM_CFG_256x256;
+  return GEMM_CFG_128x128;
+}
+
+hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s) {
+  if (p.batch <= 0) p.batch = 1;
+  if (p.ksplit <= 0) p.ksplit = 1;
+  if (p.kchunk <= 0) p.kchunk = p.K;
+  if (cfg < 0) cfg = gemm_pick_cfg(p.M, p.N, p.batch * p.ksplit);
+  switch (epi) {
+    case EPI_F32: return launch_epi<EPI_F32>(p, cfg, s);
+    case EPI_BF16: return launch_epi<EPI_BF16>(p, cfg, s);
+    case EPI_ROPE:
+      // the 256x256 tile runs out of registers for the rotary epilogue
+      return launch_epi<EPI_ROPE>(p, cfg == GEMM_CFG_256x256 ? GEMM_CFG_128x128 : cfg, s);
+    case EPI_RESID: return launch_epi<EPI_RESID>(p, cfg, s);
+    case EPI_SWIGLU:
+      if (cfg == GEMM_CFG_64x128) return launch_cfg<64, 128, 1, 2, EPI_SWIGLU>(p, s);
+      if (cfg == GEMM_CFG_128x128) return launch_cfg<128, 128, 2, 2, EPI_SWIGLU>(p, s);
+      return launch_cfg<256, 256, 2, 2, EPI_SWIGLU>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mla

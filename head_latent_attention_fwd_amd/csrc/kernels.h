@@ -1,0 +1,152 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef uint16_t bf16_t;
+
+// ------------------------------------------------------------------ GEMM
+enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_ROPE = 2, EPI_RESID = 3, EPI_SWIGLU = 4 };
+enum { GEMM_CFG_AUTO = -1, GEMM_CFG_256x256 = 0, GEMM_CFG_128x128 = 1, GEMM_CFG_64x128 = 2 };
+
+struct GemmParams {
+  const bf16_t* A;   // [M, K] row-major, leading dim lda
+  const bf16_t* B;   // [N, K] row-major (nn.Linear weight), leading dim ldb
+  const bf16_t* B2;  // second weight: SwiGLU W3 (B is W1, both [N/2, K]); or,
+                     // when b_split > 0, the rows n >= b_split of the product
+  int b_split;       // rows [0, b_split) from B, [b_split, N) from B2 (0: off)
+  void* C;           // output, leading dim ldc (fp32 for EPI_F32, else bf16)
+  const bf16_t* R;   // residual [M, N] for EPI_RESID, leading dim ldr
+  long lda, ldb, ldc, ldr;
+  int M, N, K;       // SwiGLU: N = 2 * d_ff (output has N/2 columns)
+  int ksplit;        // number of K slices (grid.y = batch * ksplit)
+  int kchunk;        // K per slice, a multiple of 64
+  long split_stride; // elements between the fp32 partial outputs of slices
+  int batch;
+  long sA, sB, sC;   // batch strides in elements
+  const float* rcos; // RoPE table [n_pos, n_pairs]
+  const float* rsin;
+  int rope_T, rope_pos0, head_dim, rope_start, n_pairs;
+  int tiles_m, tiles_n;  // filled by the launcher
+};
+
+int gemm_pick_cfg(int M, int N, int batch);
+hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s);
+
+// fp32 generic GEMM: C[b] = (R ? R : 0) + A[b] . op(B[b]); op(B) = B^T when
+// b_is_nk (B stored [N, K]) else B (stored [K, N]).
+struct GemmF32Params {
+  const float* A; const float* B; float* C; const float* R;
+  long lda, ldb, ldc, ldr;
+  int M, N, K, batch;
+  long sA, sB, sC;
+  int b_is_nk;
+};
+hipError_t gemm_f32(const GemmF32Params& p, hipStream_t s);
+
+// -------------------------------------------------------- row kernels
+// Sum the split-K partials of the joint down-projection row and produce the
+// normalised query latent, normalised kv latent and roped shared key, with
+// optional cache writes.
+template <typename T> struct LatentNormParams {
+  const float* part;  // [nsplit][M][ld_part] fp32 partials (nsplit >= 1)
+  int nsplit; long split_stride; long ld_part;
+  int M, q_lora, kv_lora, d_rope;
+  const T* g_q; const T* g_kv;
+  float eps;
+  T* cq;  long ld_cq;    // [M, q_lora]
+  T* ckv; long ld_ckv;   // [M, kv_lora]
+  T* kr;  long ld_kr;    // [M, d_rope]
+  const float* rcos; const float* rsin; int n_pairs;
+  int rope_T, rope_pos0;  // position of row m = m % rope_T + rope_pos0
+  // optional latent cache [B][L_cap][kv_lora + d_rope]: row m = b*rope_T + t
+  // goes to slot t + rope_pos0 of sequence b
+  T* latent_cache; int L_cap;
+  // optional full key cache [B][H][L_cap][dqk]: k^R copied to every head
+  T* k_cache; int n_heads; int dqk; int d_nope;
+};
+template <typename T> hipError_t latent_norm_rope(const LatentNormParams<T>& p, hipStream_t s);
+
+template <typename T>
+hipError_t rmsnorm_rows(const T* x, long ldx, const T* g, T* y, long ldy, int M, int D, float eps,
+                        hipStream_t s);
+
+hipError_t rope_table(int n_pos, int n_pairs, double base, float* cos_out, float* sin_out,
+                      hipStream_t s);
+
+// fp32-path elementwise helpers
+hipError_t rope_inplace_f32(float* x, long ldx, int M, int ncols, int head_dim, int rope_start,
+                            const float* rcos, const float* rsin, int n_pairs, int rope_T,
+                            int rope_pos0, hipStream_t s);
+hipError_t swiglu_f32(const float* g, const float* u, float* h, long n, hipStream_t s);
+
+// Scatter the per-head keys/values of new tokens into the full cache.
+// kv [M][H][d_nope + d_v] (row m = b * T + t), kr [M][d_rope]; slot t + pos0.
+template <typename T>
+hipError_t scatter_full_cache(const T* kv, const T* kr, T* k_cache, T* v_cache, int Bn, int T_,
+                              int pos0, int L_cap, int H, int d_nope, int d_rope, int d_v,
+                              hipStream_t s);
+
+// Sum fp32 split partials [nsplit][M][N] into T out [M][ldo].
+template <typename T>
+hipError_t reduce_splits(const float* part, int nsplit, long split_stride, int M, int N, T* out,
+                         long ldo, hipStream_t s);
+
+// ------------------------------------------------------------ attention
+// Generic attention (fp32 path and any head widths): one wave per query.
+struct AttnGenericParams {
+  const float* q_nope; long q_row; long q_head;    // query (b, i, h) at b*Tq*q_row... see below
+  const float* q_rope; long qr_row; long qr_head;
+  const float* k_nope; long kn_b, kn_j, kn_h;
+  const float* k_rope; long kr_b, kr_j, kr_h;
+  const float* v;      long v_b, v_j, v_h;
+  float* out; long o_row; long o_head;
+  int B, Tq, Tk, H, d_nope, d_rope, d_v;
+  int causal_offset;  // query i sees keys j <= i + causal_offset
+  float scale;
+};
+hipError_t attn_generic_f32(const AttnGenericParams& p, hipStream_t s);
+
+// bf16 flash prefill (Kimi head widths 128 + 64, value 128), causal.
+struct FlashParams {
+  const bf16_t* q;   // [B*T][H][192]   (rope part already rotated)
+  const bf16_t* kv;  // [B*T][H][256]   ([k_nope 128 | v 128] per head)
+  const bf16_t* kr;  // [B*T][64]       (rotated, shared by heads)
+  bf16_t* out;       // [B*T][H*128]
+  int B, T, H;
+  float scale_log2;  // softmax scale * log2(e)
+};
+hipError_t flash_prefill_bf16(const FlashParams& p, hipStream_t s);
+
+// bf16 decode over the full per-head cache (one query per sequence).
+struct DecodeFullParams {
+  const bf16_t* q;       // [B][H][192]
+  const bf16_t* k_cache; // [B][H][L_cap][192]
+  const bf16_t* v_cache; // [B][H][L_cap][128]
+  bf16_t* out;           // [B][H*128]
+  float* part;           // split partials: [B*H][nsplit][128 + 2]
+  int B, H, L, L_cap, nsplit, chunk;
+  float scale_log2;
+};
+hipError_t decode_full_bf16(const DecodeFullParams& p, hipStream_t s);
+
+// bf16 absorbed decode over the latent cache.
+struct DecodeLatentParams {
+  const bf16_t* q_abs;   // [B][H][512]  absorbed query (W_UK folded in)
+  const bf16_t* q;       // [B][H][192]  (rope part at offset 128)
+  const bf16_t* cache;   // [B][L_cap][576]
+  float* part;           // [B][nsplit][H][516]: m, l, pad, pad, o~[512]
+  bf16_t* o_lat;         // [B][H][512]  merged latent output
+  int B, H, L, L_cap, nsplit, chunk;
+  float scale_log2;
+};
+hipError_t decode_latent_bf16(const DecodeLatentParams& p, hipStream_t s);
+
+// bf16 query absorption q~[b,h,:] = q_nope[b,h,:] . W_UK,h  (W_UK,h = rows
+// h*256 .. h*256+127 of kv_b_proj, each of 512 latent features)
+hipError_t absorb_q_bf16(const bf16_t* q, const bf16_t* w_ukv, bf16_t* q_abs, int B, int H,
+                         hipStream_t s);
+
+}  // namespace mla

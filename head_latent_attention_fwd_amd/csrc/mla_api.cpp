@@ -1,0 +1,770 @@
+// C-ABI host layer of the MLA library: argument validation, workspace
+// carving and the launch sequence of each entry point (see include/mla.h).
+//
+// Launch sequences (bf16; the float32 path mirrors them with the generic
+// kernels):
+//  prefill : [x W_DQ^T | x W_DKVR^T] (one GEMM over both weights, fp32 out)
+//            -> latent RMSNorms + RoPE of the shared key (+ latent cache)
+//            -> q up-projection with RoPE epilogue, kv up-projection
+//            -> causal flash attention -> o_proj (+ residual in the block)
+//            (+ full-cache scatter)
+//  decode  : the same projections at M = B with split-K, cache slot P
+//            update, decode attention (full or absorbed latent), o_proj.
+//  block   : RMSNorm -> prefill with residual -> RMSNorm -> SwiGLU GEMM
+//            (W1/W3 interleaved, silu(g)*u epilogue) -> W2 GEMM + residual.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mla.h"
+#include "kernels.h"
+
+using namespace mla;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+#define HIPCHK(expr)                                                                      \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return fail(MLA_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));            \
+  } while (0)
+
+// ---- opt-in kernel timing: a pair of HIP events around each named launch
+//      on the caller's stream, read back by mla_profile_summary() ----
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+thread_local bool g_prof = false;
+thread_local std::vector<ProfRec> g_prof_pending;
+thread_local std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct ProfScope {
+  const char* name;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  ProfScope(const char* n, hipStream_t s) : name(n), st(s) {
+    if (g_prof && (a = prof_event())) hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (!a) return;
+    hipEvent_t b = prof_event();
+    if (!b) return;
+    hipEventRecord(b, st);
+    g_prof_pending.push_back({name, a, b});
+  }
+};
+
+#define LAUNCH(name, expr)        \
+  do {                            \
+    ProfScope ps_((name), st);    \
+    HIPCHK(expr);                 \
+  } while (0)
+
+size_t esize(const mla_dims* d) { return d->dtype == MLA_BF16 ? 2 : 4; }
+long rup(long x, long a) { return (x + a - 1) / a * a; }
+
+// Workspace carving: regions aligned to 256 bytes.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    off = (size_t)rup((long)off, 256);
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+int check_dims(const mla_dims* d, bool need_ff) {
+  if (!d) return fail(MLA_ERR_NULL, "dims is NULL");
+  if (d->d_model <= 0 || d->n_heads <= 0 || d->q_lora_rank <= 0 || d->kv_lora_rank <= 0 ||
+      d->qk_nope_dim <= 0 || d->qk_rope_dim <= 0 || d->v_head_dim <= 0)
+    return fail(MLA_ERR_SHAPE, "every width of mla_dims must be positive");
+  if (d->qk_rope_dim % 2) return fail(MLA_ERR_SHAPE, "qk_rope_dim must be even (RoPE pairs)");
+  if (need_ff && d->d_ff <= 0) return fail(MLA_ERR_SHAPE, "d_ff must be positive for the block");
+  if (!(d->rms_eps >= 0.f) || !std::isfinite(d->softmax_scale) || d->softmax_scale <= 0.f)
+    return fail(MLA_ERR_SHAPE, "rms_eps must be >= 0 and softmax_scale positive and finite");
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "dtype %d is neither MLA_F32 nor MLA_BF16", d->dtype);
+  if (d->dtype == MLA_F32) {
+    if (d->qk_nope_dim + d->qk_rope_dim > 1024 || d->v_head_dim > 1024 ||
+        d->kv_lora_rank + d->qk_rope_dim > 1024)
+      return fail(MLA_ERR_UNSUPPORTED, "float32 path: head widths up to 1024");
+  } else {
+    if (d->qk_nope_dim != 128 || d->qk_rope_dim != 64 || d->v_head_dim != 128)
+      return fail(MLA_ERR_UNSUPPORTED,
+                  "bf16 path serves the Kimi K2 head widths (nope 128, rope 64, value 128)");
+    if (d->d_model % 64 || d->q_lora_rank % 64 || d->kv_lora_rank % 64 ||
+        (need_ff && d->d_ff % 64))
+      return fail(MLA_ERR_UNSUPPORTED, "bf16 path: d_model, q_lora, kv_lora, d_ff multiples of 64");
+  }
+  return MLA_OK;
+}
+
+int check_weights(const mla_weights* w) {
+  if (!w) return fail(MLA_ERR_NULL, "weights is NULL");
+  if (!w->w_dq || !w->g_q || !w->w_uqr || !w->w_dkvr || !w->g_kv || !w->w_ukv || !w->w_o)
+    return fail(MLA_ERR_NULL, "a weight pointer is NULL");
+  return MLA_OK;
+}
+
+int check_rope(const float* c, const float* s, int rows, int need) {
+  if (!c || !s) return fail(MLA_ERR_NULL, "rope table pointer is NULL");
+  if (rows < need) return fail(MLA_ERR_SHAPE, "rope_rows %d < %d positions needed", rows, need);
+  return MLA_OK;
+}
+
+// 32-bit element offsets inside the GEMM kernels: every operand must have
+// fewer than 2^31 elements.
+int check_i32(long elems, const char* what) {
+  if (elems >= (long)INT_MAX) return fail(MLA_ERR_UNSUPPORTED, "%s exceeds 2^31 elements", what);
+  return MLA_OK;
+}
+
+// Split-K plan for the bf16 GEMM: enough workgroups to cover the CUs.
+void plan_splitk(int M, int N, int K, int* S, int* kchunk) {
+  int cfg = gemm_pick_cfg(M, N, 1);
+  int bm = cfg == GEMM_CFG_256x256 ? 256 : (cfg == GEMM_CFG_128x128 ? 128 : 64);
+  int bn = cfg == GEMM_CFG_256x256 ? 256 : 128;
+  long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  int kb = K / 64;
+  int s = (int)((256 + tiles - 1) / tiles);
+  if (s < 1) s = 1;
+  if (s > kb) s = kb;
+  if (s > 32) s = 32;
+  int per = (kb + s - 1) / s;
+  *kchunk = per * 64;
+  *S = (kb + per - 1) / per;
+}
+
+GemmParams gp_base() {
+  GemmParams p;
+  memset(&p, 0, sizeof p);
+  p.batch = 1;
+  p.ksplit = 1;
+  return p;
+}
+
+// ----------------------------------------------------------------- layouts
+struct ProjBufs {
+  void* part;   // fp32 [S][M][N1]
+  int S, kchunk;
+  void* cq;     // [M][q_lora]
+  void* ckv;    // [M][kv_lora]
+  void* kr;     // [M][d_rope]
+  void* q;      // [M][H*dqk]
+  void* kv;     // [M][H*(dn+dv)]   (NULL when not needed)
+  void* o;      // [M][H*dv]
+};
+
+void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, ProjBufs* b) {
+  const int N1 = d->q_lora_rank + d->kv_lora_rank + d->qk_rope_dim;
+  const int H = d->n_heads, dqk = d->qk_nope_dim + d->qk_rope_dim;
+  const size_t es = esize(d);
+  b->S = 1;
+  b->kchunk = d->d_model;
+  if (splitk && d->dtype == MLA_BF16) plan_splitk(M, N1, d->d_model, &b->S, &b->kchunk);
+  b->part = c.take((size_t)b->S * M * N1 * 4);
+  b->cq = c.take((size_t)M * d->q_lora_rank * es);
+  b->ckv = c.take((size_t)M * d->kv_lora_rank * es);
+  b->kr = c.take((size_t)M * d->qk_rope_dim * es);
+  b->q = c.take((size_t)M * H * dqk * es);
+  b->kv = need_kv ? c.take((size_t)M * H * (d->qk_nope_dim + d->v_head_dim) * es) : nullptr;
+  b->o = c.take((size_t)M * H * d->v_head_dim * es);
+}
+
+// ---------------------------------------------------- shared launch steps
+// Down-projections, latent norms and RoPE, query up-projection (roped) and,
+// if kv is given, the kv up-projection.  Rows m = b*rowsT + t at position
+// t + pos0.
+int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int M, int rowsT,
+                    int pos0, const float* rc, const float* rs, const ProjBufs& b,
+                    void* latent_cache, int L_cap, hipStream_t st) {
+  const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
+  const int dqk = dn + dr, ql = d->q_lora_rank, kl = d->kv_lora_rank;
+  const int N1 = ql + kl + dr, D = d->d_model;
+  if (d->dtype == MLA_BF16) {
+    GemmParams g = gp_base();
+    g.A = (const bf16_t*)x; g.lda = D;
+    g.B = (const bf16_t*)w->w_dq; g.B2 = (const bf16_t*)w->w_dkvr; g.ldb = D;
+    g.b_split = ql;
+    g.C = b.part; g.ldc = N1;
+    g.M = M; g.N = N1; g.K = D;
+    g.ksplit = b.S; g.kchunk = b.kchunk; g.split_stride = (long)M * N1;
+    LAUNCH("gemm_down", gemm_bf16(g, EPI_F32, -1, st));
+    LatentNormParams<bf16_t> n;
+    memset(&n, 0, sizeof n);
+    n.part = (const float*)b.part; n.nsplit = b.S; n.split_stride = (long)M * N1; n.ld_part = N1;
+    n.M = M; n.q_lora = ql; n.kv_lora = kl; n.d_rope = dr;
+    n.g_q = (const bf16_t*)w->g_q; n.g_kv = (const bf16_t*)w->g_kv; n.eps = d->rms_eps;
+    n.cq = (bf16_t*)b.cq; n.ld_cq = ql; n.ckv = (bf16_t*)b.ckv; n.ld_ckv = kl;
+    n.kr = (bf16_t*)b.kr; n.ld_kr = dr;
+    n.rcos = rc; n.rsin = rs; n.n_pairs = dr / 2; n.rope_T = rowsT; n.rope_pos0 = pos0;
+    n.latent_cache = (bf16_t*)latent_cache; n.L_cap = L_cap;
+    LAUNCH("latent_norm_rope", latent_norm_rope<bf16_t>(n, st));
+    GemmParams q = gp_base();
+    q.A = (const bf16_t*)b.cq; q.lda = ql;
+    q.B = (const bf16_t*)w->w_uqr; q.ldb = ql;
+    q.C = b.q; q.ldc = (long)H * dqk;
+    q.M = M; q.N = H * dqk; q.K = ql;
+    q.rcos = rc; q.rsin = rs; q.rope_T = rowsT; q.rope_pos0 = pos0;
+    q.head_dim = dqk; q.rope_start = dn; q.n_pairs = dr / 2;
+    LAUNCH("gemm_q_up_rope", gemm_bf16(q, EPI_ROPE, -1, st));
+    if (b.kv) {
+      GemmParams k = gp_base();
+      k.A = (const bf16_t*)b.ckv; k.lda = kl;
+      k.B = (const bf16_t*)w->w_ukv; k.ldb = kl;
+      k.C = b.kv; k.ldc = (long)H * (dn + dv);
+      k.M = M; k.N = H * (dn + dv); k.K = kl;
+      LAUNCH("gemm_kv_up", gemm_bf16(k, EPI_BF16, -1, st));
+    }
+    return MLA_OK;
+  }
+  // float32 path
+  GemmF32Params g;
+  memset(&g, 0, sizeof g);
+  g.A = (const float*)x; g.lda = D; g.B = (const float*)w->w_dq; g.ldb = D;
+  g.C = (float*)b.part; g.ldc = N1; g.M = M; g.N = ql; g.K = D; g.batch = 1; g.b_is_nk = 1;
+  LAUNCH("gemm_down", gemm_f32(g, st));
+  g.B = (const float*)w->w_dkvr; g.C = (float*)b.part + ql; g.N = kl + dr;
+  LAUNCH("gemm_down", gemm_f32(g, st));
+  LatentNormParams<float> n;
+  memset(&n, 0, sizeof n);
+  n.part = (const float*)b.part; n.nsplit = 1; n.split_stride = 0; n.ld_part = N1;
+  n.M = M; n.q_lora = ql; n.kv_lora = kl; n.d_rope = dr;
+  n.g_q = (const float*)w->g_q; n.g_kv = (const float*)w->g_kv; n.eps = d->rms_eps;
+  n.cq = (float*)b.cq; n.ld_cq = ql; n.ckv = (float*)b.ckv; n.ld_ckv = kl;
+  n.kr = (float*)b.kr; n.ld_kr = dr;
+  n.rcos = rc; n.rsin = rs; n.n_pairs = dr / 2; n.rope_T = rowsT; n.rope_pos0 = pos0;
+  n.latent_cache = (float*)latent_cache; n.L_cap = L_cap;
+  LAUNCH("latent_norm_rope", latent_norm_rope<float>(n, st));
+  GemmF32Params q;
+  memset(&q, 0, sizeof q);
+  q.A = (const float*)b.cq; q.lda = ql; q.B = (const float*)w->w_uqr; q.ldb = ql;
+  q.C = (float*)b.q; q.ldc = (long)H * dqk; q.M = M; q.N = H * dqk; q.K = ql; q.batch = 1;
+  q.b_is_nk = 1;
+  LAUNCH("gemm_q_up", gemm_f32(q, st));
+  LAUNCH("rope_q", rope_inplace_f32((float*)b.q, (long)H * dqk, M, H * dqk, dqk, dn, rc, rs, dr / 2, rowsT,
+                          pos0, st));
+  if (b.kv) {
+    GemmF32Params k;
+    memset(&k, 0, sizeof k);
+    k.A = (const float*)b.ckv; k.lda = kl; k.B = (const float*)w->w_ukv; k.ldb = kl;
+    k.C = (float*)b.kv; k.ldc = (long)H * (dn + dv); k.M = M; k.N = H * (dn + dv); k.K = kl;
+    k.batch = 1; k.b_is_nk = 1;
+    LAUNCH("gemm_kv_up", gemm_f32(k, st));
+  }
+  return MLA_OK;
+}
+
+// out[M, d] = o[M, H*dv] . W_O^T (+ R).  Split-K for small M (decode).
+int run_oproj(const mla_dims* d, const void* w_o, const void* o, int M, const void* R, void* out,
+              void* part, int S, int kchunk, hipStream_t st) {
+  const int D = d->d_model, K = d->n_heads * d->v_head_dim;
+  if (d->dtype == MLA_BF16) {
+    GemmParams g = gp_base();
+    g.A = (const bf16_t*)o; g.lda = K; g.B = (const bf16_t*)w_o; g.ldb = K;
+    g.M = M; g.N = D; g.K = K;
+    if (S > 1) {
+      g.C = part; g.ldc = D; g.ksplit = S; g.kchunk = kchunk; g.split_stride = (long)M * D;
+      LAUNCH("gemm_o_proj", gemm_bf16(g, EPI_F32, -1, st));
+      LAUNCH("reduce_splits", reduce_splits<bf16_t>((const float*)part, S, (long)M * D, M, D, (bf16_t*)out, D, st));
+      return MLA_OK;
+    }
+    g.C = out; g.ldc = D;
+    if (R) { g.R = (const bf16_t*)R; g.ldr = D; }
+    LAUNCH("gemm_o_proj", gemm_bf16(g, R ? EPI_RESID : EPI_BF16, -1, st));
+    return MLA_OK;
+  }
+  GemmF32Params g;
+  memset(&g, 0, sizeof g);
+  g.A = (const float*)o; g.lda = K; g.B = (const float*)w_o; g.ldb = K;
+  g.C = (float*)out; g.ldc = D; g.R = (const float*)R; g.ldr = D;
+  g.M = M; g.N = D; g.K = K; g.batch = 1; g.b_is_nk = 1;
+  LAUNCH("gemm_o_proj", gemm_f32(g, st));
+  return MLA_OK;
+}
+
+struct PrefillPlan {
+  ProjBufs pb;
+};
+
+size_t prefill_layout(const mla_dims* d, int B, int T, void* ws, PrefillPlan* pl) {
+  Carver c(ws);
+  carve_proj(c, d, B * T, true, false, &pl->pb);
+  return c.off + 256;
+}
+
+int prefill_core(const mla_dims* d, const mla_weights* w, const void* x, int B, int T,
+                 const float* rc, const float* rs, void* out, const void* resid, void* k_cache,
+                 void* v_cache, void* latent_cache, int L_cap, const PrefillPlan& pl,
+                 hipStream_t st) {
+  const int M = B * T, H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim;
+  const int dv = d->v_head_dim, dqk = dn + dr;
+  const ProjBufs& b = pl.pb;
+  int rc_ = run_projections(d, w, x, M, T, 0, rc, rs, b, latent_cache, L_cap, st);
+  if (rc_) return rc_;
+  if (d->dtype == MLA_BF16) {
+    FlashParams f;
+    f.q = (const bf16_t*)b.q; f.kv = (const bf16_t*)b.kv; f.kr = (const bf16_t*)b.kr;
+    f.out = (bf16_t*)b.o; f.B = B; f.T = T; f.H = H;
+    f.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    LAUNCH("flash_prefill", flash_prefill_bf16(f, st));
+  } else {
+    AttnGenericParams a;
+    memset(&a, 0, sizeof a);
+    const long kvw = (long)H * (dn + dv);
+    a.q_nope = (const float*)b.q; a.q_row = (long)H * dqk; a.q_head = dqk;
+    a.q_rope = (const float*)b.q + dn; a.qr_row = (long)H * dqk; a.qr_head = dqk;
+    a.k_nope = (const float*)b.kv; a.kn_b = (long)T * kvw; a.kn_j = kvw; a.kn_h = dn + dv;
+    a.k_rope = (const float*)b.kr; a.kr_b = (long)T * dr; a.kr_j = dr; a.kr_h = 0;
+    a.v = (const float*)b.kv + dn; a.v_b = (long)T * kvw; a.v_j = kvw; a.v_h = dn + dv;
+    a.out = (float*)b.o; a.o_row = (long)H * dv; a.o_head = dv;
+    a.B = B; a.Tq = T; a.Tk = T; a.H = H; a.d_nope = dn; a.d_rope = dr; a.d_v = dv;
+    a.causal_offset = 0; a.scale = d->softmax_scale;
+    LAUNCH("attn_generic", attn_generic_f32(a, st));
+  }
+  if (k_cache) {
+    if (d->dtype == MLA_BF16)
+      LAUNCH("scatter_cache", scatter_full_cache<bf16_t>((const bf16_t*)b.kv, (const bf16_t*)b.kr,
+                                        (bf16_t*)k_cache, (bf16_t*)v_cache, B, T, 0, L_cap, H, dn,
+                                        dr, dv, st));
+    else
+      LAUNCH("scatter_cache", scatter_full_cache<float>((const float*)b.kv, (const float*)b.kr, (float*)k_cache,
+                                       (float*)v_cache, B, T, 0, L_cap, H, dn, dr, dv, st));
+  }
+  return run_oproj(d, w->w_o, b.o, M, resid, out, nullptr, 1, 0, st);
+}
+
+// --------------------------------------------------------------- decode
+struct DecodePlan {
+  ProjBufs pb;
+  void* q_abs;      // [B][H][kv_lora]
+  void* o_lat;      // [B][H][kv_lora]
+  void* apart;      // attention split partials
+  int nsplit, chunk;
+  int ns_cap;       // split count the partial buffer was sized for
+  void* opart;      // o_proj split partials [S2][B][d]
+  int S2, kchunk2;
+};
+
+void plan_full_splits(int B, int H, int L, int* nsplit, int* chunk) {
+  int want = (512 + B * H - 1) / (B * H);
+  int maxs = (L + 127) / 128;
+  int s = want < 1 ? 1 : want;
+  if (s > maxs) s = maxs;
+  if (s < 1) s = 1;
+  int ch = (L + s - 1) / s;
+  if (ch > 4096) ch = 4096;
+  *chunk = ch;
+  *nsplit = (L + ch - 1) / ch;
+}
+
+void plan_latent_splits(int B, int L, int* nsplit, int* chunk) {
+  int s = (256 + B - 1) / B;
+  int maxs = (L + 31) / 32;
+  if (s > maxs) s = maxs;
+  if (s < 1) s = 1;
+  int ch = (L + s - 1) / s;
+  ch = (ch + 31) / 32 * 32;
+  *chunk = ch;
+  *nsplit = (L + ch - 1) / ch;
+}
+
+size_t decode_layout(const mla_dims* d, int B, int L_cap, int form, void* ws, DecodePlan* pl) {
+  Carver c(ws);
+  const int H = d->n_heads, kl = d->kv_lora_rank;
+  const size_t es = esize(d);
+  carve_proj(c, d, B, form == 0, true, &pl->pb);
+  pl->q_abs = c.take((size_t)B * H * kl * es);
+  pl->o_lat = c.take((size_t)B * H * kl * es);
+  // upper bounds of the split counts chosen for any live length L <= L_cap
+  const int want_f = (512 + B * H - 1) / (B * H);
+  int cap_f = (L_cap + 127) / 128;
+  if (cap_f > want_f) cap_f = want_f;
+  if (cap_f < (L_cap + 4095) / 4096) cap_f = (L_cap + 4095) / 4096;
+  if (cap_f < 1) cap_f = 1;
+  int cap_l = (256 + B - 1) / B;
+  if (cap_l > (L_cap + 31) / 32) cap_l = (L_cap + 31) / 32;
+  if (cap_l < 1) cap_l = 1;
+  size_t fpart = (size_t)B * H * cap_f * 130 * 4;
+  size_t lpart = (size_t)B * cap_l * H * 516 * 4;
+  pl->apart = c.take(fpart > lpart ? fpart : lpart);
+  pl->ns_cap = form == 0 ? cap_f : cap_l;
+  pl->nsplit = 1;
+  pl->chunk = L_cap;
+  pl->S2 = 1;
+  pl->kchunk2 = H * d->v_head_dim;
+  if (d->dtype == MLA_BF16) plan_splitk(B, d->d_model, H * d->v_head_dim, &pl->S2, &pl->kchunk2);
+  pl->opart = c.take((size_t)pl->S2 * B * d->d_model * 4);
+  return c.off + 256;
+}
+
+int check_decode_args(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
+                      int L_cap, const float* rc, const float* rs, int rope_rows, void* out,
+                      void* ws) {
+  int r = check_dims(d, false);
+  if (r) return r;
+  if ((r = check_weights(w))) return r;
+  if (!x || !out) return fail(MLA_ERR_NULL, "x or out is NULL");
+  if (!ws) return fail(MLA_ERR_NULL, "workspace is NULL");
+  if (B <= 0 || L_cap <= 0) return fail(MLA_ERR_SHAPE, "B and L_cap must be positive");
+  if (P < 0 || P >= L_cap) return fail(MLA_ERR_SHAPE, "P=%d outside [0, L_cap=%d)", P, L_cap);
+  if ((r = check_rope(rc, rs, rope_rows, P + 1))) return r;
+  return MLA_OK;
+}
+
+}  // namespace
+
+// ===================================================================== ABI
+extern "C" {
+
+const char* mla_status_string(int s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: a size is non-positive or inconsistent";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape or dtype not served";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP launch failed";
+    default: return "unknown mla_status";
+  }
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+int mla_profile_enable(int on) {
+  g_prof = on != 0;
+  return MLA_OK;
+}
+
+int mla_profile_summary(char* buf, size_t len, int* n_entries) {
+  g_err[0] = 0;
+  struct Acc {
+    std::string name;
+    int count;
+    double ms;
+  };
+  std::vector<Acc> acc;
+  for (auto& r : g_prof_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      ms = -1.f;
+    bool found = false;
+    for (auto& a : acc)
+      if (a.name == r.name) {
+        a.count += 1;
+        a.ms += ms;
+        found = true;
+      }
+    if (!found) acc.push_back({r.name, 1, (double)ms});
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_pending.clear();
+  if (n_entries) *n_entries = (int)acc.size();
+  if (buf && len) {
+    size_t off = 0;
+    buf[0] = 0;
+    for (auto& a : acc) {
+      int w = snprintf(buf + off, len - off, "%s %d %.6f\n", a.name.c_str(), a.count, a.ms);
+      if (w < 0 || (size_t)w >= len - off) return fail(MLA_ERR_SHAPE, "profile buffer too small");
+      off += (size_t)w;
+    }
+  }
+  return MLA_OK;
+}
+
+int mla_rope_table(int n_pos, int d_rope, double base, float* cos_out, float* sin_out,
+                   void* stream) {
+  g_err[0] = 0;
+  if (!cos_out || !sin_out) return fail(MLA_ERR_NULL, "rope table output is NULL");
+  if (n_pos <= 0 || d_rope <= 0 || d_rope % 2) return fail(MLA_ERR_SHAPE, "bad n_pos/d_rope");
+  if (!(base > 0.0)) return fail(MLA_ERR_SHAPE, "base must be positive");
+  hipStream_t st = (hipStream_t)stream;
+  LAUNCH("rope_table", rope_table(n_pos, d_rope / 2, base, cos_out, sin_out, st));
+  return MLA_OK;
+}
+
+size_t mla_prefill_workspace_size(const mla_dims* d, int B, int T) {
+  if (check_dims(d, false) || B <= 0 || T <= 0) return 0;
+  PrefillPlan pl;
+  return prefill_layout(d, B, T, nullptr, &pl);
+}
+
+int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int B, int T,
+                const float* rc, const float* rs, int rope_rows, void* out, void* k_cache,
+                void* v_cache, void* latent_cache, int L_cap, void* ws, size_t ws_bytes,
+                void* stream) {
+  g_err[0] = 0;
+  int r = check_dims(d, false);
+  if (r) return r;
+  if ((r = check_weights(w))) return r;
+  if (!x || !out) return fail(MLA_ERR_NULL, "x or out is NULL");
+  if (!ws) return fail(MLA_ERR_NULL, "workspace is NULL");
+  if (B <= 0 || T <= 0) return fail(MLA_ERR_SHAPE, "B and T must be positive");
+  if ((r = check_rope(rc, rs, rope_rows, T))) return r;
+  if ((k_cache == nullptr) != (v_cache == nullptr))
+    return fail(MLA_ERR_NULL, "k_cache and v_cache must be given together");
+  if ((k_cache || latent_cache) && L_cap < T)
+    return fail(MLA_ERR_SHAPE, "L_cap=%d smaller than T=%d", L_cap, T);
+  const long M = (long)B * T;
+  if ((r = check_i32(M * d->d_model, "x")) || (r = check_i32(M * d->n_heads * 256, "kv")))
+    return r;
+  PrefillPlan pl;
+  size_t need = prefill_layout(d, B, T, nullptr, &pl);
+  if (ws_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  prefill_layout(d, B, T, ws, &pl);
+  return prefill_core(d, w, x, B, T, rc, rs, out, nullptr, k_cache, v_cache, latent_cache, L_cap,
+                      pl, (hipStream_t)stream);
+}
+
+size_t mla_decode_workspace_size(const mla_dims* d, int B, int L_cap) {
+  if (check_dims(d, false) || B <= 0 || L_cap <= 0) return 0;
+  DecodePlan a, b;
+  size_t s0 = decode_layout(d, B, L_cap, 0, nullptr, &a);
+  size_t s1 = decode_layout(d, B, L_cap, 1, nullptr, &b);
+  return s0 > s1 ? s0 : s1;
+}
+
+int mla_decode_fullcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
+                         int L_cap, void* k_cache, void* v_cache, const float* rc, const float* rs,
+                         int rope_rows, void* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int r = check_decode_args(d, w, x, B, P, L_cap, rc, rs, rope_rows, out, ws);
+  if (r) return r;
+  if (!k_cache || !v_cache) return fail(MLA_ERR_NULL, "k_cache/v_cache is NULL");
+  DecodePlan pl;
+  size_t need = decode_layout(d, B, L_cap, 0, nullptr, &pl);
+  if (ws_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  decode_layout(d, B, L_cap, 0, ws, &pl);
+  // the attention split depends on the live length L = P + 1
+  plan_full_splits(B, d->n_heads, P + 1, &pl.nsplit, &pl.chunk);
+  if (pl.nsplit > pl.ns_cap) return fail(MLA_ERR_HIP, "internal: split plan exceeds workspace");
+  hipStream_t st = (hipStream_t)stream;
+  const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
+  const ProjBufs& b = pl.pb;
+  if ((r = run_projections(d, w, x, B, 1, P, rc, rs, b, nullptr, L_cap, st))) return r;
+  if (d->dtype == MLA_BF16) {
+    LAUNCH("scatter_cache", scatter_full_cache<bf16_t>((const bf16_t*)b.kv, (const bf16_t*)b.kr, (bf16_t*)k_cache,
+                                      (bf16_t*)v_cache, B, 1, P, L_cap, H, dn, dr, dv, st));
+    DecodeFullParams a;
+    a.q = (const bf16_t*)b.q; a.k_cache = (const bf16_t*)k_cache;
+    a.v_cache = (const bf16_t*)v_cache; a.out = (bf16_t*)b.o; a.part = (float*)pl.apart;
+    a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
+    a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    LAUNCH("decode_full", decode_full_bf16(a, st));
+  } else {
+    LAUNCH("scatter_cache", scatter_full_cache<float>((const float*)b.kv, (const float*)b.kr, (float*)k_cache,
+                                     (float*)v_cache, B, 1, P, L_cap, H, dn, dr, dv, st));
+    const int dqk = dn + dr;
+    AttnGenericParams a;
+    memset(&a, 0, sizeof a);
+    a.q_nope = (const float*)b.q; a.q_row = (long)H * dqk; a.q_head = dqk;
+    a.q_rope = (const float*)b.q + dn; a.qr_row = (long)H * dqk; a.qr_head = dqk;
+    a.k_nope = (const float*)k_cache; a.kn_b = (long)H * L_cap * dqk; a.kn_j = dqk;
+    a.kn_h = (long)L_cap * dqk;
+    a.k_rope = (const float*)k_cache + dn; a.kr_b = a.kn_b; a.kr_j = dqk; a.kr_h = a.kn_h;
+    a.v = (const float*)v_cache; a.v_b = (long)H * L_cap * dv; a.v_j = dv; a.v_h = (long)L_cap * dv;
+    a.out = (float*)b.o; a.o_row = (long)H * dv; a.o_head = dv;
+    a.B = B; a.Tq = 1; a.Tk = P + 1; a.H = H; a.d_nope = dn; a.d_rope = dr; a.d_v = dv;
+    a.causal_offset = P; a.scale = d->softmax_scale;
+    LAUNCH("attn_generic", attn_generic_f32(a, st));
+  }
+  return run_oproj(d, w->w_o, b.o, B, nullptr, out, pl.opart, pl.S2, pl.kchunk2, st);
+}
+
+int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
+                           int L_cap, void* latent_cache, const float* rc, const float* rs,
+                           int rope_rows, void* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int r = check_decode_args(d, w, x, B, P, L_cap, rc, rs, rope_rows, out, ws);
+  if (r) return r;
+  if (!latent_cache) return fail(MLA_ERR_NULL, "latent_cache is NULL");
+  if (d->dtype == MLA_BF16 && (d->kv_lora_rank != 512 || d->n_heads != 64))
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 latent decode serves kv_lora 512 and 64 heads");
+  DecodePlan pl;
+  size_t need = decode_layout(d, B, L_cap, 1, nullptr, &pl);
+  if (ws_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  decode_layout(d, B, L_cap, 1, ws, &pl);
+  plan_latent_splits(B, P + 1, &pl.nsplit, &pl.chunk);
+  if (pl.nsplit > pl.ns_cap) return fail(MLA_ERR_HIP, "internal: split plan exceeds workspace");
+  hipStream_t st = (hipStream_t)stream;
+  const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
+  const int kl = d->kv_lora_rank, dqk = dn + dr;
+  const ProjBufs& b = pl.pb;
+  if ((r = run_projections(d, w, x, B, 1, P, rc, rs, b, latent_cache, L_cap, st))) return r;
+  if (d->dtype == MLA_BF16) {
+    LAUNCH("absorb_q", absorb_q_bf16((const bf16_t*)b.q, (const bf16_t*)w->w_ukv, (bf16_t*)pl.q_abs, B, H, st));
+    DecodeLatentParams a;
+    a.q_abs = (const bf16_t*)pl.q_abs; a.q = (const bf16_t*)b.q;
+    a.cache = (const bf16_t*)latent_cache; a.part = (float*)pl.apart;
+    a.o_lat = (bf16_t*)pl.o_lat;
+    a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
+    a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    LAUNCH("decode_latent", decode_latent_bf16(a, st));
+    // O_h = o~_h W_UV,h^T, batched over heads
+    GemmParams g = gp_base();
+    g.A = (const bf16_t*)pl.o_lat; g.lda = (long)H * kl;
+    g.B = (const bf16_t*)w->w_ukv + (long)dn * kl; g.ldb = kl;
+    g.C = b.o; g.ldc = (long)H * dv;
+    g.M = B; g.N = dv; g.K = kl;
+    g.batch = H; g.sA = kl; g.sB = (long)(dn + dv) * kl; g.sC = dv;
+    LAUNCH("gemm_uv", gemm_bf16(g, EPI_BF16, -1, st));
+  } else {
+    GemmF32Params g;
+    memset(&g, 0, sizeof g);
+    // q~ = Q^C . W_UK (W_UK,h rows of kv_b_proj used as a [d_nope, kv_lora] matrix)
+    g.A = (const float*)b.q; g.lda = (long)H * dqk;
+    g.B = (const float*)w->w_ukv; g.ldb = kl; g.b_is_nk = 0;
+    g.C = (float*)pl.q_abs; g.ldc = (long)H * kl;
+    g.M = B; g.N = kl; g.K = dn; g.batch = H;
+    g.sA = dqk; g.sB = (long)(dn + dv) * kl; g.sC = kl;
+    LAUNCH("absorb_q", gemm_f32(g, st));
+    AttnGenericParams a;
+    memset(&a, 0, sizeof a);
+    const long cw = kl + dr;
+    a.q_nope = (const float*)pl.q_abs; a.q_row = (long)H * kl; a.q_head = kl;
+    a.q_rope = (const float*)b.q + dn; a.qr_row = (long)H * dqk; a.qr_head = dqk;
+    a.k_nope = (const float*)latent_cache; a.kn_b = (long)L_cap * cw; a.kn_j = cw; a.kn_h = 0;
+    a.k_rope = (const float*)latent_cache + kl; a.kr_b = a.kn_b; a.kr_j = cw; a.kr_h = 0;
+    a.v = (const float*)latent_cache; a.v_b = a.kn_b; a.v_j = cw; a.v_h = 0;
+    a.out = (float*)pl.o_lat; a.o_row = (long)H * kl; a.o_head = kl;
+    a.B = B; a.Tq = 1; a.Tk = P + 1; a.H = H; a.d_nope = kl; a.d_rope = dr; a.d_v = kl;
+    a.causal_offset = P; a.scale = d->softmax_scale;
+    LAUNCH("attn_generic", attn_generic_f32(a, st));
+    // O_h = o~_h . W_UV,h^T
+    GemmF32Params u;
+    memset(&u, 0, sizeof u);
+    u.A = (const float*)pl.o_lat; u.lda = (long)H * kl;
+    u.B = (const float*)w->w_ukv + (long)dn * kl; u.ldb = kl; u.b_is_nk = 1;
+    u.C = (float*)b.o; u.ldc = (long)H * dv;
+    u.M = B; u.N = dv; u.K = kl; u.batch = H;
+    u.sA = kl; u.sB = (long)(dn + dv) * kl; u.sC = dv;
+    LAUNCH("gemm_uv", gemm_f32(u, st));
+  }
+  return run_oproj(d, w->w_o, b.o, B, nullptr, out, pl.opart, pl.S2, pl.kchunk2, st);
+}
+
+size_t dense_block_workspace_size(const mla_dims* d, int B, int T) {
+  if (check_dims(d, true) || B <= 0 || T <= 0) return 0;
+  const size_t es = esize(d);
+  const size_t M = (size_t)B * T;
+  PrefillPlan pl;
+  size_t attn = prefill_layout(d, B, T, nullptr, &pl);
+  size_t extra = 3 * rup((long)(M * d->d_model * es), 256);          // x_attn, x1, x_ffn
+  size_t ff = d->dtype == MLA_BF16 ? M * d->d_ff * es : 3 * M * d->d_ff * es;  // h (+ g, u)
+  return attn + extra + (size_t)rup((long)ff, 256) + 1024;
+}
+
+int dense_block_fwd(const mla_dims* d, const mla_block_weights* w, const void* x, int B, int T,
+                    const float* rc, const float* rs, int rope_rows, void* out, void* ws,
+                    size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int r = check_dims(d, true);
+  if (r) return r;
+  if (!w) return fail(MLA_ERR_NULL, "block weights is NULL");
+  if ((r = check_weights(&w->attn))) return r;
+  if (!w->g_attn || !w->g_ffn || !w->w1 || !w->w3 || !w->w2)
+    return fail(MLA_ERR_NULL, "a block weight pointer is NULL");
+  if (!x || !out) return fail(MLA_ERR_NULL, "x or out is NULL");
+  if (!ws) return fail(MLA_ERR_NULL, "workspace is NULL");
+  if (B <= 0 || T <= 0) return fail(MLA_ERR_SHAPE, "B and T must be positive");
+  if ((r = check_rope(rc, rs, rope_rows, T))) return r;
+  const long M = (long)B * T;
+  if ((r = check_i32(M * d->d_ff, "ffn hidden")) || (r = check_i32(M * d->n_heads * 256, "kv")) ||
+      (r = check_i32((long)d->d_ff * d->d_model, "W1")))
+    return r;
+  size_t need = dense_block_workspace_size(d, B, T);
+  if (ws_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  const size_t es = esize(d);
+  const int D = d->d_model, F = d->d_ff;
+  Carver c(ws);
+  void* xa = c.take((size_t)M * D * es);
+  void* x1 = c.take((size_t)M * D * es);
+  void* xf = c.take((size_t)M * D * es);
+  void* hbuf = c.take((size_t)M * F * es * (d->dtype == MLA_BF16 ? 1 : 3));
+  PrefillPlan pl;
+  prefill_layout(d, B, T, c.take(0), &pl);
+  if (d->dtype == MLA_BF16) {
+    LAUNCH("rmsnorm", rmsnorm_rows<bf16_t>((const bf16_t*)x, D, (const bf16_t*)w->g_attn, (bf16_t*)xa, D,
+                                (int)M, D, d->rms_eps, st));
+    if ((r = prefill_core(d, &w->attn, xa, B, T, rc, rs, x1, x, nullptr, nullptr, nullptr, 0, pl,
+                          st)))
+      return r;
+    LAUNCH("rmsnorm", rmsnorm_rows<bf16_t>((const bf16_t*)x1, D, (const bf16_t*)w->g_ffn, (bf16_t*)xf, D,
+                                (int)M, D, d->rms_eps, st));
+    GemmParams g = gp_base();
+    g.A = (const bf16_t*)xf; g.lda = D;
+    g.B = (const bf16_t*)w->w1; g.B2 = (const bf16_t*)w->w3; g.ldb = D;
+    g.C = hbuf; g.ldc = F; g.M = (int)M; g.N = 2 * F; g.K = D;
+    LAUNCH("gemm_swiglu", gemm_bf16(g, EPI_SWIGLU, -1, st));
+    GemmParams o = gp_base();
+    o.A = (const bf16_t*)hbuf; o.lda = F; o.B = (const bf16_t*)w->w2; o.ldb = F;
+    o.C = out; o.ldc = D; o.R = (const bf16_t*)x1; o.ldr = D;
+    o.M = (int)M; o.N = D; o.K = F;
+    LAUNCH("gemm_w2_resid", gemm_bf16(o, EPI_RESID, -1, st));
+    return MLA_OK;
+  }
+  LAUNCH("rmsnorm", rmsnorm_rows<float>((const float*)x, D, (const float*)w->g_attn, (float*)xa, D, (int)M,
+                             D, d->rms_eps, st));
+  if ((r = prefill_core(d, &w->attn, xa, B, T, rc, rs, x1, x, nullptr, nullptr, nullptr, 0, pl,
+                        st)))
+    return r;
+  LAUNCH("rmsnorm", rmsnorm_rows<float>((const float*)x1, D, (const float*)w->g_ffn, (float*)xf, D, (int)M,
+                             D, d->rms_eps, st));
+  float* hg = (float*)hbuf;
+  float* hu = hg + M * F;
+  float* hh = hu + M * F;
+  GemmF32Params g;
+  memset(&g, 0, sizeof g);
+  g.A = (const float*)xf; g.lda = D; g.B = (const float*)w->w1; g.ldb = D; g.C = hg; g.ldc = F;
+  g.M = (int)M; g.N = F; g.K = D; g.batch = 1; g.b_is_nk = 1;
+  LAUNCH("gemm_w1", gemm_f32(g, st));
+  g.B = (const float*)w->w3; g.C = hu;
+  LAUNCH("gemm_w3", gemm_f32(g, st));
+  LAUNCH("swiglu", swiglu_f32(hg, hu, hh, M * F, st));
+  GemmF32Params o;
+  memset(&o, 0, sizeof o);
+  o.A = hh; o.lda = F; o.B = (const float*)w->w2; o.ldb = F; o.C = (float*)out; o.ldc = D;
+  o.R = (const float*)x1; o.ldr = D; o.M = (int)M; o.N = D; o.K = F; o.batch = 1; o.b_is_nk = 1;
+  LAUNCH("gemm_w2_resid", gemm_f32(o, st));
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,254 @@
+// Row-wise and elementwise kernels of the MLA forward: the latent RMSNorms
+// with the shared-key RoPE, the block RMSNorms, the RoPE table, cache
+// scatters and split-K reductions.  All arithmetic is fp32; T is the storage
+// type (float or bf16).
+//
+// Sources (by page title and section):
+//  "Kimi K2 · Dense transformer block": equation list (RMSNorm of the block
+//    input and of the residual stream, RMSNorm of the query latent, RoPE of
+//    the shared rotary key with the table R of the in/out line).
+//  "Kimi K2 · Key-value compression": c^KV = x W_DKV, then RMSNorm; the joint
+//    projection's 576 outputs are split into the 512 latent and the 64-wide
+//    rotary key after the product (Explanation); the latent plus the rotary
+//    key is the 576-value cache entry.
+//  "Kimi K2 · Mix and project": code excerpt, where the cache update stores
+//    each head's assembled key and value.
+// RMSNorm is g * x / sqrt(mean(x^2) + eps); RoPE turns the consecutive pair
+// (2i, 2i+1) by t * base^(-2i/d_rope).
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+// Sum over the 256 threads of a block (4 waves); every thread gets the total.
+MLA_DEV float block_sum256(float v, float* red) {
+  v = warp_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void latent_norm_rope_kernel(LatentNormParams<T> p) {
+  extern __shared__ float row[];  // [q_lora + kv_lora + d_rope]
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int N1 = p.q_lora + p.kv_lora + p.d_rope;
+  float sq = 0.f, skv = 0.f;
+  for (int c = tid; c < N1; c += 256) {
+    float v = 0.f;
+    for (int s = 0; s < p.nsplit; ++s)  // fixed order: deterministic
+      v += p.part[(long)s * p.split_stride + (long)m * p.ld_part + c];
+    row[c] = v;
+    if (c < p.q_lora) sq += v * v;
+    else if (c < p.q_lora + p.kv_lora) skv += v * v;
+  }
+  const float tq = block_sum256(sq, red);
+  const float tkv = block_sum256(skv, red);
+  const float rq = 1.0f / sqrtf(tq / (float)p.q_lora + p.eps);
+  const float rkv = 1.0f / sqrtf(tkv / (float)p.kv_lora + p.eps);
+
+  const int t = m % p.rope_T;
+  const int pos = t + p.rope_pos0;
+  const int bseq = m / p.rope_T;
+  T* lat = p.latent_cache
+               ? p.latent_cache + ((long)bseq * p.L_cap + pos) * (p.kv_lora + p.d_rope)
+               : nullptr;
+
+  for (int c = tid; c < p.q_lora; c += 256)
+    p.cq[(long)m * p.ld_cq + c] = from_f<T>(to_f<T>(p.g_q[c]) * (row[c] * rq));
+  for (int c = tid; c < p.kv_lora; c += 256) {
+    T y = from_f<T>(to_f<T>(p.g_kv[c]) * (row[p.q_lora + c] * rkv));
+    p.ckv[(long)m * p.ld_ckv + c] = y;
+    if (lat) lat[c] = y;
+  }
+  const int npairs = p.d_rope / 2;
+  const float* kp = row + p.q_lora + p.kv_lora;
+  for (int i = tid; i < npairs; i += 256) {
+    float cs = p.rcos[(long)pos * p.n_pairs + i], sn = p.rsin[(long)pos * p.n_pairs + i];
+    float a = kp[2 * i], b = kp[2 * i + 1];
+    T y0 = from_f<T>(a * cs - b * sn), y1 = from_f<T>(a * sn + b * cs);
+    p.kr[(long)m * p.ld_kr + 2 * i] = y0;
+    p.kr[(long)m * p.ld_kr + 2 * i + 1] = y1;
+    if (lat) {
+      lat[p.kv_lora + 2 * i] = y0;
+      lat[p.kv_lora + 2 * i + 1] = y1;
+    }
+    if (p.k_cache) {
+      for (int h = 0; h < p.n_heads; ++h) {
+        T* kc = p.k_cache + (((long)bseq * p.n_heads + h) * p.L_cap + pos) * p.dqk + p.d_nope;
+        kc[2 * i] = y0;
+        kc[2 * i + 1] = y1;
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t latent_norm_rope(const LatentNormParams<T>& p, hipStream_t s) {
+  size_t shm = (size_t)(p.q_lora + p.kv_lora + p.d_rope) * sizeof(float);
+  hipLaunchKernelGGL(latent_norm_rope_kernel<T>, dim3(p.M), dim3(256), shm, s, p);
+  return hipGetLastError();
+}
+template hipError_t latent_norm_rope<float>(const LatentNormParams<float>&, hipStream_t);
+template hipError_t latent_norm_rope<bf16_t>(const LatentNormParams<bf16_t>&, hipStream_t);
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T* __restrict__ x, long ldx,
+                                                          const T* __restrict__ g, T* __restrict__ y,
+                                                          long ldy, int D, float eps) {
+  extern __shared__ float rowbuf[];
+  __shared__ float red[4];
+  const long m = blockIdx.x;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < D; c += 256) {
+    float v = to_f<T>(x[m * ldx + c]);
+    rowbuf[c] = v;
+    ss += v * v;
+  }
+  const float tot = block_sum256(ss, red);
+  const float r = 1.0f / sqrtf(tot / (float)D + eps);
+  for (int c = threadIdx.x; c < D; c += 256)
+    y[m * ldy + c] = from_f<T>(to_f<T>(g[c]) * (rowbuf[c] * r));
+}
+
+template <typename T>
+hipError_t rmsnorm_rows(const T* x, long ldx, const T* g, T* y, long ldy, int M, int D, float eps,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_rows_kernel<T>, dim3(M), dim3(256), (size_t)D * sizeof(float), s, x,
+                     ldx, g, y, ldy, D, eps);
+  return hipGetLastError();
+}
+template hipError_t rmsnorm_rows<float>(const float*, long, const float*, float*, long, int, int,
+                                        float, hipStream_t);
+template hipError_t rmsnorm_rows<bf16_t>(const bf16_t*, long, const bf16_t*, bf16_t*, long, int,
+                                         int, float, hipStream_t);
+
+// R [n_pos, n_pairs]: angle t * base^(-2i / (2 n_pairs)), evaluated in fp64
+// and stored as fp32.
+__global__ void rope_table_kernel(int n_pos, int n_pairs, double base, float* cs, float* sn) {
+  long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (long)n_pos * n_pairs) return;
+  int t = (int)(e / n_pairs), i = (int)(e % n_pairs);
+  double inv_freq = pow(base, -(2.0 * i) / (2.0 * n_pairs));
+  double ang = (double)t * inv_freq;
+  cs[e] = (float)cos(ang);
+  sn[e] = (float)sin(ang);
+}
+
+hipError_t rope_table(int n_pos, int n_pairs, double base, float* cos_out, float* sin_out,
+                      hipStream_t s) {
+  long n = (long)n_pos * n_pairs;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n_pos,
+                     n_pairs, base, cos_out, sin_out);
+  return hipGetLastError();
+}
+
+// In-place RoPE of the rotary columns of each head (fp32 path).
+__global__ void rope_inplace_f32_kernel(float* x, long ldx, int M, int nheads, int head_dim,
+                                        int rope_start, const float* rcos, const float* rsin,
+                                        int n_pairs, int rope_T, int rope_pos0) {
+  const int np = (head_dim - rope_start) / 2;
+  long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (long)M * nheads * np) return;
+  int i = (int)(e % np);
+  int h = (int)((e / np) % nheads);
+  long m = e / ((long)np * nheads);
+  int pos = (int)(m % rope_T) + rope_pos0;
+  float* v = x + m * ldx + (long)h * head_dim + rope_start + 2 * i;
+  float c = rcos[(long)pos * n_pairs + i], s = rsin[(long)pos * n_pairs + i];
+  float a = v[0], b = v[1];
+  v[0] = a * c - b * s;
+  v[1] = a * s + b * c;
+}
+
+hipError_t rope_inplace_f32(float* x, long ldx, int M, int ncols, int head_dim, int rope_start,
+                            const float* rcos, const float* rsin, int n_pairs, int rope_T,
+                            int rope_pos0, hipStream_t s) {
+  int nheads = ncols / head_dim;
+  long n = (long)M * nheads * ((head_dim - rope_start) / 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_inplace_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     x, ldx, M, nheads, head_dim, rope_start, rcos, rsin, n_pairs, rope_T,
+                     rope_pos0);
+  return hipGetLastError();
+}
+
+__global__ void swiglu_f32_kernel(const float* g, const float* u, float* h, long n) {
+  long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  float gv = g[e];
+  h[e] = gv / (1.f + expf(-gv)) * u[e];
+}
+
+hipError_t swiglu_f32(const float* g, const float* u, float* h, long n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g, u,
+                     h, n);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ void scatter_full_cache_kernel(const T* __restrict__ kv, const T* __restrict__ kr,
+                                          T* __restrict__ kc, T* __restrict__ vc, int T_, int pos0,
+                                          int L_cap, int H, int dn, int dr, int dv, long total) {
+  long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int W = dn + dr + dv;
+  int c = (int)(e % W);
+  int h = (int)((e / W) % H);
+  long m = e / ((long)W * H);
+  long b = m / T_;
+  int slot = (int)(m % T_) + pos0;
+  long base = ((b * H + h) * L_cap + slot);
+  const T* src = kv + (m * H + h) * (dn + dv);
+  if (c < dn) kc[base * (dn + dr) + c] = src[c];
+  else if (c < dn + dr) kc[base * (dn + dr) + c] = kr[m * dr + (c - dn)];
+  else vc[base * dv + (c - dn - dr)] = src[dn + (c - dn - dr)];
+}
+
+template <typename T>
+hipError_t scatter_full_cache(const T* kv, const T* kr, T* k_cache, T* v_cache, int Bn, int T_,
+                              int pos0, int L_cap, int H, int d_nope, int d_rope, int d_v,
+                              hipStream_t s) {
+  long total = (long)Bn * T_ * H * (d_nope + d_rope + d_v);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_full_cache_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, s, kv, kr, k_cache, v_cache, T_, pos0, L_cap, H, d_nope, d_rope, d_v, total);
+  return hipGetLastError();
+}
+template hipError_t scatter_full_cache<float>(const float*, const float*, float*, float*, int, int,
+                                              int, int, int, int, int, int, hipStream_t);
+template hipError_t scatter_full_cache<bf16_t>(const bf16_t*, const bf16_t*, bf16_t*, bf16_t*, int,
+                                               int, int, int, int, int, int, int, hipStream_t);
+
+template <typename T>
+__global__ void reduce_splits_kernel(const float* __restrict__ part, int nsplit, long stride, int M,
+                                     int N, T* __restrict__ out, long ldo) {
+  long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (long)M * N) return;
+  long m = e / N;
+  int n = (int)(e % N);
+  float v = 0.f;
+  for (int s = 0; s < nsplit; ++s) v += part[s * stride + e];
+  out[m * ldo + n] = from_f<T>(v);
+}
+
+template <typename T>
+hipError_t reduce_splits(const float* part, int nsplit, long split_stride, int M, int N, T* out,
+                         long ldo, hipStream_t s) {
+  long n = (long)M * N;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_splits_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     part, nsplit, split_stride, M, N, out, ldo);
+  return hipGetLastError();
+}
+template hipError_t reduce_splits<float>(const float*, int, long, int, int, float*, long,
+                                         hipStream_t);
+template hipError_t reduce_splits<bf16_t>(const float*, int, long, int, int, bf16_t*, long,
+                                          hipStream_t);
+
+}  // namespace mla

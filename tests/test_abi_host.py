@@ -1,0 +1,162 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function that include/mla.h declares,
+and reject bad arguments with the documented status codes before making any
+HIP call (the size checks of the "Kimi K2 · Mix and project" code excerpt
+become error codes here).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+mla = pytest.importorskip("head_latent_attention_fwd_amd")
+
+
+def _lib():
+    try:
+        return mla.load()
+    except mla.MLAError as e:
+        pytest.fail(f"libmla.so not built: {e}")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_\w+|dense_block_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("mla_prefill", "mla_decode_fullcache", "mla_decode_latentcache", "dense_block_fwd",
+              "mla_rope_table", "mla_status_string", "mla_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} declared in mla.h but not exported"
+
+
+def kimi(dtype="bf16"):
+    return mla.make_dims(7168, 64, 1536, 512, 128, 64, 128, d_ff=18432, dtype=dtype)
+
+
+def tiny(dtype="f32"):
+    return mla.make_dims(256, 4, 96, 64, 32, 16, 32, d_ff=512, dtype=dtype)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _w(**over):
+    w = mla.Weights(*[FAKE] * 7)
+    for k, v in over.items():
+        setattr(w, k, v)
+    return w
+
+
+def _prefill(L, d, w=None, x=FAKE, B=1, T=16, rc=FAKE, rs=FAKE, rows=16, out=FAKE, kc=None,
+             vc=None, lc=None, L_cap=0, ws=FAKE, wsb=None):
+    w = w or _w()
+    if wsb is None:
+        wsb = L.mla_prefill_workspace_size(ctypes.byref(d), B, T) if B > 0 and T > 0 else 0
+    return L.mla_prefill(ctypes.byref(d), ctypes.byref(w), x, B, T, rc, rs, rows, out, kc, vc, lc,
+                         L_cap, ws, wsb, None)
+
+
+def test_workspace_sizes_positive():
+    L = _lib()
+    for d in (kimi(), tiny()):
+        assert L.mla_prefill_workspace_size(ctypes.byref(d), 1, 2048) > 0
+        assert L.mla_decode_workspace_size(ctypes.byref(d), 64, 1001) > 0
+        assert L.dense_block_workspace_size(ctypes.byref(d), 1, 128) > 0
+    # bad shapes give 0
+    assert L.mla_prefill_workspace_size(ctypes.byref(kimi()), 0, 16) == 0
+    d = tiny()
+    d.n_heads = 0
+    assert L.mla_decode_workspace_size(ctypes.byref(d), 1, 16) == 0
+
+
+def test_null_pointers_rejected():
+    L = _lib()
+    d = tiny()
+    assert _prefill(L, d, x=None) == -1
+    assert _prefill(L, d, out=None) == -1
+    assert _prefill(L, d, ws=None) == -1
+    assert _prefill(L, d, rc=None) == -1
+    assert _prefill(L, d, w=_w(w_ukv=None)) == -1
+    assert L.mla_prefill(None, ctypes.byref(_w()), FAKE, 1, 1, FAKE, FAKE, 1, FAKE, None, None, None,
+                         0, FAKE, 1 << 30, None) == -1
+    assert "NULL" in L.mla_last_error().decode() or "null" in L.mla_last_error().decode().lower()
+    # k_cache without v_cache
+    assert _prefill(L, d, kc=FAKE, L_cap=16) == -1
+
+
+def test_bad_shapes_rejected():
+    L = _lib()
+    d = tiny()
+    assert _prefill(L, d, B=0) == -2
+    assert _prefill(L, d, T=-3) == -2
+    assert _prefill(L, d, rows=15) == -2          # rope table shorter than T
+    assert _prefill(L, d, kc=FAKE, vc=FAKE, L_cap=8) == -2   # cache smaller than T
+    d2 = tiny()
+    d2.qk_rope_dim = 15                             # odd rotary width
+    assert _prefill(L, d2) == -2
+    d3 = tiny()
+    d3.softmax_scale = float("nan")
+    assert _prefill(L, d3) == -2
+    # decode: P outside the cache
+    w = _w()
+    for P in (-1, 16):
+        st = L.mla_decode_fullcache(ctypes.byref(d), ctypes.byref(w), FAKE, 2, P, 16, FAKE, FAKE,
+                                    FAKE, FAKE, 64, FAKE, FAKE, 1 << 40, None)
+        assert st == -2
+    st = L.mla_decode_latentcache(ctypes.byref(d), ctypes.byref(w), FAKE, 2, 10, 16, FAKE, FAKE,
+                                  FAKE, 5, FAKE, FAKE, 1 << 40, None)   # rope rows 5 <= P
+    assert st == -2
+
+
+def test_unsupported_rejected():
+    L = _lib()
+    d = kimi()
+    d.qk_nope_dim = 96                              # bf16 path: Kimi head widths only
+    assert _prefill(L, d, wsb=1 << 40) == -3
+    d = kimi()
+    d.dtype = 7
+    assert _prefill(L, d, wsb=1 << 40) == -3
+    d = kimi()
+    d.kv_lora_rank = 448                            # bf16 latent decode needs 512
+    st = L.mla_decode_latentcache(ctypes.byref(d), ctypes.byref(_w()), FAKE, 2, 3, 16, FAKE, FAKE,
+                                  FAKE, 16, FAKE, FAKE, 1 << 40, None)
+    assert st == -3
+
+
+def test_small_workspace_rejected():
+    L = _lib()
+    d = kimi()
+    need = L.mla_prefill_workspace_size(ctypes.byref(d), 1, 64)
+    assert _prefill(L, d, T=64, rows=64, wsb=need - 1) == -4
+    assert "workspace" in L.mla_last_error().decode()
+    need = L.mla_decode_workspace_size(ctypes.byref(d), 4, 100)
+    st = L.mla_decode_fullcache(ctypes.byref(d), ctypes.byref(_w()), FAKE, 4, 5, 100, FAKE, FAKE,
+                                FAKE, FAKE, 100, FAKE, FAKE, need - 1, None)
+    assert st == -4
+
+
+def test_status_strings():
+    L = _lib()
+    for s in (0, -1, -2, -3, -4, -5):
+        assert L.mla_status_string(s).decode().startswith("MLA_")
+
+
+def test_binding_raises_without_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    d = tiny()
+    with pytest.raises((ValueError, TypeError)):
+        mla.mla_prefill(d, {}, torch.zeros(1, 4, 256), (torch.zeros(4, 8), torch.zeros(4, 8)))

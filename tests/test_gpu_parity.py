@@ -1,0 +1,304 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Bars: max|gpu - oracle| <= 1e-4 * max|oracle| for float32 workloads and
+<= 2e-2 * max|oracle| for bf16 workloads.  Sizes span several tiles with
+ragged tails; full-size workloads are checked on sampled outputs.
+"""
+import numpy as np
+import pytest
+
+from oracle import mla_ref as ref
+from tests import synth
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, bits_to_dev, dims_of, from_dev, log,
+                            oracle_weights, to_dev, weights_to_dev)
+
+torch = pytest.importorskip("torch")
+mla = pytest.importorskip("head_latent_attention_fwd_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+# Kimi K2 widths with smaller model/latent widths, for fast oracle runs that
+# still exercise the bf16 kernels' fixed head shapes.
+KIMI_NARROW = ref.MLADims(d_model=1024, n_heads=64, q_lora_rank=256, kv_lora_rank=512,
+                          qk_nope_dim=128, qk_rope_dim=64, v_head_dim=128, d_ff=1536)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mla.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _rope(od, n):
+    return mla.mla_rope_table(n, od.qk_rope_dim, od.rope_base, DEV)
+
+
+# ------------------------------------------------------------------ prefill
+@pytest.mark.parametrize("case", [
+    ("tiny_config", ref.TINY, 1, 16, "f32", 1001),
+    ("tiny_ragged", ref.TINY, 2, 37, "f32", 7),
+    ("kimi_narrow_bf16", KIMI_NARROW, 2, 200, "bf16", 11),
+    ("kimi_bf16_T130", ref.KIMI_K2, 1, 130, "bf16", 12),
+])
+def test_prefill(case):
+    name, od, B, T, dt, seed = case
+    log(f"[prefill {name}] B={B} T={T} dtype={dt} seed={seed}")
+    x, w = synth.prefill_inputs(od, B, T, seed, bf16=(dt == "bf16"))
+    want = ref.mla_prefill(od, oracle_weights(w), x.astype(np.float64))
+    d = dims_of(mla, od, dt)
+    got = mla.mla_prefill(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), _rope(od, T))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got), want, TOL_F32 if dt == "f32" else TOL_BF16, name)
+
+
+def test_prefill_kimi_full_size_sampled_rows():
+    """The Kimi K2 prefill workload itself (B=1, T=2048, bf16) in the launch
+    configuration the benchmark times; the oracle computes all keys/values
+    and a sample of query rows (first, last, and random)."""
+    od = ref.KIMI_K2
+    B, T = 1, 2048
+    log(f"[prefill kimi full] B={B} T={T} bf16")
+    x, w = synth.prefill_inputs(od, B, T, 1002, bf16=True)
+    rows = sorted(set([0, 1, 63, 64, 127, 128, 1000, T - 1] +
+                      list(np.random.default_rng(5).choice(T, 24, replace=False))))
+    want = ref.mla_prefill(od, oracle_weights(w), x.astype(np.float64), rows=rows)
+    d = dims_of(mla, od, "bf16")
+    got = mla.mla_prefill(d, weights_to_dev(w, "bf16", DEV), to_dev(x, "bf16", DEV), _rope(od, T))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got)[:, rows], want, TOL_BF16, "kimi prefill T=2048 sampled rows")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_prefill_writes_caches(dt):
+    od = ref.TINY if dt == "f32" else KIMI_NARROW
+    B, T, L_cap = 2, 70, 80
+    log(f"[prefill caches] dtype={dt} B={B} T={T} L_cap={L_cap}")
+    x, w = synth.prefill_inputs(od, B, T, 21, bf16=(dt == "bf16"))
+    _, p = ref.mla_prefill(od, oracle_weights(w), x.astype(np.float64), return_intermediates=True)
+    K, V = ref.full_cache_entries(od, p)
+    C = ref.latent_cache_entries(od, p)
+    d = dims_of(mla, od, dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    kc = torch.zeros(B, od.n_heads, L_cap, od.q_head_dim, dtype=tdt, device=DEV)
+    vc = torch.zeros(B, od.n_heads, L_cap, od.v_head_dim, dtype=tdt, device=DEV)
+    lc = torch.zeros(B, L_cap, od.kv_lora_rank + od.qk_rope_dim, dtype=tdt, device=DEV)
+    mla.mla_prefill(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), _rope(od, T),
+                    k_cache=kc, v_cache=vc, latent_cache=lc)
+    torch.cuda.synchronize()
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(from_dev(kc)[:, :, :T], K, tol, "k_cache")
+    assert_close(from_dev(vc)[:, :, :T], V, tol, "v_cache")
+    assert_close(from_dev(lc)[:, :T], C, tol, "latent_cache")
+    assert torch.count_nonzero(kc[:, :, T:]) == 0 and torch.count_nonzero(lc[:, T:]) == 0
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_prefill_causality_bitwise(dt):
+    """Perturbing tokens after position t leaves outputs 0..t bitwise equal."""
+    od = ref.TINY if dt == "f32" else KIMI_NARROW
+    B, T = 1, 150
+    x, w = synth.prefill_inputs(od, B, T, 31, bf16=(dt == "bf16"))
+    d = dims_of(mla, od, dt)
+    tw = weights_to_dev(w, dt, DEV)
+    rope = _rope(od, T)
+    a = mla.mla_prefill(d, tw, to_dev(x, dt, DEV), rope).clone()
+    for t in (0, 63, 64, 129):
+        y = x.copy()
+        y[:, t + 1:] = synth.bf16_round(y[:, t + 1:] * -1.5 + 0.25) if dt == "bf16" else y[:, t + 1:] * -1.5 + 0.25
+        b = mla.mla_prefill(d, tw, to_dev(y, dt, DEV), rope)
+        torch.cuda.synchronize()
+        assert torch.equal(a[:, :t + 1], b[:, :t + 1]), f"t={t}"
+        assert not torch.equal(a[:, t + 1:], b[:, t + 1:])
+
+
+def test_prefill_deterministic():
+    od = KIMI_NARROW
+    x, w = synth.prefill_inputs(od, 1, 300, 41, bf16=True)
+    d = dims_of(mla, od, "bf16")
+    tw = weights_to_dev(w, "bf16", DEV)
+    rope = _rope(od, 300)
+    xd = to_dev(x, "bf16", DEV)
+    a = mla.mla_prefill(d, tw, xd, rope).clone()
+    for _ in range(3):
+        assert torch.equal(a, mla.mla_prefill(d, tw, xd, rope))
+
+
+# ------------------------------------------------------------------- decode
+def _decode_full_case(od, B, P, L_cap, dt, seed, sample=None):
+    x, w, kc, vc = synth.decode_full_inputs(od, B, P, L_cap, seed, bf16=(dt == "bf16"))
+    d = dims_of(mla, od, dt)
+    kd, vd = bits_to_dev(kc, dt, DEV), bits_to_dev(vc, dt, DEV)
+    got = mla.mla_decode_fullcache(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), P, kd, vd,
+                                   _rope(od, P + 1))
+    torch.cuda.synchronize()
+    bs = list(range(B)) if sample is None else sample
+    kf = synth.as_f32(kc[bs], dt == "bf16").astype(np.float64)
+    vf = synth.as_f32(vc[bs], dt == "bf16").astype(np.float64)
+    want, kc2, vc2 = ref.mla_decode_fullcache(od, oracle_weights(w), x[bs].astype(np.float64), P, kf, vf)
+    return from_dev(got)[bs], want, kd, vd, kc2, vc2, bs
+
+
+@pytest.mark.parametrize("case", [
+    ("tiny_f32", ref.TINY, 3, 20, 24, "f32", 51),
+    ("tiny_f32_P0", ref.TINY, 2, 0, 4, "f32", 52),
+    ("kimi_narrow_bf16", KIMI_NARROW, 3, 300, 320, "bf16", 53),
+    ("kimi_bf16_long", ref.KIMI_K2, 2, 5000, 5001, "bf16", 54),
+])
+def test_decode_fullcache(case):
+    name, od, B, P, L_cap, dt, seed = case
+    log(f"[decode full {name}] B={B} P={P} L_cap={L_cap} dtype={dt}")
+    got, want, kd, vd, kc2, vc2, bs = _decode_full_case(od, B, P, L_cap, dt, seed)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(got, want, tol, name)
+    # slot P now holds the new token's key and value; other slots untouched
+    assert_close(from_dev(kd[:, :, P]), kc2[:, :, P], tol, "k_cache slot P")
+    assert_close(from_dev(vd[:, :, P]), vc2[:, :, P], tol, "v_cache slot P")
+    if P > 0:
+        np.testing.assert_array_equal(from_dev(kd[:, :, :P]), kc2[:, :, :P])
+
+
+def test_decode_fullcache_kimi_full_size_sampled():
+    """The full-cache decode workload: B=64, P=1000 (L=1001 keys), bf16;
+    oracle on a sample of sequences."""
+    od = ref.KIMI_K2
+    log("[decode full kimi] B=64 P=1000 bf16")
+    got, want, *_ = _decode_full_case(od, 64, 1000, 1001, "bf16", 1003, sample=[0, 17, 63])
+    assert_close(got, want, TOL_BF16, "decode full B=64 P=1000 sampled")
+
+
+def _decode_latent_case(od, B, P, L_cap, dt, seed, sample=None):
+    x, w, cc = synth.decode_latent_inputs(od, B, P, L_cap, seed, bf16=(dt == "bf16"))
+    d = dims_of(mla, od, dt)
+    cd = bits_to_dev(cc, dt, DEV)
+    got = mla.mla_decode_latentcache(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), P, cd,
+                                     _rope(od, P + 1))
+    torch.cuda.synchronize()
+    bs = list(range(B)) if sample is None else sample
+    cf = synth.as_f32(cc[bs], dt == "bf16").astype(np.float64)
+    want, cc2 = ref.mla_decode_latentcache(od, oracle_weights(w), x[bs].astype(np.float64), P, cf)
+    return from_dev(got)[bs], want, cd, cc2, bs
+
+
+@pytest.mark.parametrize("case", [
+    ("tiny_f32", ref.TINY, 3, 20, 24, "f32", 61),
+    ("tiny_f32_P0", ref.TINY, 2, 0, 3, "f32", 62),
+    ("kimi_narrow_bf16", KIMI_NARROW, 3, 700, 701, "bf16", 63),
+    ("kimi_bf16_ragged", ref.KIMI_K2, 5, 333, 400, "bf16", 64),
+])
+def test_decode_latentcache(case):
+    name, od, B, P, L_cap, dt, seed = case
+    log(f"[decode latent {name}] B={B} P={P} L_cap={L_cap} dtype={dt}")
+    got, want, cd, cc2, bs = _decode_latent_case(od, B, P, L_cap, dt, seed)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(got, want, tol, name)
+    assert_close(from_dev(cd[:, P]), cc2[:, P], tol, "latent cache slot P")
+
+
+def test_decode_latentcache_kimi_full_size_sampled():
+    """The latent-cache decode workload: B=32, P=8192 (L=8193), bf16."""
+    od = ref.KIMI_K2
+    log("[decode latent kimi] B=32 P=8192 bf16")
+    got, want, *_ = _decode_latent_case(od, 32, 8192, 8193, "bf16", 1004, sample=[0, 13, 31])
+    assert_close(got, want, TOL_BF16, "decode latent B=32 P=8192 sampled")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_absorbed_equals_full_on_gpu(dt):
+    """Latent decode and full-cache decode over the cache expanded from the
+    same latents agree (associativity), on the GPU."""
+    od = ref.TINY if dt == "f32" else KIMI_NARROW
+    B, P, L_cap = 2, 90, 96
+    log(f"[absorbed==full] dtype={dt}")
+    x, w, cc = synth.decode_latent_inputs(od, B, P, L_cap, 71, bf16=(dt == "bf16"))
+    cf = synth.as_f32(cc, dt == "bf16").astype(np.float64)
+    r, H, dn = od.kv_lora_rank, od.n_heads, od.qk_nope_dim
+    kv = (cf[..., :r] @ np.asarray(w["w_ukv"], np.float64).T).reshape(B, L_cap, H, -1)
+    K = np.concatenate([kv[..., :dn], np.broadcast_to(cf[:, :, None, r:], (B, L_cap, H, od.qk_rope_dim))], -1)
+    V = kv[..., dn:]
+    K = synth.bf16_round(K.astype(np.float32)) if dt == "bf16" else K.astype(np.float32)
+    V = synth.bf16_round(V.astype(np.float32)) if dt == "bf16" else V.astype(np.float32)
+    d = dims_of(mla, od, dt)
+    tw = weights_to_dev(w, dt, DEV)
+    rope = _rope(od, P + 1)
+    xd = to_dev(x, dt, DEV)
+    ol = mla.mla_decode_latentcache(d, tw, xd, P, bits_to_dev(cc, dt, DEV), rope)
+    kd = to_dev(np.ascontiguousarray(K.transpose(0, 2, 1, 3)), dt, DEV)
+    vd = to_dev(np.ascontiguousarray(V.transpose(0, 2, 1, 3)), dt, DEV)
+    of = mla.mla_decode_fullcache(d, tw, xd, P, kd, vd, rope)
+    torch.cuda.synchronize()
+    assert_close(from_dev(ol), from_dev(of), TOL_F32 if dt == "f32" else TOL_BF16, "absorbed vs full")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_prefill_last_row_equals_decode(dt):
+    """Decode at P = T-1 over caches written by a (T-1)-token prefill equals
+    the last row of a T-token prefill, for both cache forms (GPU only)."""
+    od = ref.TINY if dt == "f32" else KIMI_NARROW
+    B, T = 2, 66
+    log(f"[prefill==decode] dtype={dt}")
+    x, w = synth.prefill_inputs(od, B, T, 81, bf16=(dt == "bf16"))
+    d = dims_of(mla, od, dt)
+    tw = weights_to_dev(w, dt, DEV)
+    rope = _rope(od, T)
+    xd = to_dev(x, dt, DEV)
+    full = mla.mla_prefill(d, tw, xd, rope)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    kc = torch.zeros(B, od.n_heads, T, od.q_head_dim, dtype=tdt, device=DEV)
+    vc = torch.zeros(B, od.n_heads, T, od.v_head_dim, dtype=tdt, device=DEV)
+    lc = torch.zeros(B, T, od.kv_lora_rank + od.qk_rope_dim, dtype=tdt, device=DEV)
+    mla.mla_prefill(d, tw, xd[:, :T - 1].contiguous(), rope, k_cache=kc, v_cache=vc, latent_cache=lc)
+    xl = xd[:, T - 1].contiguous()
+    of = mla.mla_decode_fullcache(d, tw, xl, T - 1, kc, vc, rope)
+    ol = mla.mla_decode_latentcache(d, tw, xl, T - 1, lc, rope)
+    torch.cuda.synchronize()
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(from_dev(of), from_dev(full[:, -1]), tol, "full-cache decode vs prefill last row")
+    assert_close(from_dev(ol), from_dev(full[:, -1]), tol, "latent decode vs prefill last row")
+
+
+# -------------------------------------------------------------------- block
+@pytest.mark.parametrize("case", [
+    ("tiny_f32", ref.TINY, 2, 19, "f32", 91),
+    ("kimi_narrow_bf16", KIMI_NARROW, 1, 150, "bf16", 92),
+])
+def test_dense_block(case):
+    name, od, B, T, dt, seed = case
+    log(f"[block {name}] B={B} T={T} dtype={dt}")
+    x, w, blk = synth.block_inputs(od, B, T, seed, bf16=(dt == "bf16"))
+    bw = ref.BlockWeights(attn=oracle_weights(w), **{k: np.asarray(v, np.float64) for k, v in blk.items()})
+    want = ref.dense_block(od, bw, x.astype(np.float64))
+    d = dims_of(mla, od, dt)
+    got = mla.dense_block_fwd(d, weights_to_dev(w, dt, DEV), weights_to_dev(blk, dt, DEV),
+                              to_dev(x, dt, DEV), _rope(od, T))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got), want, TOL_F32 if dt == "f32" else TOL_BF16, name)
+
+
+def test_dense_block_kimi_sampled_rows():
+    """Kimi K2 block widths (d_ff 18432) at T=256, sampled rows."""
+    od = ref.KIMI_K2
+    B, T = 1, 256
+    log(f"[block kimi] B={B} T={T} bf16")
+    x, w, blk = synth.block_inputs(od, B, T, 1005, bf16=True)
+    rows = [0, 1, 100, 128, 200, T - 1]
+    bw = ref.BlockWeights(attn=oracle_weights(w), **{k: np.asarray(v, np.float64) for k, v in blk.items()})
+    want = ref.dense_block(od, bw, x.astype(np.float64), rows=rows)
+    d = dims_of(mla, od, "bf16")
+    got = mla.dense_block_fwd(d, weights_to_dev(w, "bf16", DEV), weights_to_dev(blk, "bf16", DEV),
+                              to_dev(x, "bf16", DEV), _rope(od, T))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got)[:, rows], want, TOL_BF16, "kimi block sampled rows")
+
+
+def test_rope_table_matches_definition():
+    """The device-built table against the oracle's float64 angles (float32 storage)."""
+    c, s = mla.mla_rope_table(8192, 64, 10000.0, DEV)
+    oc, os_ = ref.rope_angles(np.arange(8192), 64, 10000.0)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(c.cpu().numpy() - oc)) < 1e-6
+    assert np.max(np.abs(s.cpu().numpy() - os_)) < 1e-6
