@@ -9,8 +9,8 @@
 // with no transposition anywhere.
 //
 // Tile: BM x BN x 64, WM x WN waves, each wave (BM/WM) x (BN/WN) built from
-// 32x32 MFMA blocks.  Two LDS stages: the next K tile's global loads are in
-// flight while the current one is multiplied.  Split-K writes fp32 partials
+// 32x32 MFMA blocks.  Two LDS stages and two MFMA-fragment register sets form
+// a software pipeline (see the main loop).  Split-K writes fp32 partials
 // whose consumer sums them in a fixed order (deterministic).
 //
 // Epilogues (fused, lane-local):
@@ -28,6 +28,15 @@
 
 namespace mla {
 
+#define MLA_SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+enum { SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200 };
+
+// LDS swizzle of the 16-byte chunk of a 128-byte tile row.  gfx950 serves a
+// ds_read_b128 16 lanes at a time from 64 banks (256 bytes), so the 16 rows a
+// half-wave reads must land on 16 distinct 16-byte bank groups: even and odd
+// rows share a 256-byte line, and (row >> 1) spreads eight line pairs.
+MLA_DEV int gemm_swz(int r) { return (r >> 1) & 7; }
+
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
   constexpr int NT = WM * WN * 64;
@@ -36,6 +45,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
   constexpr int ROWS_PER_PASS = NT / 8;               // 8 threads x 16 B cover one 64-wide K row
   constexpr int A_CH = BM / ROWS_PER_PASS;
   constexpr int B_CH = BN / ROWS_PER_PASS;
+  constexpr int NLD = A_CH + B_CH;                    // 16-byte loads per thread per K tile
+  constexpr int NMF = FM * FN;                        // MFMAs per wave per 16-wide K step
+  constexpr int NRD = FM + FN;                        // fragment reads per K step
   static_assert(FM >= 1 && FN >= 1, "wave tile");
   static_assert(A_CH >= 1 && B_CH >= 1, "tile too small for the block");
   static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU pairs 32-column blocks inside a wave");
@@ -96,29 +108,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
     }
     b_off[i] = src * (int)p.ldb + ch * 8 + k_begin;
   }
+  // LDS slots this thread stores into (u32x4 units)
+  int st_idx[NLD];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int r = tid / 8 + i * ROWS_PER_PASS;
+    st_idx[i] = r * 8 + (ch ^ gemm_swz(r));
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int r = tid / 8 + i * ROWS_PER_PASS;
+    st_idx[A_CH + i] = (BM + r) * 8 + (ch ^ gemm_swz(r));
+  }
 
-  u32x4 ra[A_CH], rb[B_CH];
-#define GEMM_GLOAD(koff)                                                              \
-  do {                                                                                \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                  \
-        ra[i] = *(const u32x4*)(A + a_off[i] + (koff));                                \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                \
-      const bf16_t* src_ = ((b2mask >> i) & 1) ? B2 : B;                               \
-      rb[i] = *(const u32x4*)(src_ + b_off[i] + (koff));                               \
-    }                                                                                 \
-  } while (0)
-#define GEMM_SSTORE(buf)                                                              \
-  do {                                                                                \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                \
-      const int r_ = tid / 8 + i * ROWS_PER_PASS;                                      \
-      lds[buf][r_ * 8 + (ch ^ (r_ & 7))] = ra[i];                                      \
-    }                                                                                 \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                \
-      const int r_ = tid / 8 + i * ROWS_PER_PASS;                                      \
-      lds[buf][(BM + r_) * 8 + (ch ^ (r_ & 7))] = rb[i];                               \
-    }                                                                                 \
-  } while (0)
-
+  // Software pipeline: the K tile in LDS buffer `cur` is multiplied in four
+  // 16-wide steps while (step 0) the next tile's global loads are issued,
+  // (steps 0-2) the next step's MFMA fragments are read from LDS into the
+  // other fragment register set, and (step 3) the next tile is stored to the
+  // other LDS buffer, one barrier is passed and its first fragments are read.
+  // sched_group_barrier interleaves those memory instructions with the MFMAs
+  // so the matrix pipe is never left waiting on a load issued just before.
+  u32x4 stg[NLD];
+  bf16x8 fa[2][FM], fb[2][FN];
   floatx16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -128,39 +139,95 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int lr = lane & 31, lg = lane >> 5;
+#define GEMM_GLOAD(kt_)                                                                   \
+  do {                                                                                    \
+    const int ko_ = (kt_) * 64;                                                           \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                      \
+        stg[i] = *(const u32x4*)(A + a_off[i] + ko_);                                      \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                    \
+      const bf16_t* src_ = ((b2mask >> i) & 1) ? B2 : B;                                   \
+      stg[A_CH + i] = *(const u32x4*)(src_ + b_off[i] + ko_);                              \
+    }                                                                                     \
+  } while (0)
+#define GEMM_SSTORE(buf)                                                                  \
+  do {                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < NLD; ++i) lds[buf][st_idx[i]] = stg[i];         \
+  } while (0)
+#define GEMM_FREAD(buf, s, slot)                                                          \
+  do {                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                      \
+      const int r = wm * WTM + i * 32 + lr;                                               \
+      fa[slot][i] = __builtin_bit_cast(bf16x8, lds[buf][r * 8 + ((2 * (s) + lg) ^ gemm_swz(r))]); \
+    }                                                                                     \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                      \
+      const int r = wn * WTN + j * 32 + lr;                                               \
+      fb[slot][j] = __builtin_bit_cast(bf16x8, lds[buf][(BM + r) * 8 + ((2 * (s) + lg) ^ gemm_swz(r))]); \
+    }                                                                                     \
+  } while (0)
+#define GEMM_MFMAS(slot, lo, hi)                                                          \
+  do {                                                                                    \
+    _Pragma("unroll") for (int q = (lo); q < (hi); ++q) {                                 \
+      const int i = q / FN, j = q % FN;                                                   \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0); \
+    }                                                                                     \
+  } while (0)
+
   if (nk > 0) {
     GEMM_GLOAD(0);
     GEMM_SSTORE(0);
   }
   __syncthreads();
+  if (nk > 0) GEMM_FREAD(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) GEMM_GLOAD((kt + 1) * 64);
+    const int cur = kt & 1, nxt = cur ^ 1;
+    const int kn = min(kt + 1, nk - 1);  // the last iteration reloads a valid tile
+    // step 0
+    GEMM_GLOAD(kn);
+    GEMM_FREAD(cur, 1, 1);
+    GEMM_MFMAS(0, 0, NMF);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        int r = wm * WTM + i * 32 + lr;
-        u32x4 v = lds[cur][r * 8 + ((2 * s + lg) ^ (r & 7))];
-        af[i] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        int r = wn * WTN + j * 32 + lr;
-        u32x4 v = lds[cur][(BM + r) * 8 + ((2 * s + lg) ^ (r & 7))];
-        bfr[j] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < NMF; ++q) {
+      MLA_SGB(SG_MFMA, 1);
+      if (q < NLD) MLA_SGB(SG_VMEM_RD, (NLD + NMF - 1) / NMF);
+      if (q < NRD) MLA_SGB(SG_DS_RD, (NRD + NMF - 1) / NMF);
     }
-    if (kt + 1 < nk) GEMM_SSTORE(cur ^ 1);
+    // step 1
+    GEMM_FREAD(cur, 2, 0);
+    GEMM_MFMAS(1, 0, NMF);
+#pragma unroll
+    for (int q = 0; q < NMF; ++q) {
+      MLA_SGB(SG_MFMA, 1);
+      MLA_SGB(SG_DS_RD, (NRD + NMF - 1) / NMF);
+    }
+    // step 2
+    GEMM_FREAD(cur, 3, 1);
+    GEMM_MFMAS(0, 0, NMF);
+#pragma unroll
+    for (int q = 0; q < NMF; ++q) {
+      MLA_SGB(SG_MFMA, 1);
+      MLA_SGB(SG_DS_RD, (NRD + NMF - 1) / NMF);
+    }
+    // step 3: store the next tile under half the MFMAs, barrier, read its
+    // first fragments under the other half
+    GEMM_SSTORE(nxt);
+    GEMM_MFMAS(1, 0, NMF / 2);
+#pragma unroll
+    for (int q = 0; q < NMF / 2; ++q) {
+      MLA_SGB(SG_MFMA, 1);
+      MLA_SGB(SG_DS_WR, (2 * NLD + NMF - 1) / NMF);
+    }
     __syncthreads();
+    GEMM_FREAD(nxt, 0, 0);
+    GEMM_MFMAS(1, NMF / 2, NMF);
+#pragma unroll
+    for (int q = 0; q < NMF / 2; ++q) {
+      MLA_SGB(SG_MFMA, 1);
+      MLA_SGB(SG_DS_RD, (2 * NRD + NMF - 1) / NMF);
+    }
   }
 
+#undef GEMM_FREAD
+#undef GEMM_MFMAS
 #undef GEMM_GLOAD
 #undef GEMM_SSTORE
 
@@ -238,21 +305,21 @@ static hipError_t launch_cfg(GemmParams p, hipStream_t s) {
 template <int EPI>
 static hipError_t launch_epi(GemmParams p, int cfg, hipStream_t s) {
   switch (cfg) {
-    case GEMM_CFG_256x256:
-      if (EPI == EPI_ROPE) return hipErrorInvalidValue;
-      return launch_cfg<256, 256, 2, 2, (EPI == EPI_ROPE ? EPI_BF16 : EPI)>(p, s);
+    case GEMM_CFG_256x256: return launch_cfg<256, 256, 2, 4, EPI>(p, s);
     case GEMM_CFG_128x128: return launch_cfg<128, 128, 2, 2, EPI>(p, s);
     case GEMM_CFG_64x128: return launch_cfg<64, 128, 1, 2, EPI>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-// Tile choice: the largest tile that still gives every CU work; small-M
-// (decode) products use a 64-row tile whose B stream dominates.
-int gemm_pick_cfg(int M, int N, int batch) {
+// Tile choice (measured on MI355X over the projection shapes): the 256x256
+// eight-wave tile wins when K is long enough to amortise its prologue and
+// there are enough tiles to cover the CUs; otherwise 128x128.  Small-M
+// (decode) products use a 64-row tile whose weight stream dominates.
+int gemm_pick_cfg(int M, int N, int K, int batch) {
   if (M <= 64) return GEMM_CFG_64x128;
   long t256 = (long)((M + 255) / 256) * ((N + 255) / 256) * batch;
-  if (t256 >= 200) return GEMM_CFG_256x256;
+  if (t256 >= 200 && K >= 4096) return GEMM_CFG_256x256;
   return GEMM_CFG_128x128;
 }
 
@@ -260,18 +327,16 @@ hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s) {
   if (p.batch <= 0) p.batch = 1;
   if (p.ksplit <= 0) p.ksplit = 1;
   if (p.kchunk <= 0) p.kchunk = p.K;
-  if (cfg < 0) cfg = gemm_pick_cfg(p.M, p.N, p.batch * p.ksplit);
+  if (cfg < 0) cfg = gemm_pick_cfg(p.M, p.N, p.kchunk, p.batch * p.ksplit);
   switch (epi) {
     case EPI_F32: return launch_epi<EPI_F32>(p, cfg, s);
     case EPI_BF16: return launch_epi<EPI_BF16>(p, cfg, s);
-    case EPI_ROPE:
-      // the 256x256 tile runs out of registers for the rotary epilogue
-      return launch_epi<EPI_ROPE>(p, cfg == GEMM_CFG_256x256 ? GEMM_CFG_128x128 : cfg, s);
+    case EPI_ROPE: return launch_epi<EPI_ROPE>(p, cfg, s);
     case EPI_RESID: return launch_epi<EPI_RESID>(p, cfg, s);
     case EPI_SWIGLU:
       if (cfg == GEMM_CFG_64x128) return launch_cfg<64, 128, 1, 2, EPI_SWIGLU>(p, s);
       if (cfg == GEMM_CFG_128x128) return launch_cfg<128, 128, 2, 2, EPI_SWIGLU>(p, s);
-      return launch_cfg<256, 256, 2, 2, EPI_SWIGLU>(p, s);
+      return launch_cfg<256, 256, 2, 4, EPI_SWIGLU>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

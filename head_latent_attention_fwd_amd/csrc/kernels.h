@@ -32,7 +32,7 @@ struct GemmParams {
   int tiles_m, tiles_n;  // filled by the launcher
 };
 
-int gemm_pick_cfg(int M, int N, int batch);
+int gemm_pick_cfg(int M, int N, int K, int batch);
 hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s);
 
 // fp32 generic GEMM: C[b] = (R ? R : 0) + A[b] . op(B[b]); op(B) = B^T when

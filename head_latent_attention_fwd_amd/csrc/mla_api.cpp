@@ -153,7 +153,7 @@ int check_i32(long elems, const char* what) {
 
 // Split-K plan for the bf16 GEMM: enough workgroups to cover the CUs.
 void plan_splitk(int M, int N, int K, int* S, int* kchunk) {
-  int cfg = gemm_pick_cfg(M, N, 1);
+  int cfg = gemm_pick_cfg(M, N, K, 1);
   int bm = cfg == GEMM_CFG_256x256 ? 256 : (cfg == GEMM_CFG_128x128 ? 128 : 64);
   int bn = cfg == GEMM_CFG_256x256 ? 256 : 128;
   long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
