@@ -8,8 +8,10 @@
 // [B*T, H*128] (column h*128 + c) that o_proj reads.
 //
 // Design (CDNA4):
-//  * 256 threads, 4 waves, 128 queries per workgroup (32 per wave), key
-//    tiles of 64.  Scores are formed transposed, S^T = K . Q^T, with
+//  * 512 threads = 8 waves, 256 queries per workgroup (32 per wave), key
+//    tiles of 64.  Registers stay within 256 per lane so two waves share each
+//    SIMD: one wave's softmax (VALU) overlaps the other's MFMAs.
+//  * Scores are formed transposed, S^T = K . Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K rows are the A operand (K-contiguous rows in
 //    LDS) and the wave's queries are the B operand, held in registers for the
 //    whole loop.  Each lane then owns one query column, so the softmax
@@ -20,18 +22,33 @@
 //    each group of 16 so that a lane's 8 keys are one 16-byte read.
 //  * The shared rotary key k^R is loaded once per key into the 64 rotary
 //    columns of the K tile (never replicated per head in memory).
-//  * Two LDS stages (K 24 KB + V^T 16 KB each): the next tile's global loads
-//    are in flight during the MFMAs.  Query tiles are issued longest-first;
-//    heads map to XCD h % 8, so all query tiles of a head share one L2.
+//  * Softmax in the log2 domain with the scale folded into one FMA before
+//    v_exp_f32.  The running maximum is only raised when a tile's maximum
+//    exceeds it by more than 2^8 (exact: numerator and denominator share the
+//    reference point; values stay below 2^8 * 64 per tile), so the O rescale
+//    is skipped for most tiles.
+//  * LDS swizzles are for 64 banks (gfx950 serves ds_read_b128 16 lanes at a
+//    time from 256 bytes).  Two LDS stages (K 24 KB + V^T 16 KB each): the
+//    next tile's global loads are in flight during the MFMAs.  Query tiles are
+//    issued longest-first; heads map to XCD h % 8, so all query tiles of a
+//    head share one L2.
 #include "common.h"
 #include "kernels.h"
 
 namespace mla {
 
 namespace {
-constexpr int KCH = 24;  // 16-byte chunks per K row (192 bf16)
+constexpr int KCH = 24;   // 16-byte chunks per K row (192 bf16)
+constexpr int BQ = 256;   // queries per workgroup
+constexpr int NW = 8;     // waves per workgroup
+constexpr float LAZY = 8.0f;  // raise the running max only past this margin (log2 units)
 
-MLA_DEV int kphys(int c, int row) { return (c & ~7) | ((c ^ row) & 7); }
+// K row = 384 bytes = 1.5 lines of 256 bytes.  Rows r and r + 2 start on the
+// same bank group offset parity; XOR the chunk's low 3 bits with (r >> 1) so
+// the 16 rows a half-wave reads hit 16 distinct 16-byte bank groups.
+MLA_DEV int kphys(int c, int row) { return (c & ~7) | ((c ^ (row >> 1)) & 7); }
+// V^T row = 128 bytes: pairs of rows share a 256-byte line.
+MLA_DEV int vswz(int dv) { return (dv >> 1) & 7; }
 
 // position of key offset k (0..63) inside a V^T row (see header comment)
 MLA_DEV int vpos(int k) {
@@ -40,18 +57,18 @@ MLA_DEV int vpos(int k) {
 }
 }  // namespace
 
-__global__ __launch_bounds__(256) void flash_prefill_kernel(FlashParams p) {
+__global__ __launch_bounds__(512) void flash_prefill_kernel(FlashParams p) {
   __shared__ u32x4 Ks[2][64 * KCH];
   __shared__ u32x4 Vt[2][128 * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
-  const int nqt = (p.T + 127) / 128;
+  const int nqt = (p.T + BQ - 1) / BQ;
   const int HB = p.H * p.B;
   const int qt = nqt - 1 - (int)(blockIdx.x / HB);
   const int rem = blockIdx.x % HB;
   const int h = rem % p.H, b = rem / p.H;
-  const int q0 = qt * 128;
+  const int q0 = qt * BQ;
   const long rowbase = (long)b * p.T;
   const long HS = p.H;
 
@@ -64,45 +81,45 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashParams p) {
     for (int s = 0; s < 12; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 16 * s));
   }
 
-  const int qlast = min(q0 + 127, p.T - 1);
+  const int qlast = min(q0 + BQ - 1, p.T - 1);
   const int n_kv = qlast / 64 + 1;
 
-  u32x4 rk[6], rv[4];
+  // loaders: K tile = 64 rows x 24 chunks (3 per thread); V tile = 32 key
+  // pairs x 16 chunks (one pair per thread)
+  u32x4 rk[3], rv[2];
 #define FP_LOAD(kv0)                                                                      \
   do {                                                                                    \
-    _Pragma("unroll") for (int i = 0; i < 6; ++i) {                                       \
-      const int e = tid + 256 * i, row = e / KCH, c = e % KCH;                            \
+    _Pragma("unroll") for (int i = 0; i < 3; ++i) {                                       \
+      const int e = tid + 512 * i, row = e / KCH, c = e % KCH;                            \
       const long key = rowbase + min((kv0) + row, p.T - 1);                               \
       const bf16_t* src = c < 16 ? p.kv + (key * HS + h) * 256 + 8 * c                    \
                                  : p.kr + key * 64 + 8 * (c - 16);                        \
       rk[i] = *(const u32x4*)src;                                                         \
     }                                                                                     \
-    _Pragma("unroll") for (int it = 0; it < 2; ++it) {                                    \
-      const int kp = tid & 31, c = (tid >> 5) + 8 * it;                                   \
+    {                                                                                     \
+      const int kp = tid & 31, c = tid >> 5;                                              \
       const long k0 = rowbase + min((kv0) + 2 * kp, p.T - 1);                             \
       const long k1 = rowbase + min((kv0) + 2 * kp + 1, p.T - 1);                         \
-      rv[2 * it] = *(const u32x4*)(p.kv + (k0 * HS + h) * 256 + 128 + 8 * c);             \
-      rv[2 * it + 1] = *(const u32x4*)(p.kv + (k1 * HS + h) * 256 + 128 + 8 * c);         \
+      rv[0] = *(const u32x4*)(p.kv + (k0 * HS + h) * 256 + 128 + 8 * c);                  \
+      rv[1] = *(const u32x4*)(p.kv + (k1 * HS + h) * 256 + 128 + 8 * c);                  \
     }                                                                                     \
   } while (0)
 #define FP_STORE(buf)                                                                     \
   do {                                                                                    \
-    _Pragma("unroll") for (int i = 0; i < 6; ++i) {                                       \
-      const int e = tid + 256 * i, row = e / KCH, c = e % KCH;                            \
+    _Pragma("unroll") for (int i = 0; i < 3; ++i) {                                       \
+      const int e = tid + 512 * i, row = e / KCH, c = e % KCH;                            \
       Ks[buf][row * KCH + kphys(c, row)] = rk[i];                                         \
     }                                                                                     \
     uint32_t* vt32 = (uint32_t*)&Vt[buf][0];                                              \
-    _Pragma("unroll") for (int it = 0; it < 2; ++it) {                                    \
-      const int kp = tid & 31, c = (tid >> 5) + 8 * it;                                   \
-      const int pos = vpos(2 * kp);                                                       \
-      _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
-        const int dv = 8 * c + i;                                                         \
-        const uint32_t w0 = rv[2 * it][i >> 1], w1 = rv[2 * it + 1][i >> 1];              \
-        const uint32_t val = (i & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))                  \
-                                     : ((w0 & 0xffffu) | (w1 << 16));                     \
-        const int ph = (((pos >> 3) ^ (dv & 7)) << 3) | (pos & 7);                        \
-        vt32[(dv * 64 + ph) >> 1] = val;                                                  \
-      }                                                                                   \
+    const int kp = tid & 31, c = tid >> 5;                                                \
+    const int pos = vpos(2 * kp);                                                         \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                       \
+      const int dv = 8 * c + i;                                                           \
+      const uint32_t w0 = rv[0][i >> 1], w1 = rv[1][i >> 1];                              \
+      const uint32_t val = (i & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))                    \
+                                   : ((w0 & 0xffffu) | (w1 << 16));                       \
+      const int ph = (((pos >> 3) ^ vswz(dv)) << 3) | (pos & 7);                          \
+      vt32[(dv * 64 + ph) >> 1] = val;                                                    \
     }                                                                                     \
   } while (0)
 
@@ -112,6 +129,7 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) O[d][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = p.scale_log2;
   const int qi = q0 + 32 * w + lr;
   const int wq_first = q0 + 32 * w, wq_last = wq_first + 31;
 
@@ -136,36 +154,47 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashParams p) {
           S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], S[mb], 0, 0, 0);
         }
       }
+      // scores in log2 units: sl2 * S; masked keys (after the query) -> -inf
       const bool diag = kv0 + 63 > wq_first;
       float tmax = -INFINITY;
+      if (diag) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float v = S[mb][e] * p.scale_log2;
-          const int key = kv0 + 32 * mb + 8 * (e >> 2) + 4 * lg + (e & 3);
-          if (diag && key > qi) v = -INFINITY;
-          S[mb][e] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = exp2f(m_run - m_new);
+          for (int e = 0; e < 16; ++e) {
+            const int key = kv0 + 32 * mb + 8 * (e >> 2) + 4 * lg + (e & 3);
+            if (key > qi) S[mb][e] = -INFINITY;
+            tmax = fmaxf(tmax, S[mb][e]);
+          }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, S[mb][e]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sl2;
+      // lazy running max: only move it when the tile max is far above it
+      const bool raise = tmax > m_run + LAZY;
+      const float m_new = raise ? tmax : m_run;
+      if (__any(raise)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 for unchanged lanes
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) O[d][e] *= alpha;
+      }
+      m_run = m_new;
       float psum = 0.f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float pv = exp2f(S[mb][e] - m_new);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(S[mb][e], sl2, -m_new));
           S[mb][e] = pv;
           psum += pv;
         }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) O[d][e] *= alpha;
+      l_run += psum;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -177,7 +206,7 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashParams p) {
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
             const int dv = 32 * d + lr;
-            const bf16x8 a = __builtin_bit_cast(bf16x8, Vt[cur][dv * 8 + ((2 * ks + lg) ^ (dv & 7))]);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, Vt[cur][dv * 8 + ((2 * ks + lg) ^ vswz(dv))]);
             O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, O[d], 0, 0, 0);
           }
         }
@@ -205,8 +234,8 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashParams p) {
 }
 
 hipError_t flash_prefill_bf16(const FlashParams& p, hipStream_t s) {
-  const int nqt = (p.T + 127) / 128;
-  hipLaunchKernelGGL(flash_prefill_kernel, dim3(nqt * p.H * p.B), dim3(256), 0, s, p);
+  const int nqt = (p.T + BQ - 1) / BQ;
+  hipLaunchKernelGGL(flash_prefill_kernel, dim3(nqt * p.H * p.B), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
