@@ -42,7 +42,7 @@ def prefill_kernel_flops(B, T, k=KIMI):
     n1 = k["q_lora_rank"] + k["kv_lora_rank"] + k["qk_rope_dim"]
     return {
         "gemm_down": 2.0 * M * n1 * k["d_model"],
-        "gemm_q_up_rope": 2.0 * M * H * dqk * k["q_lora_rank"],
+        "gemm_q_up": 2.0 * M * H * dqk * k["q_lora_rank"],
         "gemm_kv_up": 2.0 * M * H * (k["qk_nope_dim"] + k["v_head_dim"]) * k["kv_lora_rank"],
         "flash_prefill": 2.0 * H * B * (T * (T + 1) / 2) * (dqk + k["v_head_dim"]),
         "gemm_o_proj": 2.0 * M * k["d_model"] * H * k["v_head_dim"],
@@ -267,7 +267,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode_full", "decode_latent", "block"])
+    ap.add_argument("--only", choices=["prefill", "decode_full", "decode_latent", "block", "copy"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -286,6 +286,16 @@ def main():
     def flush():
         flush_buf.fill_(1)   # 1 GiB write evicts the 256 MB Infinity Cache
 
+    if args.only == "copy":
+        # calibration for HBM byte counters: a plain device copy of known size
+        n = 1 << 28                                 # 256 Mi bf16 = 512 MiB each way
+        src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 2, "launches": args.steps}))
+        return
     if args.only and args.only != "prefill":
         d, w, _ = make_weights(torch, dev, KIMI, 1002)
         fn = {"decode_full": lambda: bench_decode_full(torch, mla, dev, d, w, args.steps, args.warmup, flush),

@@ -64,3 +64,19 @@ MLA_DEV int xcd_remap(int b, int nblocks) {
 }
 
 #define MLA_LDS __attribute__((address_space(3)))
+
+// RoPE of 8 consecutive bf16 features (4 pairs (2i, 2i+1), pair index
+// pair0 + i) at table row `pos`: (a, b) -> (a cos - b sin, a sin + b cos),
+// computed in fp32 and rounded back to bf16.
+MLA_DEV u32x4 rope8_bf16(u32x4 v, const float* __restrict__ rcos, const float* __restrict__ rsin,
+                         long pos, int n_pairs, int pair0) {
+  const floatx4 c = *(const floatx4*)(rcos + pos * n_pairs + pair0);
+  const floatx4 s = *(const floatx4*)(rsin + pos * n_pairs + pair0);
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = lo_bf(v[i]), b = hi_bf(v[i]);
+    o[i] = pack2bf(a * c[i] - b * s[i], a * s[i] + b * c[i]);
+  }
+  return o;
+}

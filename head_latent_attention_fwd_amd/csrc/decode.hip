@@ -60,7 +60,9 @@ __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullParams p) {
   float qf[24];
 #pragma unroll
   for (int c = 0; c < 3; ++c) {
-    const u32x4 v = *(const u32x4*)(qp + 64 * c + 8 * g8);
+    u32x4 v = *(const u32x4*)(qp + 64 * c + 8 * g8);
+    // chunk 2 holds rotary features 8*g8 .. +8: rotate by the token's position
+    if (c == 2) v = rope8_bf16(v, p.rcos, p.rsin, p.L - 1, 32, 4 * g8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       qf[8 * c + 2 * i] = lo_bf(v[i]);
@@ -206,7 +208,9 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
     const int f = 32 * s + 8 * g4;
     const bf16_t* src = f < 512 ? p.q_abs + ((long)b * p.H + head) * 512 + f
                                 : p.q + ((long)b * p.H + head) * 192 + 128 + (f - 512);
-    qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)src);
+    u32x4 v = *(const u32x4*)src;
+    if (f >= 512) v = rope8_bf16(v, p.rcos, p.rsin, p.L - 1, 32, (f - 512) / 2);
+    qf[s] = __builtin_bit_cast(bf16x8, v);
   }
   const bf16_t* cb = p.cache + (long)b * p.L_cap * 576;
 

@@ -5,7 +5,8 @@
 // sequence b, head h and query i, scores s_ij = scale * [Q^C ; Q^R]_i .
 // [K^C_h ; k^R]_j over keys j <= i, a float32 softmax over j, and
 // O_i = sum_j p_ij V_h,j, written straight into the head-merged layout
-// [B*T, H*128] (column h*128 + c) that o_proj reads.
+// [B*T, H*128] (column h*128 + c) that o_proj reads.  RoPE of the query's
+// rotary part is applied here, as the query fragments are loaded.
 //
 // Design (CDNA4):
 //  * 512 threads = 8 waves, 256 queries per workgroup (32 per wave), key
@@ -72,13 +73,19 @@ __global__ __launch_bounds__(512) void flash_prefill_kernel(FlashParams p) {
   const long rowbase = (long)b * p.T;
   const long HS = p.H;
 
-  // this wave's queries as MFMA B fragments: features 16 s + 8 lg .. +8
+  // this wave's queries as MFMA B fragments: features 16 s + 8 lg .. +8.
+  // The rotary features (s >= 8) are rotated here by the RoPE table row of
+  // the query's position: each fragment holds 4 whole (2i, 2i+1) pairs.
   bf16x8 qf[12];
   {
     const int qrow = min(q0 + 32 * w + lr, p.T - 1);
     const bf16_t* qp = p.q + ((rowbase + qrow) * HS + h) * 192 + 8 * lg;
 #pragma unroll
-    for (int s = 0; s < 12; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 16 * s));
+    for (int s = 0; s < 12; ++s) {
+      u32x4 v = *(const u32x4*)(qp + 16 * s);
+      if (s >= 8) v = rope8_bf16(v, p.rcos, p.rsin, qrow, 32, (16 * s + 8 * lg - 128) / 2);
+      qf[s] = __builtin_bit_cast(bf16x8, v);
+    }
   }
 
   const int qlast = min(q0 + BQ - 1, p.T - 1);

@@ -13,12 +13,10 @@
 // a software pipeline (see the main loop).  Split-K writes fp32 partials
 // whose consumer sums them in a fixed order (deterministic).
 //
-// Epilogues (fused, lane-local):
+// Epilogues (bf16 outputs are staged through LDS and written with 16-byte
+// coalesced stores):
 //   EPI_F32    fp32 store (split-K partial or fp32 result)
 //   EPI_BF16   bf16 store
-//   EPI_ROPE   bf16 store; the rotary columns of each head are rotated by the
-//              RoPE table row of the token's position (pair partner read with
-//              a lane shuffle: pair (2i, 2i+1) sits in adjacent lanes)
 //   EPI_RESID  bf16 store of R + acc (residual add of the dense block)
 //   EPI_SWIGLU dual-B product: 32-column blocks alternate W1 / W3 rows, so a
 //              lane holds g and u of the same output column and writes
@@ -231,65 +229,90 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
 #undef GEMM_GLOAD
 #undef GEMM_SSTORE
 
-  // ---- epilogue: lane holds column (lane & 31) of each 32x32 block and rows
-  //      8*i + 4*(lane >> 5) + j in acc[...][4*i + j] ----
-  if (EPI == EPI_SWIGLU) {
-    bf16_t* C = (bf16_t*)p.C + (long)bidx * p.sC;
+  // ---- epilogue.  A lane holds column (lane & 31) of each 32x32 block and
+  //      rows 8*i + 4*(lane >> 5) + j in acc[...][4*i + j]. ----
+  const int lr_ = lane & 31;
+  if (EPI == EPI_F32) {
+    float* C = (float*)p.C + (long)bidx * p.sC + (long)split * p.split_stride;
 #pragma unroll
-    for (int j = 0; j < FN; j += 2) {
-      int rbk = (wn * WTN) / 32 + j;                 // even: W1 block, +1: W3 block
-      int col = n0 / 2 + (rbk >> 1) * 32 + lr;
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn * WTN + j * 32 + lr_;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          int row = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + lg * 4 + (e & 3);
-          float g = acc[i][j][e], u = acc[i][j + 1][e];
-          float h = g / (1.f + __expf(-g)) * u;
-          if (row < p.M && col < p.N / 2) C[(long)row * p.ldc + col] = f2bf(h);
+          const int row = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + lg * 4 + (e & 3);
+          if (row < p.M && col < p.N) C[(long)row * p.ldc + col] = acc[i][j][e];
         }
     }
     return;
   }
-
+  // bf16 outputs: the fp32 tile is staged in the (now free) LDS in passes of
+  // RP rows, then every thread writes 8 consecutive outputs with one 16-byte
+  // store (residual add / SwiGLU in fp32, one rounding).
+  constexpr int OUTN = (EPI == EPI_SWIGLU) ? BN / 2 : BN;   // output columns of the tile
+  constexpr int LDS_F = 2 * (BM + BN) * 8 * 4;              // floats available
+  constexpr int RP0 = LDS_F / OUTN;
+  constexpr int RP = RP0 >= BM ? BM : (RP0 >= WTM ? (RP0 / WTM) * WTM : WTM);
+  static_assert(RP * OUTN <= LDS_F, "epilogue staging does not fit the LDS");
+  static_assert(OUTN % 64 == 0, "output tile width");
+  float* cst = (float*)&lds[0][0];
+  // 16-byte chunk swizzle: rows r and r+4 (the two half-waves) use opposite
+  // halves of each 256-byte bank window
+  auto cidx = [](int r, int c) { return r * OUTN + ((((c >> 2) ^ (((r >> 2) & 1) << 3))) << 2) + (c & 3); };
+  const int out_cols = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
+  const int on0 = (EPI == EPI_SWIGLU) ? n0 / 2 : n0;
+  bf16_t* C = (bf16_t*)p.C + (long)bidx * p.sC;
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int col = n0 + wn * WTN + j * 32 + lr;
-    // RoPE pair index of this column (-1 if not a rotary column)
-    int pair = -1;
-    if (EPI == EPI_ROPE) {
-      int cin = col % p.head_dim - p.rope_start;
-      pair = cin >= 0 ? (cin >> 1) : -1;
-    }
+  for (int pass = 0; pass < BM / RP; ++pass) {
+    __syncthreads();  // LDS free: last K tile read (pass 0) or previous pass stored
+    const int rlo = pass * RP;
+    if (wm * WTM + WTM > rlo && wm * WTM < rlo + RP) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + lg * 4 + (e & 3);
-        float v = acc[i][j][e];
-        if (EPI == EPI_ROPE) {
-          float partner = __shfl_xor(v, 1, 64);
-          if (pair >= 0 && row < p.M) {
-            int pos = row % p.rope_T + p.rope_pos0;
-            float c = p.rcos[(long)pos * p.n_pairs + pair];
-            float sn = p.rsin[(long)pos * p.n_pairs + pair];
-            // even lane holds x_{2i}, odd lane holds x_{2i+1}
-            v = (lr & 1) ? (partner * sn + v * c) : (v * c - partner * sn);
+        for (int e = 0; e < 16; ++e) {
+          const int rl = wm * WTM + i * 32 + (e >> 2) * 8 + lg * 4 + (e & 3) - rlo;
+          if (EPI == EPI_SWIGLU) {
+#pragma unroll
+            for (int j = 0; j < FN; j += 2) {
+              const int cl = ((wn * WTN) / 32 + j) / 2 * 32 + lr_;   // output column in tile
+              const float g = acc[i][j][e], u = acc[i][j + 1][e];
+              cst[cidx(rl, cl)] = g / (1.f + __expf(-g)) * u;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) cst[cidx(rl, wn * WTN + j * 32 + lr_)] = acc[i][j][e];
           }
         }
-        if (row < p.M && col < p.N) {
-          if (EPI == EPI_F32) {
-            float* C = (float*)p.C + (long)bidx * p.sC + (long)split * p.split_stride;
-            C[(long)row * p.ldc + col] = v;
-          } else if (EPI == EPI_RESID) {
-            bf16_t* C = (bf16_t*)p.C + (long)bidx * p.sC;
-            C[(long)row * p.ldc + col] = f2bf(bf2f(p.R[(long)row * p.ldr + col]) + v);
-          } else {
-            bf16_t* C = (bf16_t*)p.C + (long)bidx * p.sC;
-            C[(long)row * p.ldc + col] = f2bf(v);
-          }
+    }
+    __syncthreads();
+    constexpr int CH8 = OUTN / 8;            // 8-output chunks per row
+    for (int idx = tid; idx < RP * CH8; idx += NT) {
+      const int rl = idx / CH8, c8 = idx % CH8;
+      const int row = m0 + rlo + rl, col = on0 + 8 * c8;
+      if (row >= p.M || col >= out_cols) continue;
+      const floatx4 v0 = *(const floatx4*)&cst[cidx(rl, 8 * c8)];
+      const floatx4 v1 = *(const floatx4*)&cst[cidx(rl, 8 * c8 + 4)];
+      float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      if (EPI == EPI_RESID) {
+        const u32x4 r = *(const u32x4*)(p.R + (long)row * p.ldr + col);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] += lo_bf(r[q]);
+          v[2 * q + 1] += hi_bf(r[q]);
         }
       }
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = pack2bf(v[2 * q], v[2 * q + 1]);
+      if (col + 8 <= out_cols) {
+        *(u32x4*)(C + (long)row * p.ldc + col) = o;
+      } else {
+        for (int q = 0; q < out_cols - col; ++q)
+          C[(long)row * p.ldc + col + q] = (bf16_t)((q & 1) ? (o[q >> 1] >> 16) : (o[q >> 1] & 0xffffu));
+      }
+    }
   }
 }
 
@@ -331,7 +354,6 @@ hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s) {
   switch (epi) {
     case EPI_F32: return launch_epi<EPI_F32>(p, cfg, s);
     case EPI_BF16: return launch_epi<EPI_BF16>(p, cfg, s);
-    case EPI_ROPE: return launch_epi<EPI_ROPE>(p, cfg, s);
     case EPI_RESID: return launch_epi<EPI_RESID>(p, cfg, s);
     case EPI_SWIGLU:
       if (cfg == GEMM_CFG_64x128) return launch_cfg<64, 128, 1, 2, EPI_SWIGLU>(p, s);

@@ -8,7 +8,7 @@ namespace mla {
 typedef uint16_t bf16_t;
 
 // ------------------------------------------------------------------ GEMM
-enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_ROPE = 2, EPI_RESID = 3, EPI_SWIGLU = 4 };
+enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_RESID = 3, EPI_SWIGLU = 4 };
 enum { GEMM_CFG_AUTO = -1, GEMM_CFG_256x256 = 0, GEMM_CFG_128x128 = 1, GEMM_CFG_64x128 = 2 };
 
 struct GemmParams {
@@ -26,14 +26,17 @@ struct GemmParams {
   long split_stride; // elements between the fp32 partial outputs of slices
   int batch;
   long sA, sB, sC;   // batch strides in elements
-  const float* rcos; // RoPE table [n_pos, n_pairs]
-  const float* rsin;
-  int rope_T, rope_pos0, head_dim, rope_start, n_pairs;
   int tiles_m, tiles_n;  // filled by the launcher
 };
 
 int gemm_pick_cfg(int M, int N, int K, int batch);
 hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s);
+
+// Weight-streaming product for M <= 64 rows (decode): K is cut into 512-wide
+// slices; more than one slice writes fp32 partials [slices][M][ldc]
+// (split_stride apart), a single slice may write bf16.
+int skinny_splits(int K);
+hipError_t gemm_skinny_bf16(GemmParams p, bool bf16_out, hipStream_t s);
 
 // fp32 generic GEMM: C[b] = (R ? R : 0) + A[b] . op(B[b]); op(B) = B^T when
 // b_is_nk (B stored [N, K]) else B (stored [K, N]).
@@ -111,10 +114,12 @@ hipError_t attn_generic_f32(const AttnGenericParams& p, hipStream_t s);
 
 // bf16 flash prefill (Kimi head widths 128 + 64, value 128), causal.
 struct FlashParams {
-  const bf16_t* q;   // [B*T][H][192]   (rope part already rotated)
+  const bf16_t* q;   // [B*T][H][192]   (rope part NOT yet rotated: RoPE is
+                     // applied to the query fragments as they are loaded)
   const bf16_t* kv;  // [B*T][H][256]   ([k_nope 128 | v 128] per head)
   const bf16_t* kr;  // [B*T][64]       (rotated, shared by heads)
   bf16_t* out;       // [B*T][H*128]
+  const float* rcos; const float* rsin;  // RoPE table [>= T][32]
   int B, T, H;
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -122,11 +127,12 @@ hipError_t flash_prefill_bf16(const FlashParams& p, hipStream_t s);
 
 // bf16 decode over the full per-head cache (one query per sequence).
 struct DecodeFullParams {
-  const bf16_t* q;       // [B][H][192]
+  const bf16_t* q;       // [B][H][192] (rope part rotated here, at position L-1)
   const bf16_t* k_cache; // [B][H][L_cap][192]
   const bf16_t* v_cache; // [B][H][L_cap][128]
   bf16_t* out;           // [B][H*128]
   float* part;           // split partials: [B*H][nsplit][128 + 2]
+  const float* rcos; const float* rsin;  // RoPE table, row L-1 used
   int B, H, L, L_cap, nsplit, chunk;
   float scale_log2;
 };
@@ -135,10 +141,11 @@ hipError_t decode_full_bf16(const DecodeFullParams& p, hipStream_t s);
 // bf16 absorbed decode over the latent cache.
 struct DecodeLatentParams {
   const bf16_t* q_abs;   // [B][H][512]  absorbed query (W_UK folded in)
-  const bf16_t* q;       // [B][H][192]  (rope part at offset 128)
+  const bf16_t* q;       // [B][H][192]  (rope part at offset 128, rotated here)
   const bf16_t* cache;   // [B][L_cap][576]
   float* part;           // [B][nsplit][H][516]: m, l, pad, pad, o~[512]
   bf16_t* o_lat;         // [B][H][512]  merged latent output
+  const float* rcos; const float* rsin;  // RoPE table, row L-1 used
   int B, H, L, L_cap, nsplit, chunk;
   float scale_log2;
 };

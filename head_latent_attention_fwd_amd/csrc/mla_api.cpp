@@ -185,6 +185,8 @@ struct ProjBufs {
   void* q;      // [M][H*dqk]
   void* kv;     // [M][H*(dn+dv)]   (NULL when not needed)
   void* o;      // [M][H*dv]
+  void* upart;  // fp32 split-K partials of the small-M up-projections (or NULL)
+  size_t upart_floats;
 };
 
 void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, ProjBufs* b) {
@@ -193,7 +195,7 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
   const size_t es = esize(d);
   b->S = 1;
   b->kchunk = d->d_model;
-  if (splitk && d->dtype == MLA_BF16) plan_splitk(M, N1, d->d_model, &b->S, &b->kchunk);
+  if (splitk && d->dtype == MLA_BF16) b->S = skinny_splits(d->d_model);
   b->part = c.take((size_t)b->S * M * N1 * 4);
   b->cq = c.take((size_t)M * d->q_lora_rank * es);
   b->ckv = c.take((size_t)M * d->kv_lora_rank * es);
@@ -201,6 +203,49 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
   b->q = c.take((size_t)M * H * dqk * es);
   b->kv = need_kv ? c.take((size_t)M * H * (d->qk_nope_dim + d->v_head_dim) * es) : nullptr;
   b->o = c.take((size_t)M * H * d->v_head_dim * es);
+  b->upart = nullptr;
+  b->upart_floats = 0;
+  if (splitk && d->dtype == MLA_BF16) {
+    // partials of the q and kv up-projections when M is small (decode)
+    size_t need = 0;
+    const int shapes[2][2] = {{H * dqk, d->q_lora_rank},
+                              {H * (d->qk_nope_dim + d->v_head_dim), d->kv_lora_rank}};
+    for (auto& sh : shapes) {
+      const int S = skinny_splits(sh[1]);
+      size_t n = (size_t)S * M * sh[0];
+      if (S > 1 && n > need) need = n;
+    }
+    if (need) {
+      b->upart = c.take(need * 4);
+      b->upart_floats = need;
+    }
+  }
+}
+
+// bf16-output product.  Decode-sized products (M <= 64) go to the weight-
+// streaming kernel: one K slice writes bf16 directly, several write fp32
+// partials to `part` that a fixed-order reduction sums.
+int gemm_bf16_out(const char* name, GemmParams g, void* part, size_t part_floats,
+                  hipStream_t st) {
+  if (g.M > 64) {
+    LAUNCH(name, gemm_bf16(g, EPI_BF16, -1, st));
+    return MLA_OK;
+  }
+  const int S = skinny_splits(g.K);
+  if (S == 1) {
+    LAUNCH(name, gemm_skinny_bf16(g, true, st));
+    return MLA_OK;
+  }
+  if (!part || (size_t)S * g.M * g.N > part_floats || g.N % 4)
+    return fail(MLA_ERR_HIP, "internal: split-K partial buffer too small for %s", name);
+  GemmParams f = g;
+  f.C = part;
+  f.ldc = g.N;
+  f.split_stride = (long)g.M * g.N;
+  LAUNCH(name, gemm_skinny_bf16(f, false, st));
+  LAUNCH("reduce_splits", reduce_splits<bf16_t>((const float*)part, S, (long)g.M * g.N, g.M, g.N,
+                                                 (bf16_t*)g.C, g.ldc, st));
+  return MLA_OK;
 }
 
 // ---------------------------------------------------- shared launch steps
@@ -220,8 +265,12 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
     g.b_split = ql;
     g.C = b.part; g.ldc = N1;
     g.M = M; g.N = N1; g.K = D;
-    g.ksplit = b.S; g.kchunk = b.kchunk; g.split_stride = (long)M * N1;
-    LAUNCH("gemm_down", gemm_bf16(g, EPI_F32, -1, st));
+    g.split_stride = (long)M * N1;
+    if (b.S > 1) {
+      LAUNCH("gemm_down", gemm_skinny_bf16(g, false, st));  // decode: K-sliced weight stream
+    } else {
+      LAUNCH("gemm_down", gemm_bf16(g, EPI_F32, -1, st));
+    }
     LatentNormParams<bf16_t> n;
     memset(&n, 0, sizeof n);
     n.part = (const float*)b.part; n.nsplit = b.S; n.split_stride = (long)M * N1; n.ld_part = N1;
@@ -237,16 +286,18 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
     q.B = (const bf16_t*)w->w_uqr; q.ldb = ql;
     q.C = b.q; q.ldc = (long)H * dqk;
     q.M = M; q.N = H * dqk; q.K = ql;
-    q.rcos = rc; q.rsin = rs; q.rope_T = rowsT; q.rope_pos0 = pos0;
-    q.head_dim = dqk; q.rope_start = dn; q.n_pairs = dr / 2;
-    LAUNCH("gemm_q_up_rope", gemm_bf16(q, EPI_ROPE, -1, st));
+    // the query's rotary part is rotated by the attention kernels as they
+    // load it (each 16-byte fragment holds four whole RoPE pairs)
+    int r_ = gemm_bf16_out("gemm_q_up", q, b.upart, b.upart_floats, st);
+    if (r_) return r_;
     if (b.kv) {
       GemmParams k = gp_base();
       k.A = (const bf16_t*)b.ckv; k.lda = kl;
       k.B = (const bf16_t*)w->w_ukv; k.ldb = kl;
       k.C = b.kv; k.ldc = (long)H * (dn + dv);
       k.M = M; k.N = H * (dn + dv); k.K = kl;
-      LAUNCH("gemm_kv_up", gemm_bf16(k, EPI_BF16, -1, st));
+      r_ = gemm_bf16_out("gemm_kv_up", k, b.upart, b.upart_floats, st);
+      if (r_) return r_;
     }
     return MLA_OK;
   }
@@ -296,10 +347,8 @@ int run_oproj(const mla_dims* d, const void* w_o, const void* o, int M, const vo
     g.A = (const bf16_t*)o; g.lda = K; g.B = (const bf16_t*)w_o; g.ldb = K;
     g.M = M; g.N = D; g.K = K;
     if (S > 1) {
-      g.C = part; g.ldc = D; g.ksplit = S; g.kchunk = kchunk; g.split_stride = (long)M * D;
-      LAUNCH("gemm_o_proj", gemm_bf16(g, EPI_F32, -1, st));
-      LAUNCH("reduce_splits", reduce_splits<bf16_t>((const float*)part, S, (long)M * D, M, D, (bf16_t*)out, D, st));
-      return MLA_OK;
+      g.C = out; g.ldc = D;
+      return gemm_bf16_out("gemm_o_proj", g, part, (size_t)S * M * D, st);
     }
     g.C = out; g.ldc = D;
     if (R) { g.R = (const bf16_t*)R; g.ldr = D; }
@@ -337,7 +386,7 @@ int prefill_core(const mla_dims* d, const mla_weights* w, const void* x, int B, 
   if (d->dtype == MLA_BF16) {
     FlashParams f;
     f.q = (const bf16_t*)b.q; f.kv = (const bf16_t*)b.kv; f.kr = (const bf16_t*)b.kr;
-    f.out = (bf16_t*)b.o; f.B = B; f.T = T; f.H = H;
+    f.out = (bf16_t*)b.o; f.B = B; f.T = T; f.H = H; f.rcos = rc; f.rsin = rs;
     f.scale_log2 = d->softmax_scale * 1.4426950408889634f;
     LAUNCH("flash_prefill", flash_prefill_bf16(f, st));
   } else {
@@ -425,7 +474,7 @@ size_t decode_layout(const mla_dims* d, int B, int L_cap, int form, void* ws, De
   pl->chunk = L_cap;
   pl->S2 = 1;
   pl->kchunk2 = H * d->v_head_dim;
-  if (d->dtype == MLA_BF16) plan_splitk(B, d->d_model, H * d->v_head_dim, &pl->S2, &pl->kchunk2);
+  if (d->dtype == MLA_BF16 && B <= 64) pl->S2 = skinny_splits(H * d->v_head_dim);
   pl->opart = c.take((size_t)pl->S2 * B * d->d_model * 4);
   return c.off + 256;
 }
@@ -583,6 +632,7 @@ int mla_decode_fullcache(const mla_dims* d, const mla_weights* w, const void* x,
     DecodeFullParams a;
     a.q = (const bf16_t*)b.q; a.k_cache = (const bf16_t*)k_cache;
     a.v_cache = (const bf16_t*)v_cache; a.out = (bf16_t*)b.o; a.part = (float*)pl.apart;
+    a.rcos = rc; a.rsin = rs;
     a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
     a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
     LAUNCH("decode_full", decode_full_bf16(a, st));
@@ -633,6 +683,7 @@ int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* 
     a.q_abs = (const bf16_t*)pl.q_abs; a.q = (const bf16_t*)b.q;
     a.cache = (const bf16_t*)latent_cache; a.part = (float*)pl.apart;
     a.o_lat = (bf16_t*)pl.o_lat;
+    a.rcos = rc; a.rsin = rs;
     a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
     a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
     LAUNCH("decode_latent", decode_latent_bf16(a, st));
@@ -643,7 +694,11 @@ int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* 
     g.C = b.o; g.ldc = (long)H * dv;
     g.M = B; g.N = dv; g.K = kl;
     g.batch = H; g.sA = kl; g.sB = (long)(dn + dv) * kl; g.sC = dv;
-    LAUNCH("gemm_uv", gemm_bf16(g, EPI_BF16, -1, st));
+    if (B <= 64 && kl <= 512) {
+      LAUNCH("gemm_uv", gemm_skinny_bf16(g, true, st));
+    } else {
+      LAUNCH("gemm_uv", gemm_bf16(g, EPI_BF16, -1, st));
+    }
   } else {
     GemmF32Params g;
     memset(&g, 0, sizeof g);

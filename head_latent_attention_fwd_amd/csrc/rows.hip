@@ -38,13 +38,31 @@ __global__ __launch_bounds__(256) void latent_norm_rope_kernel(LatentNormParams<
   const int tid = threadIdx.x;
   const int N1 = p.q_lora + p.kv_lora + p.d_rope;
   float sq = 0.f, skv = 0.f;
-  for (int c = tid; c < N1; c += 256) {
-    float v = 0.f;
-    for (int s = 0; s < p.nsplit; ++s)  // fixed order: deterministic
-      v += p.part[(long)s * p.split_stride + (long)m * p.ld_part + c];
-    row[c] = v;
-    if (c < p.q_lora) sq += v * v;
-    else if (c < p.q_lora + p.kv_lora) skv += v * v;
+  // sum the split-K partials of this row in a fixed order (deterministic);
+  // 4 columns per thread and iteration, all splits' loads in flight together
+  const bool vec = (N1 % 4 == 0) && (p.ld_part % 4 == 0) && (p.split_stride % 4 == 0);
+  if (vec) {
+    for (int c4 = tid; c4 < N1 / 4; c4 += 256) {
+      const float* src = p.part + (long)m * p.ld_part + 4 * c4;
+      floatx4 v = *(const floatx4*)src;
+      for (int s = 1; s < p.nsplit; ++s) v += *(const floatx4*)(src + (long)s * p.split_stride);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 4 * c4 + q;
+        row[c] = v[q];
+        if (c < p.q_lora) sq += v[q] * v[q];
+        else if (c < p.q_lora + p.kv_lora) skv += v[q] * v[q];
+      }
+    }
+  } else {
+    for (int c = tid; c < N1; c += 256) {
+      float v = 0.f;
+      for (int s = 0; s < p.nsplit; ++s)
+        v += p.part[(long)s * p.split_stride + (long)m * p.ld_part + c];
+      row[c] = v;
+      if (c < p.q_lora) sq += v * v;
+      else if (c < p.q_lora + p.kv_lora) skv += v * v;
+    }
   }
   const float tq = block_sum256(sq, red);
   const float tkv = block_sum256(skv, red);
@@ -228,20 +246,24 @@ template hipError_t scatter_full_cache<bf16_t>(const bf16_t*, const bf16_t*, bf1
 template <typename T>
 __global__ void reduce_splits_kernel(const float* __restrict__ part, int nsplit, long stride, int M,
                                      int N, T* __restrict__ out, long ldo) {
-  long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (long)M * N) return;
-  long m = e / N;
-  int n = (int)(e % N);
-  float v = 0.f;
-  for (int s = 0; s < nsplit; ++s) v += part[s * stride + e];
-  out[m * ldo + n] = from_f<T>(v);
+  // 4 consecutive columns per thread (N % 4 == 0 checked by the launcher)
+  long e4 = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e4 >= (long)M * N / 4) return;
+  const long e = 4 * e4;
+  const long m = e / N;
+  const int n = (int)(e % N);
+  floatx4 v = *(const floatx4*)(part + e);
+  for (int s = 1; s < nsplit; ++s) v += *(const floatx4*)(part + s * stride + e);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) out[m * ldo + n + q] = from_f<T>(v[q]);
 }
 
 template <typename T>
 hipError_t reduce_splits(const float* part, int nsplit, long split_stride, int M, int N, T* out,
                          long ldo, hipStream_t s) {
-  long n = (long)M * N;
+  long n = (long)M * N / 4;
   if (n == 0) return hipSuccess;
+  if (N % 4 || split_stride % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(reduce_splits_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      part, nsplit, split_stride, M, N, out, ldo);
   return hipGetLastError();
