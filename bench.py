@@ -62,6 +62,25 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the GEMM source changed since the counters were
+    taken (the summary records a hash of the source it measured)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "prefill_kimi_T2048_hbm_traffic.md")
+    src = os.path.join(ROOT, "head_latent_attention_fwd_amd", "csrc", "gemm_bf16.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    m = re.search(rf"{kernel} traffic_bytes_per_launch=(\d+) gemm_source_sha256_16=([0-9a-f]+)", text)
+    if not m or m.group(2) != sha:
+        return None
+    return int(m.group(1))
+
+
 def make_weights(torch, dev, k, seed):
     """Synthetic N(0, 0.02^2) weights with unit gains, drawn on the device."""
     import head_latent_attention_fwd_amd as mla
@@ -311,7 +330,8 @@ def main():
     dom = max(gemmlike, key=lambda n: gemmlike[n]["avg_ms"])
     dv = gemmlike[dom]
     roofline = {"kernel": dom, "bound": "mfma", "achieved": dv["tflops"], "peak": MFMA_BF16_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": dv["tflops"] / MFMA_BF16_PEAK_TFS, "traffic": None,
+                "unit": "TFLOP/s", "frac": dv["tflops"] / MFMA_BF16_PEAK_TFS,
+                "traffic": measured_traffic(dom),
                 "avg_ms": dv["avg_ms"], "gflop_per_launch": dv["gflop"]}
     value = r["flops"] / (r["ms"] * 1e-3) / 1e12
     line = {
