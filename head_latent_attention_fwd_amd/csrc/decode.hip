@@ -182,25 +182,91 @@ hipError_t decode_full_bf16(const DecodeFullParams& p, hipStream_t s) {
 // latent-cache decode (absorbed)
 // ------------------------------------------------------------------------
 namespace {
-constexpr int LT = 32;     // keys per tile
-constexpr int LCH = 72;    // 16-byte chunks per cache row (576 bf16)
+constexpr int LT = 32;                  // keys per tile
+constexpr int ROWB = 1152;              // bytes per cache row (576 bf16)
+constexpr int STAGE = LT * ROWB;        // one tile in LDS
+constexpr int NST = 4;                  // LDS ring depth: NST - 1 tiles in flight
+constexpr int DMA_PER_WAVE = STAGE / 1024 / 4;  // 1 KB per wave-wide DMA, 4 waves
+// A head's running max is raised only when a tile exceeds it by this many
+// log2 units, so bf16 probabilities stay below 2^16.
+constexpr float LAZY_L = 16.0f;
 
-MLA_DEV int cphys(int c, int row) { return (c & ~7) | ((c ^ row) & 7); }
-// position of key offset k (0..31) inside a C^T row
-MLA_DEV int lpos(int k) { return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3); }
-MLA_DEV int ctswz(int f) { return ((f >> 1) ^ (f >> 3)) & 3; }
+// Tile layout in LDS: 16-byte chunk c (0..71) of key row r sits at chunk slot
+// r * 72 + ((c & ~7) | ((c ^ lat_fr(r)) & 7)), with lat_fr a permutation of
+// the row pair index u = (r >> 1) & 7.  Rows are 1152 bytes (4.5 windows of
+// 64 banks), so both reads of a tile depend on u alone: the QK read (16 rows,
+// one chunk each per 16 lanes) and the transposed PV read (8 rows x 2
+// chunks).  Of the 168 linear (GF(2)) permutations of u, this one was
+// measured free of bank conflicts for both on gfx950 (hardware counters);
+// u itself leaves the PV reads 2-way, a rotation of u the QK reads.
+MLA_DEV int lat_fr(int r) {
+  const int u = (r >> 1) & 7;
+  return ((u << 1) ^ (0 - (u >> 2))) & 7;  // 0 2 4 6 7 5 3 1
+}
+MLA_DEV int lat_slot(int c, int r) { return (c & ~7) | ((c ^ lat_fr(r)) & 7); }
+
+// Wave-wide direct-to-LDS load: lane l's 16 bytes at global
+// rsrc.base + voff go to LDS byte m0 + 16 l; lanes past the resource's size
+// write zeros.  Issued from asm so the compiler's wait counting, which cannot
+// tell ring stages apart and would wait for every load in flight, stays out;
+// the kernel waits with explicit vmcnt values instead.
+MLA_DEV void dma16(unsigned m0, int voff, u32x4 rsrc) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(m0), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+MLA_DEV u32x4 lat_rsrc(const char* base, int bytes) {
+  const unsigned long a = (unsigned long)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane((unsigned)max(bytes, 0));
+  r[3] = 0x00020000u;  // raw buffer, 32-bit data format
+  return r;
+}
+// wait until at most n tiles of this wave's DMAs are still in flight
+MLA_DEV void wait_tiles(int n) {
+  if (n >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * DMA_PER_WAVE) : "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(DMA_PER_WAVE) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 }  // namespace
 
+// One workgroup = one (batch row, key split); 4 waves x 16 heads.  Per tile of
+// 32 cache rows: S^T[key, head] = C[key, 0:576] . q~[head]^T (16x16x32 MFMA,
+// key rows read from LDS, the absorbed query held in registers), exp2 in
+// registers, O~^T[feature, head] += C^T[feature, key] . P^T with the C^T
+// operand read straight from the row-major tile by ds_read_b64_tr_b16 (two
+// 4-key reads per MFMA).  Tiles stream through an NST-stage LDS ring by
+// direct-to-LDS buffer loads, NST - 1 tiles ahead of the compute.
+//
+// k-slot order of the PV product: the QK accumulator holds keys
+// 16 mb + 4 g + j in lane group g, so slot 8 g + 4 mb + j; a transposed read
+// of rows 16 mb + 4 g + (0..3) yields slots 8 g + 4 mb + (0..3).
+//
+// The running max is raised lazily.  When a head's tile max clears its
+// current max by LAZY_L after the first tile, the workgroup restarts its
+// split with the higher max rather than rescaling 128 accumulators per lane,
+// so the hot loop carries no rescale at all.  Each restart needs a jump of
+// 2^16 in some head's probabilities; splits with ordinary score ranges never
+// restart.
 __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p) {
-  __shared__ u32x4 Cs[2][LT * LCH];   // [key][576] row-major, swizzled
-  __shared__ u32x4 Ct[2][512 * 4];    // [feature][32 keys], keys permuted
+  __shared__ __attribute__((aligned(16))) char lds[NST * STAGE + 32];
+  int* rflag = (int*)(lds + NST * STAGE);
+  const unsigned lds_base = (unsigned)(unsigned long)(__attribute__((address_space(3))) char*)lds;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   const int split = blockIdx.x, b = blockIdx.y;
   const int j0 = split * p.chunk;
   const int j1 = min(p.L, j0 + p.chunk);
   const int head = 16 * w + l16;
+  const int ntiles = j1 > j0 ? (j1 - j0 + LT - 1) / LT : 0;
 
   bf16x8 qf[18];
 #pragma unroll
@@ -212,104 +278,161 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
     if (f >= 512) v = rope8_bf16(v, p.rcos, p.rsin, p.L - 1, 32, (f - 512) / 2);
     qf[s] = __builtin_bit_cast(bf16x8, v);
   }
-  const bf16_t* cb = p.cache + (long)b * p.L_cap * 576;
+  const char* cb = (const char*)(p.cache + ((long)b * p.L_cap + j0) * 576);
 
-  // loader: item e = kp + 16 c (key pair kp, chunk c), up to 5 per thread
-  u32x4 r0[5], r1[5];
-#define DL_LOAD(kv0)                                                                      \
-  do {                                                                                    \
-    _Pragma("unroll") for (int i = 0; i < 5; ++i) {                                       \
-      const int e = min(tid + 256 * i, 16 * LCH - 1);                                     \
-      const int kp = e & 15, c = e >> 4;                                                  \
-      const int ka = min((kv0) + 2 * kp, j1 - 1), kb = min((kv0) + 2 * kp + 1, j1 - 1);   \
-      r0[i] = *(const u32x4*)(cb + (long)ka * 576 + 8 * c);                               \
-      r1[i] = *(const u32x4*)(cb + (long)kb * 576 + 8 * c);                               \
-    }                                                                                     \
-  } while (0)
-#define DL_STORE(buf)                                                                     \
-  do {                                                                                    \
-    uint32_t* ct32 = (uint32_t*)&Ct[buf][0];                                              \
-    _Pragma("unroll") for (int i = 0; i < 5; ++i) {                                       \
-      const int e = tid + 256 * i;                                                        \
-      if (e < 16 * LCH) {                                                                 \
-        const int kp = e & 15, c = e >> 4;                                                \
-        Cs[buf][(2 * kp) * LCH + cphys(c, 2 * kp)] = r0[i];                               \
-        Cs[buf][(2 * kp + 1) * LCH + cphys(c, 2 * kp + 1)] = r1[i];                       \
-        if (c < 64) {                                                                     \
-          const int pos = lpos(2 * kp);                                                   \
-          _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                 \
-            const int f = 8 * c + q;                                                      \
-            const uint32_t w0 = r0[i][q >> 1], w1 = r1[i][q >> 1];                        \
-            const uint32_t val = (q & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))              \
-                                         : ((w0 & 0xffffu) | (w1 << 16));                 \
-            const int ph = (((pos >> 3) ^ ctswz(f)) << 3) | (pos & 7);                    \
-            ct32[(f * 32 + ph) >> 1] = val;                                               \
-          }                                                                               \
-        }                                                                                 \
-      }                                                                                   \
-    }                                                                                     \
-  } while (0)
-
-  floatx4 O[32];
+  // DMA k of this wave fills LDS bytes [1024 (w * DMA_PER_WAVE + k), +1024) of
+  // a stage: chunk slot P = 64 (w * DMA_PER_WAVE + k) + lane holds row P / 72,
+  // logical chunk lat_slot(P % 72, row) (the swizzle is an involution).
+  int voff[DMA_PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) O[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < DMA_PER_WAVE; ++k) {
+    const int P = 64 * (w * DMA_PER_WAVE + k) + lane, row = P / 72;
+    voff[k] = row * ROWB + 16 * lat_slot(P % 72, row);
+  }
+#define LAT_ISSUE(tt)                                                                       \
+  do {                                                                                      \
+    const u32x4 rs_ = lat_rsrc(cb + (long)(tt) * LT * ROWB, (j1 - j0 - (tt) * LT) * ROWB);   \
+    const unsigned m0_ = lds_base + ((tt) % NST) * STAGE + w * DMA_PER_WAVE * 1024;         \
+    _Pragma("unroll") for (int k = 0; k < DMA_PER_WAVE; ++k) dma16(m0_ + 1024 * k, voff[k], rs_); \
+  } while (0)
+
+  // QK fragment (s, mb): row 16 mb + l16, chunk 4 s + g4
+  //   -> qk_off[s & 1] + 16 ROWB mb + 128 (s >> 1)
+  int qk_off[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    qk_off[par] = l16 * ROWB + 16 * (((4 * par + g4) ^ lat_fr(l16)) & 7);
+  // PV transposed read (n, mb): source row 16 mb + 4 g4 + (l16 >> 2), features
+  // 16 n + 4 (l16 & 3) .. + 3  ->  pv_off[n & 3] + 16 ROWB mb + 128 (n >> 2)
+  int pv_off[4];
+#pragma unroll
+  for (int n3 = 0; n3 < 4; ++n3) {
+    const int row = 4 * g4 + (l16 >> 2);
+    const int c = 2 * n3 + ((l16 >> 1) & 1);
+    pv_off[n3] = row * ROWB + 16 * ((c ^ lat_fr(row)) & 7) + 8 * (l16 & 1);
+  }
+
+  const float sl2 = p.scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
-  const int ntiles = (j1 - j0 + LT - 1) / LT;
-
-  DL_LOAD(j0);
-  DL_STORE(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1, kv0 = j0 + t * LT;
-    if (t + 1 < ntiles) DL_LOAD(kv0 + LT);
-    floatx4 S[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int s = 0; s < 18; ++s)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int row = 16 * mb + l16;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, Cs[cur][row * LCH + cphys(4 * s + g4, row)]);
-        S[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], S[mb], 0, 0, 0);
-      }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float v = S[mb][jj] * p.scale_log2;
-        if (kv0 + 16 * mb + 4 * g4 + jj >= j1) v = -INFINITY;
-        S[mb][jj] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    float psum = 0.f;
-    bf16x8 pf;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float pv = exp2f(S[mb][jj] - m_new);
-        psum += pv;
-        pf[4 * mb + jj] = (__bf16)pv;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+  floatx4 O[32];
+  bool restart = ntiles > 0;
+  while (restart) {
+    restart = false;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      O[i] *= alpha;
-      const int f = 16 * i + l16;
-      const bf16x8 a = __builtin_bit_cast(bf16x8, Ct[cur][f * 4 + (g4 ^ ctswz(f))]);
-      O[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, O[i], 0, 0, 0);
+      O[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+a"(O[i]));  // keep the accumulators in AGPRs across both loops
     }
-    if (t + 1 < ntiles) DL_STORE(cur ^ 1);
-    __syncthreads();
-  }
-#undef DL_LOAD
-#undef DL_STORE
+    l_run = 0.f;
+    for (int tt = 0; tt < NST - 1 && tt < ntiles; ++tt) LAT_ISSUE(tt);
+    for (int t = 0;; ++t) {
+      wait_tiles(min(NST - 2, ntiles - 1 - t));
+      __syncthreads();
+      if (t > 0) {
+        const int4 fl = *(const int4*)&rflag[4 * ((t - 1) & 1)];
+        if (fl.x | fl.y | fl.z | fl.w) {
+          restart = true;
+          break;
+        }
+      }
+      if (t == ntiles) break;
+      if (t + NST - 1 < ntiles) LAT_ISSUE(t + NST - 1);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) asm volatile("" : "+a"(O[i]));
+      const char* cs = lds + (t % NST) * STAGE;
+      const int kv0 = j0 + t * LT;
 
+      // QK: 36 fragments read RQ ahead of their MFMA, four accumulation chains
+      constexpr int RQ = 8, RP = 8;
+#define QK_FRAG(x) (*(const bf16x8*)(cs + qk_off[((x) >> 1) & 1] + 16 * ROWB * ((x) & 1) + 128 * ((x) >> 2)))
+#define PV_FRAG(y)                                                                          \
+  __builtin_amdgcn_ds_read_tr16_b64_v4i16(                                                  \
+      (__attribute__((address_space(3))) s16x4*)(cs + pv_off[((y) >> 1) & 3] +             \
+                                                  16 * ROWB * ((y) & 1) + 128 * ((y) >> 3)))
+      bf16x8 fa[RQ];
+#pragma unroll
+      for (int u = 0; u < RQ; ++u) fa[u] = QK_FRAG(u);
+      floatx4 S4[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) S4[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int x = 0; x < 36; ++x) {
+        const int s = x >> 1, mb = x & 1;
+        S4[mb + 2 * (s & 1)] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[x % RQ], qf[s], S4[mb + 2 * (s & 1)], 0, 0, 0);
+        if (x + RQ < 36) fa[x % RQ] = QK_FRAG(x + RQ);
+      }
+      // PV operand halves y = 2 n + mb; the first ones do not depend on the
+      // softmax, so they are read under the tail of the QK products
+      s16x4 fp[2 * RP];
+#pragma unroll
+      for (int u = 0; u < 2 * RP; ++u) fp[u] = PV_FRAG(u);
+      __builtin_amdgcn_sched_group_barrier(0x100, RQ, 0);
+#pragma unroll
+      for (int x = 0; x < 36; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (x < 36 - RQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      floatx4 S[2] = {S4[0] + S4[2], S4[1] + S4[3]};
+      // S[mb][jj]: key 16 mb + 4 g4 + jj of the tile, head `head`
+      if (kv0 + LT > j1) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (kv0 + 16 * mb + 4 * g4 + jj >= j1) S[mb][jj] = -INFINITY;
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                         fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+      {  // max over the four lane groups (same head): lanes l ^ 16, l ^ 32
+        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1])) * sl2;
+      }
+      const bool raise = tmax > m_run + LAZY_L;
+      if (raise) m_run = tmax;
+      // the accumulators are still zero on the first tile: no restart needed
+      const bool redo = __any(raise) && t > 0;
+      float psum = 0.f;
+      bf16x8 pf;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(S[mb][jj], sl2, -m_run));
+          psum += pv;
+          pf[4 * mb + jj] = (__bf16)pv;
+        }
+      l_run += psum;
+#pragma unroll
+      for (int n = 0; n < 32; ++n) {
+        const s16x4 lo = fp[(2 * n) % (2 * RP)], hi = fp[(2 * n + 1) % (2 * RP)];
+        const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, O[n], 0, 0, 0);
+        if (n + RP < 32) {
+          fp[(2 * n) % (2 * RP)] = PV_FRAG(2 * (n + RP));
+          fp[(2 * n + 1) % (2 * RP)] = PV_FRAG(2 * (n + RP) + 1);
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < 32; ++n) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (n + RP < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#undef QK_FRAG
+#undef PV_FRAG
+      if (lane == 0) rflag[4 * (t & 1) + w] = redo ? 1 : 0;
+    }
+    if (restart) {
+      // drain the ring before it is refilled from the first tile
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  }
+
+#undef LAT_ISSUE
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   // partial record: m, l, 2 pad, o~[512] (16-byte aligned)
@@ -320,7 +443,7 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
   }
 #pragma unroll
   for (int i = 0; i < 32; ++i)
-    *(floatx4*)(pp + 4 + 16 * i + 4 * g4) = O[i];
+    *(floatx4*)(pp + 4 + 16 * i + 4 * g4) = ntiles > 0 ? O[i] : floatx4{0.f, 0.f, 0.f, 0.f};
 }
 
 __global__ __launch_bounds__(256) void latent_combine_kernel(const float* part, int nsplit, int H,

@@ -207,6 +207,55 @@ def test_decode_latentcache_kimi_full_size_sampled():
     assert_close(got, want, TOL_BF16, "decode latent B=32 P=8192 sampled")
 
 
+def _spike_scale(od, w, x_b, P, cf_b, pos, floor_rows):
+    """Power of two that lifts row `pos`'s score, for its best head, at least
+    12 (natural-log units) above every score in `floor_rows`; oracle steps."""
+    pr = ref.mla_project(od, oracle_weights(w), x_b[None, None, :].astype(np.float64), np.array([P]))
+    q_t = ref.absorbed_query(od, oracle_weights(w), pr["q_nope"][0, 0])       # [H, r]
+    q_r = pr["q_rope"][0, 0]                                                    # [H, dr]
+    r = od.kv_lora_rank
+    S = (q_t @ cf_b[:, :r].T + q_r @ cf_b[:, r:].T) * od.softmax_scale          # [H, L]
+    h = int(np.argmax(S[:, pos]))
+    assert S[h, pos] > 0
+    need = (S[h, floor_rows].max() + 12.0) / S[h, pos]
+    return 2.0 ** int(np.ceil(np.log2(max(need, 1.0))))
+
+
+def test_decode_latentcache_max_jump_restart():
+    """Cache rows whose scores jump far above the running max after the first
+    key tile of their split (B=32, L=1501: 192-key splits of 32-key tiles).
+    The latent kernel raises a head's running max lazily and restarts the
+    split when a later tile clears it by 2^16 in probability; rows at 230
+    (sequence 0) and at 1000 then 1100 (sequence 5, two restarts) exercise
+    that path.  Oracle on sequences 0, 5, 7."""
+    od = ref.KIMI_K2
+    B, P = 32, 1500
+    log(f"[decode latent restart] B={B} P={P} bf16")
+    x, w, cc = synth.decode_latent_inputs(od, B, P, P + 1, 1005, bf16=True)
+    cf = synth.as_f32(cc, True).astype(np.float64)
+    cf[:, P] = 0.0  # slot P is overwritten by the step; keep it out of the floor
+    everything = np.arange(P)
+    k0 = _spike_scale(od, w, x[0], P, cf[0], 230, everything)
+    cc[0, 230] = synth.bf16_bits(cf[0, 230] * k0)
+    k1 = _spike_scale(od, w, x[5], P, cf[5], 1000, everything)
+    cc[5, 1000] = synth.bf16_bits(cf[5, 1000] * k1)
+    cf5 = synth.as_f32(cc[5], True).astype(np.float64)
+    cf5[1100] = cf5[1000]
+    k2 = _spike_scale(od, w, x[5], P, cf5, 1100, np.arange(P)[np.arange(P) != 1100])
+    cc[5, 1100] = synth.bf16_bits(cf5[1000] * k2)
+    log(f"  spike scales {k0} {k1} {k2}")
+    assert max(k0, k1, k2) <= 2.0 ** 12
+    d = dims_of(mla, od, "bf16")
+    cd = bits_to_dev(cc, "bf16", DEV)
+    got = mla.mla_decode_latentcache(d, weights_to_dev(w, "bf16", DEV), to_dev(x, "bf16", DEV), P, cd,
+                                     _rope(od, P + 1))
+    torch.cuda.synchronize()
+    bs = [0, 5, 7]
+    cfs = synth.as_f32(cc[bs], True).astype(np.float64)
+    want, _ = ref.mla_decode_latentcache(od, oracle_weights(w), x[bs].astype(np.float64), P, cfs)
+    assert_close(from_dev(got)[bs], want, TOL_BF16, "decode latent with score jumps")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_absorbed_equals_full_on_gpu(dt):
     """Latent decode and full-cache decode over the cache expanded from the
