@@ -130,6 +130,19 @@ def timed(torch, fn, steps, warmup, flush=None):
     return tot / steps, time.perf_counter() - t0
 
 
+def timed_profiled(torch, mla, fn, steps, flush=None):
+    """Time `steps` steps as they run (no per-kernel events), then time them
+    again with the library's per-launch HIP events on the launch stream for
+    the kernel table.  Returns (ms_per_step, wall_s, kernel_table,
+    ms_per_step_with_events)."""
+    ms, wall = timed(torch, fn, steps, 0, flush)
+    mla.mla_profile_summary()                  # drop anything recorded so far
+    mla.mla_profile_enable(True)
+    ms_ev, _ = timed(torch, fn, steps, 0, flush)
+    mla.mla_profile_enable(False)
+    return ms, wall, kernel_table(mla, steps), ms_ev
+
+
 def kernel_table(mla, steps):
     prof = mla.mla_profile_summary()
     return {n: {"launches": c, "avg_ms": ms / c} for n, (c, ms) in prof.items()}
@@ -145,18 +158,14 @@ def bench_prefill(torch, mla, dev, steps, warmup, k=KIMI, B=1, T=2048):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    mla.mla_profile_summary()                  # drop anything recorded so far
-    mla.mla_profile_enable(True)
-    ms, wall = timed(torch, fn, steps, 0)
-    mla.mla_profile_enable(False)
-    kern = kernel_table(mla, steps)
+    ms, wall, kern, ms_ev = timed_profiled(torch, mla, fn, steps)
     flops = prefill_kernel_flops(B, T, k)
     for n, v in kern.items():
         if n in flops:
             v["gflop"] = flops[n] / 1e9
             v["tflops"] = flops[n] / (v["avg_ms"] * 1e-3) / 1e12
     total = sum(flops.values())
-    return {"ms": ms, "wall_s": wall, "flops": total, "kernels": kern, "w": w, "d": d}
+    return {"ms": ms, "ms_with_kernel_events": ms_ev, "wall_s": wall, "flops": total, "kernels": kern, "w": w, "d": d}
 
 
 def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000):
@@ -175,11 +184,7 @@ def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    mla.mla_profile_summary()
-    mla.mla_profile_enable(True)
-    ms, _ = timed(torch, fn, steps, 0, flush)
-    mla.mla_profile_enable(False)
-    kern = kernel_table(mla, steps)
+    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush)
     L = P + 1
     cache_bytes = B * H * L * (192 + 128) * 2
     nbytes = cache_bytes + mla_param_count() * 2 + B * H * 320 * 2 + 2 * B * k["d_model"] * 2
@@ -187,7 +192,7 @@ def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000)
         kern["decode_full"]["gbs"] = cache_bytes / (kern["decode_full"]["avg_ms"] * 1e-3) / 1e9
     del kc, vc
     return {"workload": f"MLA decode, full cache, bf16, B={B}, P={P} (L={L} keys)",
-            "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3),
+            "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev, "tokens_per_s": B / (ms * 1e-3),
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None}
 
@@ -206,18 +211,14 @@ def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=819
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    mla.mla_profile_summary()
-    mla.mla_profile_enable(True)
-    ms, _ = timed(torch, fn, steps, 0, flush)
-    mla.mla_profile_enable(False)
-    kern = kernel_table(mla, steps)
+    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush)
     L = P + 1
     cache_bytes = B * L * 576 * 2
     nbytes = cache_bytes + mla_param_count() * 2 + B * 576 * 2 + 2 * B * k["d_model"] * 2
     if "decode_latent" in kern:
         kern["decode_latent"]["gbs"] = cache_bytes / (kern["decode_latent"]["avg_ms"] * 1e-3) / 1e9
     return {"workload": f"MLA decode, absorbed latent cache, bf16, B={B}, P={P} (L={L} keys)",
-            "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3),
+            "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev, "tokens_per_s": B / (ms * 1e-3),
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None}
 
@@ -239,11 +240,7 @@ def bench_block(torch, mla, dev, d, w, steps, warmup, B=1, T=4096):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    mla.mla_profile_summary()
-    mla.mla_profile_enable(True)
-    ms, _ = timed(torch, fn, steps, 0)
-    mla.mla_profile_enable(False)
-    kern = kernel_table(mla, steps)
+    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps)
     fl = prefill_kernel_flops(B, T)
     flops = sum(fl.values()) + 2.0 * B * T * D * F * 3
     fl["gemm_swiglu"] = 2.0 * B * T * D * F * 2
@@ -252,7 +249,7 @@ def bench_block(torch, mla, dev, d, w, steps, warmup, B=1, T=4096):
         if n in fl:
             v["tflops"] = fl[n] / (v["avg_ms"] * 1e-3) / 1e12
     return {"workload": f"dense block (RMSNorm, MLA, residual, RMSNorm, SwiGLU 18432, residual), bf16, B={B}, T={T}",
-            "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev, "tflops": flops / (ms * 1e-3) / 1e12,
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, "gflop": flops / 1e9,
             "kernels": kern}
 

@@ -38,6 +38,26 @@ hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s);
 int skinny_splits(int K);
 hipError_t gemm_skinny_bf16(GemmParams p, bool bf16_out, hipStream_t s);
 
+// Balanced weight-streaming GEMM (M <= 64): units of 128 weight rows x 128 k
+// dealt out to G workgroups in equal runs; each writes <= 2 fp32 partial
+// blocks [Mp][128] (slots 2 w and 2 w + 1), summed per n-block in workgroup
+// order by stream_reduce / stream_sum4.
+struct StreamInfo {
+  int G;    // workgroups
+  int U;    // units = NB * KS
+  int KS;   // units per 128-column block (K / 128)
+  int NB;   // 128-column blocks
+  int Mp;   // padded rows per partial block (32 or 64)
+};
+bool stream_ok(const GemmParams& p);  // M <= 64, K % 128 == 0, N % 4 == 0, b_split % 128 == 0
+StreamInfo stream_info(int M, int N, int K);
+size_t stream_part_floats(const StreamInfo& s);
+hipError_t gemm_stream_bf16(const GemmParams& p, float* part, const StreamInfo& s, hipStream_t st);
+// out[m, n] = sum of the partials (+ R[m, n] when R is not NULL)
+template <typename T>
+hipError_t stream_reduce(const float* part, const StreamInfo& s, int M, int N, T* out, long ldo,
+                         const bf16_t* R, long ldr, hipStream_t st);
+
 // fp32 generic GEMM: C[b] = (R ? R : 0) + A[b] . op(B[b]); op(B) = B^T when
 // b_is_nk (B stored [N, K]) else B (stored [K, N]).
 struct GemmF32Params {

@@ -187,6 +187,7 @@ struct ProjBufs {
   void* o;      // [M][H*dv]
   void* upart;  // fp32 split-K partials of the small-M up-projections (or NULL)
   size_t upart_floats;
+  void* cred;   // fp32 [M][N1]: the down-projection summed over its stream partials (decode)
 };
 
 void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, ProjBufs* b) {
@@ -196,7 +197,12 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
   b->S = 1;
   b->kchunk = d->d_model;
   if (splitk && d->dtype == MLA_BF16) b->S = skinny_splits(d->d_model);
-  b->part = c.take((size_t)b->S * M * N1 * 4);
+  size_t part_floats = (size_t)b->S * M * N1;
+  if (b->S > 1 && M <= 64) {
+    const size_t sf = stream_part_floats(stream_info(M, N1, d->d_model));
+    if (sf > part_floats) part_floats = sf;
+  }
+  b->part = c.take(part_floats * 4);
   b->cq = c.take((size_t)M * d->q_lora_rank * es);
   b->ckv = c.take((size_t)M * d->kv_lora_rank * es);
   b->kr = c.take((size_t)M * d->qk_rope_dim * es);
@@ -205,6 +211,7 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
   b->o = c.take((size_t)M * H * d->v_head_dim * es);
   b->upart = nullptr;
   b->upart_floats = 0;
+  b->cred = (splitk && d->dtype == MLA_BF16 && M <= 64) ? c.take((size_t)M * N1 * 4) : nullptr;
   if (splitk && d->dtype == MLA_BF16) {
     // partials of the q and kv up-projections when M is small (decode)
     size_t need = 0;
@@ -214,6 +221,10 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
       const int S = skinny_splits(sh[1]);
       size_t n = (size_t)S * M * sh[0];
       if (S > 1 && n > need) need = n;
+      if (M <= 64) {
+        const size_t sf = stream_part_floats(stream_info(M, sh[0], sh[1]));
+        if (sf > need) need = sf;
+      }
     }
     if (need) {
       b->upart = c.take(need * 4);
@@ -230,6 +241,15 @@ int gemm_bf16_out(const char* name, GemmParams g, void* part, size_t part_floats
   if (g.M > 64) {
     LAUNCH(name, gemm_bf16(g, EPI_BF16, -1, st));
     return MLA_OK;
+  }
+  if (stream_ok(g)) {
+    const StreamInfo si = stream_info(g.M, g.N, g.K);
+    if (part && stream_part_floats(si) <= part_floats) {
+      LAUNCH(name, gemm_stream_bf16(g, (float*)part, si, st));
+      LAUNCH("stream_reduce", stream_reduce<bf16_t>((const float*)part, si, g.M, g.N, (bf16_t*)g.C,
+                                                    g.ldc, nullptr, 0, st));
+      return MLA_OK;
+    }
   }
   const int S = skinny_splits(g.K);
   if (S == 1) {
@@ -266,14 +286,24 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
     g.C = b.part; g.ldc = N1;
     g.M = M; g.N = N1; g.K = D;
     g.split_stride = (long)M * N1;
-    if (b.S > 1) {
+    bool streamed = false;
+    if (b.S > 1 && b.cred && stream_ok(g)) {
+      // decode: balanced weight stream; its partials are summed by a wide
+      // reduction (one thread per 4 outputs) before the per-row norms
+      const StreamInfo si = stream_info(M, N1, D);
+      LAUNCH("gemm_down", gemm_stream_bf16(g, (float*)b.part, si, st));
+      LAUNCH("stream_reduce", stream_reduce<float>((const float*)b.part, si, M, N1, (float*)b.cred, N1,
+                                                   nullptr, 0, st));
+      streamed = true;
+    } else if (b.S > 1) {
       LAUNCH("gemm_down", gemm_skinny_bf16(g, false, st));  // decode: K-sliced weight stream
     } else {
       LAUNCH("gemm_down", gemm_bf16(g, EPI_F32, -1, st));
     }
     LatentNormParams<bf16_t> n;
     memset(&n, 0, sizeof n);
-    n.part = (const float*)b.part; n.nsplit = b.S; n.split_stride = (long)M * N1; n.ld_part = N1;
+    n.part = (const float*)(streamed ? b.cred : b.part); n.nsplit = streamed ? 1 : b.S;
+    n.split_stride = (long)M * N1; n.ld_part = N1;
     n.M = M; n.q_lora = ql; n.kv_lora = kl; n.d_rope = dr;
     n.g_q = (const bf16_t*)w->g_q; n.g_kv = (const bf16_t*)w->g_kv; n.eps = d->rms_eps;
     n.cq = (bf16_t*)b.cq; n.ld_cq = ql; n.ckv = (bf16_t*)b.ckv; n.ld_ckv = kl;
@@ -340,7 +370,7 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
 
 // out[M, d] = o[M, H*dv] . W_O^T (+ R).  Split-K for small M (decode).
 int run_oproj(const mla_dims* d, const void* w_o, const void* o, int M, const void* R, void* out,
-              void* part, int S, int kchunk, hipStream_t st) {
+              void* part, size_t part_floats, int S, hipStream_t st) {
   const int D = d->d_model, K = d->n_heads * d->v_head_dim;
   if (d->dtype == MLA_BF16) {
     GemmParams g = gp_base();
@@ -348,7 +378,7 @@ int run_oproj(const mla_dims* d, const void* w_o, const void* o, int M, const vo
     g.M = M; g.N = D; g.K = K;
     if (S > 1) {
       g.C = out; g.ldc = D;
-      return gemm_bf16_out("gemm_o_proj", g, part, (size_t)S * M * D, st);
+      return gemm_bf16_out("gemm_o_proj", g, part, part_floats, st);
     }
     g.C = out; g.ldc = D;
     if (R) { g.R = (const bf16_t*)R; g.ldr = D; }
@@ -412,7 +442,7 @@ int prefill_core(const mla_dims* d, const mla_weights* w, const void* x, int B, 
       LAUNCH("scatter_cache", scatter_full_cache<float>((const float*)b.kv, (const float*)b.kr, (float*)k_cache,
                                        (float*)v_cache, B, T, 0, L_cap, H, dn, dr, dv, st));
   }
-  return run_oproj(d, w->w_o, b.o, M, resid, out, nullptr, 1, 0, st);
+  return run_oproj(d, w->w_o, b.o, M, resid, out, nullptr, 0, 1, st);
 }
 
 // --------------------------------------------------------------- decode
@@ -423,7 +453,8 @@ struct DecodePlan {
   void* apart;      // attention split partials
   int nsplit, chunk;
   int ns_cap;       // split count the partial buffer was sized for
-  void* opart;      // o_proj split partials [S2][B][d]
+  void* opart;      // o_proj split partials ([S2][B][d], or the stream GEMM's blocks)
+  size_t opart_floats;
   int S2, kchunk2;
 };
 
@@ -475,7 +506,13 @@ size_t decode_layout(const mla_dims* d, int B, int L_cap, int form, void* ws, De
   pl->S2 = 1;
   pl->kchunk2 = H * d->v_head_dim;
   if (d->dtype == MLA_BF16 && B <= 64) pl->S2 = skinny_splits(H * d->v_head_dim);
-  pl->opart = c.take((size_t)pl->S2 * B * d->d_model * 4);
+  size_t of = (size_t)pl->S2 * B * d->d_model;
+  if (d->dtype == MLA_BF16 && B <= 64) {
+    const size_t sf = stream_part_floats(stream_info(B, d->d_model, H * d->v_head_dim));
+    if (sf > of) of = sf;
+  }
+  pl->opart = c.take(of * 4);
+  pl->opart_floats = of;
   return c.off + 256;
 }
 
@@ -653,7 +690,7 @@ int mla_decode_fullcache(const mla_dims* d, const mla_weights* w, const void* x,
     a.causal_offset = P; a.scale = d->softmax_scale;
     LAUNCH("attn_generic", attn_generic_f32(a, st));
   }
-  return run_oproj(d, w->w_o, b.o, B, nullptr, out, pl.opart, pl.S2, pl.kchunk2, st);
+  return run_oproj(d, w->w_o, b.o, B, nullptr, out, pl.opart, pl.opart_floats, pl.S2, st);
 }
 
 int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
@@ -731,7 +768,7 @@ int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* 
     u.sA = kl; u.sB = (long)(dn + dv) * kl; u.sC = dv;
     LAUNCH("gemm_uv", gemm_f32(u, st));
   }
-  return run_oproj(d, w->w_o, b.o, B, nullptr, out, pl.opart, pl.S2, pl.kchunk2, st);
+  return run_oproj(d, w->w_o, b.o, B, nullptr, out, pl.opart, pl.opart_floats, pl.S2, st);
 }
 
 size_t dense_block_workspace_size(const mla_dims* d, int B, int T) {

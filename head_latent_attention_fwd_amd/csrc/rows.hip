@@ -30,6 +30,22 @@ MLA_DEV float block_sum256(float v, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
+// Sum of 4 consecutive fp32 columns over the split-K partials p[s * stride],
+// s = 0..nsplit-1, in split order (deterministic).  Loads are issued 8 splits
+// at a time so their latencies overlap instead of one round trip per split.
+MLA_DEV floatx4 sum_splits4(const float* __restrict__ p, long stride, int nsplit) {
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    floatx4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = s0 + j < nsplit ? *(const floatx4*)(p + (long)(s0 + j) * stride) : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += v[j];
+  }
+  return acc;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void latent_norm_rope_kernel(LatentNormParams<T> p) {
   extern __shared__ float row[];  // [q_lora + kv_lora + d_rope]
@@ -43,9 +59,7 @@ __global__ __launch_bounds__(256) void latent_norm_rope_kernel(LatentNormParams<
   const bool vec = (N1 % 4 == 0) && (p.ld_part % 4 == 0) && (p.split_stride % 4 == 0);
   if (vec) {
     for (int c4 = tid; c4 < N1 / 4; c4 += 256) {
-      const float* src = p.part + (long)m * p.ld_part + 4 * c4;
-      floatx4 v = *(const floatx4*)src;
-      for (int s = 1; s < p.nsplit; ++s) v += *(const floatx4*)(src + (long)s * p.split_stride);
+      const floatx4 v = sum_splits4(p.part + (long)m * p.ld_part + 4 * c4, p.split_stride, p.nsplit);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c = 4 * c4 + q;
@@ -252,8 +266,7 @@ __global__ void reduce_splits_kernel(const float* __restrict__ part, int nsplit,
   const long e = 4 * e4;
   const long m = e / N;
   const int n = (int)(e % N);
-  floatx4 v = *(const floatx4*)(part + e);
-  for (int s = 1; s < nsplit; ++s) v += *(const floatx4*)(part + s * stride + e);
+  const floatx4 v = sum_splits4(part + e, stride, nsplit);
 #pragma unroll
   for (int q = 0; q < 4; ++q) out[m * ldo + n + q] = from_f<T>(v[q]);
 }
