@@ -29,6 +29,9 @@ struct GemmParams {
   int tiles_m, tiles_n;  // filled by the launcher
 };
 
+struct GemmPlan { int cfg, ksplit, kchunk; };
+// tile config and K split (<= max_split; splits need fp32 partial outputs)
+GemmPlan gemm_plan(int M, int N, int K, int batch, int max_split);
 int gemm_pick_cfg(int M, int N, int K, int batch);
 hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s);
 

@@ -151,21 +151,6 @@ int check_i32(long elems, const char* what) {
   return MLA_OK;
 }
 
-// Split-K plan for the bf16 GEMM: enough workgroups to cover the CUs.
-void plan_splitk(int M, int N, int K, int* S, int* kchunk) {
-  int cfg = gemm_pick_cfg(M, N, K, 1);
-  int bm = cfg == GEMM_CFG_256x256 ? 256 : (cfg == GEMM_CFG_128x128 ? 128 : 64);
-  int bn = cfg == GEMM_CFG_256x256 ? 256 : 128;
-  long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-  int kb = K / 64;
-  int s = (int)((256 + tiles - 1) / tiles);
-  if (s < 1) s = 1;
-  if (s > kb) s = kb;
-  if (s > 32) s = 32;
-  int per = (kb + s - 1) / s;
-  *kchunk = per * 64;
-  *S = (kb + per - 1) / per;
-}
 
 GemmParams gp_base() {
   GemmParams p;
@@ -179,6 +164,8 @@ GemmParams gp_base() {
 struct ProjBufs {
   void* part;   // fp32 [S][M][N1]
   int S, kchunk;
+  int cfg;      // tile config of the down-projection GEMM (prefill)
+  bool decode;  // small-M weight-streaming products
   void* cq;     // [M][q_lora]
   void* ckv;    // [M][kv_lora]
   void* kr;     // [M][d_rope]
@@ -196,9 +183,20 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
   const size_t es = esize(d);
   b->S = 1;
   b->kchunk = d->d_model;
-  if (splitk && d->dtype == MLA_BF16) b->S = skinny_splits(d->d_model);
+  b->cfg = GEMM_CFG_AUTO;
+  b->decode = splitk && d->dtype == MLA_BF16 && M <= 64;
+  if (b->decode) {
+    b->S = skinny_splits(d->d_model);
+  } else if (d->dtype == MLA_BF16) {
+    // the down-projection writes fp32 partials that the latent norm sums, so
+    // it may split K to balance its few tiles over the CUs
+    const GemmPlan gp = gemm_plan(M, N1, d->d_model, 1, 4);
+    b->S = gp.ksplit;
+    b->kchunk = gp.kchunk;
+    b->cfg = gp.cfg;
+  }
   size_t part_floats = (size_t)b->S * M * N1;
-  if (b->S > 1 && M <= 64) {
+  if (b->decode) {
     const size_t sf = stream_part_floats(stream_info(M, N1, d->d_model));
     if (sf > part_floats) part_floats = sf;
   }
@@ -211,7 +209,7 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
   b->o = c.take((size_t)M * H * d->v_head_dim * es);
   b->upart = nullptr;
   b->upart_floats = 0;
-  b->cred = (splitk && d->dtype == MLA_BF16 && M <= 64) ? c.take((size_t)M * N1 * 4) : nullptr;
+  b->cred = b->decode ? c.take((size_t)M * N1 * 4) : nullptr;
   if (splitk && d->dtype == MLA_BF16) {
     // partials of the q and kv up-projections when M is small (decode)
     size_t need = 0;
@@ -287,7 +285,7 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
     g.M = M; g.N = N1; g.K = D;
     g.split_stride = (long)M * N1;
     bool streamed = false;
-    if (b.S > 1 && b.cred && stream_ok(g)) {
+    if (b.decode && stream_ok(g)) {
       // decode: balanced weight stream; its partials are summed by a wide
       // reduction (one thread per 4 outputs) before the per-row norms
       const StreamInfo si = stream_info(M, N1, D);
@@ -295,10 +293,12 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
       LAUNCH("stream_reduce", stream_reduce<float>((const float*)b.part, si, M, N1, (float*)b.cred, N1,
                                                    nullptr, 0, st));
       streamed = true;
-    } else if (b.S > 1) {
+    } else if (b.decode) {
       LAUNCH("gemm_down", gemm_skinny_bf16(g, false, st));  // decode: K-sliced weight stream
     } else {
-      LAUNCH("gemm_down", gemm_bf16(g, EPI_F32, -1, st));
+      g.ksplit = b.S;
+      g.kchunk = b.kchunk;
+      LAUNCH("gemm_down", gemm_bf16(g, EPI_F32, b.cfg, st));
     }
     LatentNormParams<bf16_t> n;
     memset(&n, 0, sizeof n);
