@@ -27,6 +27,17 @@
 namespace mla {
 
 #define MLA_SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+// Direct-to-LDS pipeline shape: k per stage and ring depth.  Measured on the
+// prefill shapes: 64-k stages (whole 128-byte lines per tile row) in a
+// 2-deep ring beat 32-k stages in a 3- or 4-deep ring (o_proj 187 vs 205 us):
+// half-line requests cost more than the shorter prefetch distance, and a
+// deeper ring would cost the 128x128 tile its second workgroup per CU.
+#ifndef GEMM_DMA_SK
+#define GEMM_DMA_SK(bm) 64
+#endif
+#ifndef GEMM_DMA_NSTG
+#define GEMM_DMA_NSTG(bm) 2
+#endif
 enum { SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200 };
 
 // LDS swizzle of the 16-byte chunk of a 128-byte tile row.  gfx950 serves a
@@ -35,7 +46,30 @@ enum { SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200 }
 // rows share a 256-byte line, and (row >> 1) spreads eight line pairs.
 MLA_DEV int gemm_swz(int r) { return (r >> 1) & 7; }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// Wave-wide direct-to-LDS load of 16 bytes per lane (global rsrc.base + voff
+// -> LDS byte m0 + 16 lane); issued from asm so the compiler's wait counting
+// (which cannot tell ring stages apart) stays out: the kernel waits with
+// explicit vmcnt values.
+MLA_DEV void gemm_dma16(unsigned m0, int voff, u32x4 rsrc) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(m0), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+MLA_DEV u32x4 gemm_rsrc(const void* base) {
+  const unsigned long a = (unsigned long)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu);
+  r[2] = 0x7fffffffu;  // rows are clamped in range; offsets stay below 2^31
+  r[3] = 0x00020000u;
+  return r;
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, bool DMA>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -50,7 +84,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
   static_assert(A_CH >= 1 && B_CH >= 1, "tile too small for the block");
   static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU pairs 32-column blocks inside a wave");
 
-  __shared__ u32x4 lds[2][(BM + BN) * 8];
+  // LDS: the two-stage register-staged layout, or the direct-to-LDS ring
+  constexpr int LDS_U4_REG = 2 * (BM + BN) * 8;
+  constexpr int LDS_U4_DMA = DMA ? GEMM_DMA_NSTG(BM) * (BM + BN) * GEMM_DMA_SK(BM) * 2 / 16 : 0;
+  constexpr int LDS_U4 = LDS_U4_REG > LDS_U4_DMA ? LDS_U4_REG : LDS_U4_DMA;
+  __shared__ u32x4 lds_raw[LDS_U4];
+  u32x4 (*lds)[(BM + BN) * 8] = reinterpret_cast<u32x4 (*)[(BM + BN) * 8]>(lds_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -78,56 +117,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
   const int k_end = min(p.K, k_begin + p.kchunk);
   const int nk = (k_end - k_begin) / 64;
 
-  // ---- per-thread global source rows as 32-bit element offsets (rows past
-  //      the edge are clamped: loaded from a valid row and never stored) ----
-  const int ch = tid & 7;
-  int a_off[A_CH], b_off[B_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    int r = tid / 8 + i * ROWS_PER_PASS;
-    int gr = min(m0 + r, p.M - 1);
-    a_off[i] = gr * (int)p.lda + ch * 8 + k_begin;
-  }
-  unsigned b2mask = 0;  // bit i: chunk row i comes from B2
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    int r = tid / 8 + i * ROWS_PER_PASS;
-    int src;
-    if (EPI == EPI_SWIGLU) {
-      int rb = r >> 5;
-      src = min(n0 / 2 + (rb >> 1) * 32 + (r & 31), p.N / 2 - 1);
-      if (rb & 1) b2mask |= 1u << i;
-    } else {
-      src = min(n0 + r, p.N - 1);
-      if (p.b_split > 0 && src >= p.b_split) {
-        src -= p.b_split;
-        b2mask |= 1u << i;
-      }
-    }
-    b_off[i] = src * (int)p.ldb + ch * 8 + k_begin;
-  }
-  // LDS slots this thread stores into (u32x4 units)
-  int st_idx[NLD];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int r = tid / 8 + i * ROWS_PER_PASS;
-    st_idx[i] = r * 8 + (ch ^ gemm_swz(r));
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int r = tid / 8 + i * ROWS_PER_PASS;
-    st_idx[A_CH + i] = (BM + r) * 8 + (ch ^ gemm_swz(r));
-  }
-
-  // Software pipeline: the K tile in LDS buffer `cur` is multiplied in four
-  // 16-wide steps while (step 0) the next tile's global loads are issued,
-  // (steps 0-2) the next step's MFMA fragments are read from LDS into the
-  // other fragment register set, and (step 3) the next tile is stored to the
-  // other LDS buffer, one barrier is passed and its first fragments are read.
-  // sched_group_barrier interleaves those memory instructions with the MFMAs
-  // so the matrix pipe is never left waiting on a load issued just before.
-  u32x4 stg[NLD];
-  bf16x8 fa[2][FM], fb[2][FN];
   floatx16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -135,99 +124,275 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
   const int lr = lane & 31, lg = lane >> 5;
-#define GEMM_GLOAD(kt_)                                                                   \
-  do {                                                                                    \
-    const int ko_ = (kt_) * 64;                                                           \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                      \
-        stg[i] = *(const u32x4*)(A + a_off[i] + ko_);                                      \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                    \
-      const bf16_t* src_ = ((b2mask >> i) & 1) ? B2 : B;                                   \
-      stg[A_CH + i] = *(const u32x4*)(src_ + b_off[i] + ko_);                              \
-    }                                                                                     \
-  } while (0)
-#define GEMM_SSTORE(buf)                                                                  \
-  do {                                                                                    \
-    _Pragma("unroll") for (int i = 0; i < NLD; ++i) lds[buf][st_idx[i]] = stg[i];         \
-  } while (0)
-#define GEMM_FREAD(buf, s, slot)                                                          \
-  do {                                                                                    \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                      \
-      const int r = wm * WTM + i * 32 + lr;                                               \
-      fa[slot][i] = __builtin_bit_cast(bf16x8, lds[buf][r * 8 + ((2 * (s) + lg) ^ gemm_swz(r))]); \
-    }                                                                                     \
-    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                      \
-      const int r = wn * WTN + j * 32 + lr;                                               \
-      fb[slot][j] = __builtin_bit_cast(bf16x8, lds[buf][(BM + r) * 8 + ((2 * (s) + lg) ^ gemm_swz(r))]); \
-    }                                                                                     \
-  } while (0)
-#define GEMM_MFMAS(slot, lo, hi)                                                          \
-  do {                                                                                    \
-    _Pragma("unroll") for (int q = (lo); q < (hi); ++q) {                                 \
-      const int i = q / FN, j = q % FN;                                                   \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0); \
-    }                                                                                     \
-  } while (0)
 
-  if (nk > 0) {
-    GEMM_GLOAD(0);
-    GEMM_SSTORE(0);
+  if constexpr (DMA) {
+    // Direct-to-LDS pipeline.  K advances in stages of SK (tile rows of SK*2
+    // bytes, CH chunks of 16 B; chunk c of row r at position c ^ swz(r), with
+    // swz spreading the rows that share a 256-byte bank window).  An NSTG
+    // ring: the loads of stage t + NSTG are issued in iteration t, after the
+    // barrier that frees stage t's buffer.  Within a stage, k-step s + 1's
+    // fragments are read under k-step s's MFMAs; the barrier sits before the
+    // last k-step, whose MFMAs cover the next stage's first fragment reads.
+    constexpr int SK = GEMM_DMA_SK(BM);
+    constexpr int NSTG = GEMM_DMA_NSTG(BM);
+    constexpr int KSTEPS = SK / 16, CH = SK / 8, ROWB = SK * 2;
+    constexpr int RPW = 256 / ROWB;  // rows per 256-byte bank window
+    constexpr int NW = WM * WN;
+    constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE_B = A_BYTES + B_BYTES;
+    constexpr int A_DMA = A_BYTES / 1024 / NW, B_DMA = B_BYTES / 1024 / NW;  // per wave per stage
+    constexpr int DPW = A_DMA + B_DMA;
+    constexpr int RPD = 1024 / ROWB;  // rows per DMA
+    static_assert(KSTEPS % 2 == 0, "k-steps per stage");
+    static_assert(A_DMA >= 1 && B_DMA >= 1 && A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0,
+                  "DMA split");
+    static_assert(NSTG * STAGE_B <= LDS_U4 * 16, "ring does not fit the LDS");
+    auto swz = [](int r) { return (r / RPW) & (CH - 1); };
+    const unsigned lds_base = (unsigned)(unsigned long)(__attribute__((address_space(3))) char*)&lds[0][0];
+    const int wv = __builtin_amdgcn_readfirstlane(wid);
+    // DMA d of this wave fills tile rows RPD g .. RPD g + RPD - 1 (g = wv *
+    // X_DMA + d): lane l -> row RPD g + l / CH, chunk position l % CH
+    int a_vo[A_DMA], b_vo[B_DMA];
+    unsigned b_src2 = 0;  // bit d: DMA d reads from B2
+#pragma unroll
+    for (int d = 0; d < A_DMA; ++d) {
+      const int r = RPD * (wv * A_DMA + d) + lane / CH;
+      const int c = (lane % CH) ^ swz(r);
+      a_vo[d] = (min(m0 + r, p.M - 1) * (int)p.lda + k_begin + 8 * c) * 2;
+    }
+#pragma unroll
+    for (int d = 0; d < B_DMA; ++d) {
+      const int r = RPD * (wv * B_DMA + d) + lane / CH;
+      const int c = (lane % CH) ^ swz(r);
+      int src;
+      if (EPI == EPI_SWIGLU) {
+        const int rb = r >> 5;
+        src = min(n0 / 2 + (rb >> 1) * 32 + (r & 31), p.N / 2 - 1);
+        if (rb & 1) b_src2 |= 1u << d;
+      } else {
+        src = min(n0 + r, p.N - 1);
+        if (p.b_split > 0 && n0 + RPD * (wv * B_DMA + d) >= p.b_split) {
+          src -= p.b_split;
+          b_src2 |= 1u << d;
+        }
+      }
+      b_vo[d] = (src * (int)p.ldb + k_begin + 8 * c) * 2;
+    }
+    const u32x4 ra = gemm_rsrc(A), rb1 = gemm_rsrc(B), rb2 = gemm_rsrc(B2 ? B2 : B);
+    const int nst = (k_end - k_begin) / SK;
+#define GD_ISSUE(u_)                                                                         \
+  do {                                                                                       \
+    const unsigned sb_ = lds_base + ((u_) % NSTG) * STAGE_B;                                 \
+    const int ko_ = ROWB * (u_);                                                             \
+    _Pragma("unroll") for (int d = 0; d < A_DMA; ++d)                                        \
+      gemm_dma16(sb_ + 1024 * (wv * A_DMA + d), a_vo[d] + ko_, ra);                          \
+    _Pragma("unroll") for (int d = 0; d < B_DMA; ++d)                                        \
+      gemm_dma16(sb_ + A_BYTES + 1024 * (wv * B_DMA + d), b_vo[d] + ko_,                     \
+                 ((b_src2 >> d) & 1) ? rb2 : rb1);                                           \
+  } while (0)
+#define GD_WAIT(n_after)                                                                     \
+  do {                                                                                       \
+    if ((n_after) >= 2 && NSTG >= 4) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * DPW) : "memory"); \
+    else if ((n_after) >= 1 && NSTG >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(DPW) : "memory"); \
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                    \
+  } while (0)
+    // fragment rows are lr (mod 32), so swz(row) = swz(lr) for every fragment
+    const int sw = swz(lr);
+    const int a_rd = (wm * WTM + lr) * ROWB, b_rd = A_BYTES + (wn * WTN + lr) * ROWB;
+    const char* ldsc = (const char*)&lds[0][0];
+#define GD_FREAD(u_, s_, slot)                                                               \
+  do {                                                                                       \
+    const char* sb_ = ldsc + ((u_) % NSTG) * STAGE_B;                                        \
+    const int co_ = 16 * ((2 * (s_) + lg) ^ sw);                                             \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                           \
+      fa[slot][i] = *(const bf16x8*)(sb_ + a_rd + i * 32 * ROWB + co_);                      \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
+      fb[slot][j] = *(const bf16x8*)(sb_ + b_rd + j * 32 * ROWB + co_);                      \
+  } while (0)
+#define GD_MFMAS(slot)                                                                       \
+  _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                          \
+    const int i = q / FN, j = q % FN;                                                        \
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0); \
   }
-  __syncthreads();
-  if (nk > 0) GEMM_FREAD(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
-    const int kn = min(kt + 1, nk - 1);  // the last iteration reloads a valid tile
-    // step 0
-    GEMM_GLOAD(kn);
-    GEMM_FREAD(cur, 1, 1);
-    GEMM_MFMAS(0, 0, NMF);
-#pragma unroll
-    for (int q = 0; q < NMF; ++q) {
-      MLA_SGB(SG_MFMA, 1);
-      if (q < NLD) MLA_SGB(SG_VMEM_RD, (NLD + NMF - 1) / NMF);
-      if (q < NRD) MLA_SGB(SG_DS_RD, (NRD + NMF - 1) / NMF);
+#define GD_SCHED()                                                                           \
+  _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                          \
+    MLA_SGB(SG_MFMA, 1);                                                                     \
+    if (q < NRD) MLA_SGB(SG_DS_RD, 1);                                                       \
+  }
+    bf16x8 fa[2][FM], fb[2][FN];
+    for (int u = 0; u < NSTG - 1 && u < nst; ++u) GD_ISSUE(u);
+    if (nst > 0) {
+      GD_WAIT(min(NSTG - 2, nst - 1));
+      __syncthreads();
+      if (nst > NSTG - 1) GD_ISSUE(NSTG - 1);
+      GD_FREAD(0, 0, 0);
     }
-    // step 1
-    GEMM_FREAD(cur, 2, 0);
-    GEMM_MFMAS(1, 0, NMF);
+    for (int t = 0; t < nst; ++t) {
 #pragma unroll
-    for (int q = 0; q < NMF; ++q) {
-      MLA_SGB(SG_MFMA, 1);
-      MLA_SGB(SG_DS_RD, (NRD + NMF - 1) / NMF);
+      for (int s = 0; s + 1 < KSTEPS; ++s) {
+        GD_FREAD(t, s + 1, (s + 1) & 1);
+        GD_MFMAS(s & 1)
+        GD_SCHED()
+      }
+      // Straight-line on purpose (the last iteration re-reads its own
+      // stage): a branch around these reads would make the compiler wait
+      // for them before the MFMAs below, at the join.
+      GD_WAIT(min(NSTG - 2, nst - 2 - t));
+      __syncthreads();
+      if (t + NSTG < nst) GD_ISSUE(t + NSTG);  // into stage t's buffer, free now
+      GD_FREAD(min(t + 1, nst - 1), 0, 0);
+      GD_MFMAS(1)
+      GD_SCHED()
     }
-    // step 2
-    GEMM_FREAD(cur, 3, 1);
-    GEMM_MFMAS(0, 0, NMF);
-#pragma unroll
-    for (int q = 0; q < NMF; ++q) {
-      MLA_SGB(SG_MFMA, 1);
-      MLA_SGB(SG_DS_RD, (NRD + NMF - 1) / NMF);
+#undef GD_ISSUE
+#undef GD_WAIT
+#undef GD_FREAD
+#undef GD_MFMAS
+#undef GD_SCHED
+  } else {
+  // ---- per-thread global source rows as 32-bit element offsets (rows past
+    //      the edge are clamped: loaded from a valid row and never stored) ----
+    const int ch = tid & 7;
+    int a_off[A_CH], b_off[B_CH];
+  #pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      int r = tid / 8 + i * ROWS_PER_PASS;
+      int gr = min(m0 + r, p.M - 1);
+      a_off[i] = gr * (int)p.lda + ch * 8 + k_begin;
     }
-    // step 3: store the next tile under half the MFMAs, barrier, read its
-    // first fragments under the other half
-    GEMM_SSTORE(nxt);
-    GEMM_MFMAS(1, 0, NMF / 2);
-#pragma unroll
-    for (int q = 0; q < NMF / 2; ++q) {
-      MLA_SGB(SG_MFMA, 1);
-      MLA_SGB(SG_DS_WR, (2 * NLD + NMF - 1) / NMF);
+    unsigned b2mask = 0;  // bit i: chunk row i comes from B2
+  #pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      int r = tid / 8 + i * ROWS_PER_PASS;
+      int src;
+      if (EPI == EPI_SWIGLU) {
+        int rb = r >> 5;
+        src = min(n0 / 2 + (rb >> 1) * 32 + (r & 31), p.N / 2 - 1);
+        if (rb & 1) b2mask |= 1u << i;
+      } else {
+        src = min(n0 + r, p.N - 1);
+        if (p.b_split > 0 && src >= p.b_split) {
+          src -= p.b_split;
+          b2mask |= 1u << i;
+        }
+      }
+      b_off[i] = src * (int)p.ldb + ch * 8 + k_begin;
+    }
+    // LDS slots this thread stores into (u32x4 units)
+    int st_idx[NLD];
+  #pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int r = tid / 8 + i * ROWS_PER_PASS;
+      st_idx[i] = r * 8 + (ch ^ gemm_swz(r));
+    }
+  #pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int r = tid / 8 + i * ROWS_PER_PASS;
+      st_idx[A_CH + i] = (BM + r) * 8 + (ch ^ gemm_swz(r));
+    }
+  
+    // Software pipeline: the K tile in LDS buffer `cur` is multiplied in four
+    // 16-wide steps while (step 0) the next tile's global loads are issued,
+    // (steps 0-2) the next step's MFMA fragments are read from LDS into the
+    // other fragment register set, and (step 3) the next tile is stored to the
+    // other LDS buffer, one barrier is passed and its first fragments are read.
+    // sched_group_barrier interleaves those memory instructions with the MFMAs
+    // so the matrix pipe is never left waiting on a load issued just before.
+    u32x4 stg[NLD];
+    bf16x8 fa[2][FM], fb[2][FN];
+  
+  #define GEMM_GLOAD(kt_)                                                                   \
+    do {                                                                                    \
+      const int ko_ = (kt_) * 64;                                                           \
+      _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                      \
+          stg[i] = *(const u32x4*)(A + a_off[i] + ko_);                                      \
+      _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                    \
+        const bf16_t* src_ = ((b2mask >> i) & 1) ? B2 : B;                                   \
+        stg[A_CH + i] = *(const u32x4*)(src_ + b_off[i] + ko_);                              \
+      }                                                                                     \
+    } while (0)
+  #define GEMM_SSTORE(buf)                                                                  \
+    do {                                                                                    \
+      _Pragma("unroll") for (int i = 0; i < NLD; ++i) lds[buf][st_idx[i]] = stg[i];         \
+    } while (0)
+  #define GEMM_FREAD(buf, s, slot)                                                          \
+    do {                                                                                    \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                      \
+        const int r = wm * WTM + i * 32 + lr;                                               \
+        fa[slot][i] = __builtin_bit_cast(bf16x8, lds[buf][r * 8 + ((2 * (s) + lg) ^ gemm_swz(r))]); \
+      }                                                                                     \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                      \
+        const int r = wn * WTN + j * 32 + lr;                                               \
+        fb[slot][j] = __builtin_bit_cast(bf16x8, lds[buf][(BM + r) * 8 + ((2 * (s) + lg) ^ gemm_swz(r))]); \
+      }                                                                                     \
+    } while (0)
+  #define GEMM_MFMAS(slot, lo, hi)                                                          \
+    do {                                                                                    \
+      _Pragma("unroll") for (int q = (lo); q < (hi); ++q) {                                 \
+        const int i = q / FN, j = q % FN;                                                   \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0); \
+      }                                                                                     \
+    } while (0)
+  
+    if (nk > 0) {
+      GEMM_GLOAD(0);
+      GEMM_SSTORE(0);
     }
     __syncthreads();
-    GEMM_FREAD(nxt, 0, 0);
-    GEMM_MFMAS(1, NMF / 2, NMF);
-#pragma unroll
-    for (int q = 0; q < NMF / 2; ++q) {
-      MLA_SGB(SG_MFMA, 1);
-      MLA_SGB(SG_DS_RD, (2 * NRD + NMF - 1) / NMF);
+    if (nk > 0) GEMM_FREAD(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1, nxt = cur ^ 1;
+      const int kn = min(kt + 1, nk - 1);  // the last iteration reloads a valid tile
+      // step 0
+      GEMM_GLOAD(kn);
+      GEMM_FREAD(cur, 1, 1);
+      GEMM_MFMAS(0, 0, NMF);
+  #pragma unroll
+      for (int q = 0; q < NMF; ++q) {
+        MLA_SGB(SG_MFMA, 1);
+        if (q < NLD) MLA_SGB(SG_VMEM_RD, (NLD + NMF - 1) / NMF);
+        if (q < NRD) MLA_SGB(SG_DS_RD, (NRD + NMF - 1) / NMF);
+      }
+      // step 1
+      GEMM_FREAD(cur, 2, 0);
+      GEMM_MFMAS(1, 0, NMF);
+  #pragma unroll
+      for (int q = 0; q < NMF; ++q) {
+        MLA_SGB(SG_MFMA, 1);
+        MLA_SGB(SG_DS_RD, (NRD + NMF - 1) / NMF);
+      }
+      // step 2
+      GEMM_FREAD(cur, 3, 1);
+      GEMM_MFMAS(0, 0, NMF);
+  #pragma unroll
+      for (int q = 0; q < NMF; ++q) {
+        MLA_SGB(SG_MFMA, 1);
+        MLA_SGB(SG_DS_RD, (NRD + NMF - 1) / NMF);
+      }
+      // step 3: store the next tile under half the MFMAs, barrier, read its
+      // first fragments under the other half
+      GEMM_SSTORE(nxt);
+      GEMM_MFMAS(1, 0, NMF / 2);
+  #pragma unroll
+      for (int q = 0; q < NMF / 2; ++q) {
+        MLA_SGB(SG_MFMA, 1);
+        MLA_SGB(SG_DS_WR, (2 * NLD + NMF - 1) / NMF);
+      }
+      __syncthreads();
+      GEMM_FREAD(nxt, 0, 0);
+      GEMM_MFMAS(1, NMF / 2, NMF);
+  #pragma unroll
+      for (int q = 0; q < NMF / 2; ++q) {
+        MLA_SGB(SG_MFMA, 1);
+        MLA_SGB(SG_DS_RD, (2 * NRD + NMF - 1) / NMF);
+      }
     }
+  
+  #undef GEMM_FREAD
+  #undef GEMM_MFMAS
+  #undef GEMM_GLOAD
+  #undef GEMM_SSTORE
   }
-
-#undef GEMM_FREAD
-#undef GEMM_MFMAS
-#undef GEMM_GLOAD
-#undef GEMM_SSTORE
 
   // ---- epilogue.  A lane holds column (lane & 31) of each 32x32 block and
   //      rows 8*i + 4*(lane >> 5) + j in acc[...][4*i + j]. ----
@@ -321,7 +486,19 @@ static hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;  // SwiGLU: N counts both W1 and W3 columns
   dim3 grid(p.tiles_m * p.tiles_n, p.batch * p.ksplit);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), grid, dim3(WM * WN * 64), 0, s, p);
+  // direct-to-LDS pipeline: whole k stages, byte offsets within 2^31, B2
+  // rows starting on a 16-row boundary
+  const long rowsA = p.M, rowsB = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
+  const bool dma = BM >= 128 && p.kchunk % GEMM_DMA_SK(BM) == 0 && p.K % GEMM_DMA_SK(BM) == 0 &&
+                   rowsA * p.lda * 2 < 0x7fffffffL && rowsB * p.ldb * 2 < 0x7fffffffL &&
+                   (p.b_split <= 0 || p.b_split % 16 == 0);
+  if constexpr (BM >= 128) {
+    if (dma) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI, true>), grid, dim3(WM * WN * 64), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI, false>), grid, dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -335,14 +512,11 @@ static hipError_t launch_epi(GemmParams p, int cfg, hipStream_t s) {
   }
 }
 
-// Tile choice (measured on MI355X over the projection shapes): the 256x256
-// eight-wave tile wins when K is long enough to amortise its prologue and
-// there are enough tiles to cover the CUs; otherwise 128x128.  Small-M
-// (decode) products use a 64-row tile whose weight stream dominates.
 // Tile config and split-K count by a wave-quantisation cost model: a launch
 // of T work units runs in ceil(T / 256) waves on the 256 CUs, each wave as
 // long as one unit (a tile over K / S), and a 256x256 tile computes about
-// 1.2x faster per CU than four 128x128 tiles (fewer LDS bytes per MFMA).
+// 1.35x faster per CU than four 128x128 tiles (fewer LDS bytes per MFMA;
+// measured 1.3-1.4 on the prefill shapes).
 // Measured on the prefill shapes (M = 2048): it picks 256x256 with three
 // K splits for the 2112 x 7168 down-projection, 128x128 for the q
 // up-projection and 256x256 for kv and o_proj.
@@ -353,7 +527,7 @@ GemmPlan gemm_plan(int M, int N, int K, int batch, int max_split) {
   const int kb = (K + 63) / 64;
   for (int cfg : {GEMM_CFG_256x256, GEMM_CFG_128x128}) {
     const int b = cfg == GEMM_CFG_256x256 ? 256 : 128;
-    const double rate = cfg == GEMM_CFG_256x256 ? 1.2 : 1.0;
+    const double rate = cfg == GEMM_CFG_256x256 ? 1.35 : 1.0;
     const long tiles = (long)((M + b - 1) / b) * ((N + b - 1) / b) * batch;
     for (int S = 1; S <= max_split; ++S) {
       const int per = (kb + S - 1) / S;
