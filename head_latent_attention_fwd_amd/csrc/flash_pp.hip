@@ -1,0 +1,337 @@
+// Causal flash attention for the MLA prefill, bf16 with fp32 softmax, gfx950:
+// ping-pong form.
+//
+// What it computes is what flash_prefill.hip computes ("Kimi K2 · Mix and
+// project", code excerpt; query/key assembly of "Kimi K2 · Dense transformer
+// block"): s_ij = scale * [Q^C ; Q^R]_i . [K^C_h ; k^R]_j over keys j <= i,
+// a float32 softmax over j, O_i = sum_j p_ij V_h,j, written into the
+// head-merged layout [B*T, H*128].  RoPE of the query's rotary part is applied
+// as the query fragments are loaded.
+//
+// Why a second form: with one barrier per key tile, all eight waves run the
+// QK products, the softmax and the PV products in lockstep, so the two waves
+// sharing a SIMD reach their softmax (VALU) together and the matrix pipe
+// idles.  Here the waves of the second half (4..7) run the same work rotated
+// by one phase: in segment k the first half runs QK(k), softmax(k), PV(k) and
+// the second half runs softmax(k-1), PV(k-1), QK(k), so while one wave of a
+// SIMD is in its softmax the other issues MFMAs.
+//
+// Data movement: per key tile (64 keys) the content key tile [64 x 256 B],
+// the rotary key tile [64 x 128 B] and the value tile [64 x 256 B] (row-major,
+// as in memory) arrive by wave-wide direct-to-LDS buffer loads into a ring of
+// NST stages; keys past T read as zero (buffer range) and are masked anyway
+// by causality.  A tile is live in three consecutive segments (loading; first
+// half + second-half QK; second-half PV), so the ring holds NST >= 3 tiles and
+// the loads of tile k + NST - 2 are issued at the start of segment k.
+//
+// Products (v_mfma_f32_32x32x16_bf16): S^T = K . Q^T with key rows as the A
+// operand (from LDS) and the wave's 32 queries as the B operand (registers),
+// so each lane owns one query column and the softmax statistics are
+// lane-local (plus one cross-half shuffle).  O^T = V^T . P^T with the score
+// accumulator converted to bf16 as the B operand, and the V^T operand read
+// from the row-major value tile with ds_read_b64_tr_b16: within each 16-lane
+// group, output lane i receives element i % 4 of the 8-byte rows addressed by
+// lanes i / 4 + 4 j (j = 0..3), so lanes addressing 4 consecutive key rows x 4
+// feature quads yield, per lane, one feature over 4 consecutive keys.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+constexpr int PP_BQ = 256;                   // queries per workgroup: 8 waves x 32
+constexpr int PP_NST = 3;                    // LDS ring stages
+constexpr int PP_KC = 64 * 256;              // content key tile (128 features)
+constexpr int PP_KR = 64 * 128;              // rotary key tile (64 features)
+constexpr int PP_V = 64 * 256;               // value tile (128 features)
+constexpr int PP_STG = PP_KC + PP_KR + PP_V; // 40 KB
+constexpr int PP_DPW = 5;                    // DMAs per wave per tile (2 + 1 + 2)
+constexpr float PP_LAZY = 8.0f;              // raise the running max past this margin (log2)
+
+MLA_DEV void pp_dma16(unsigned m0, int voff, u32x4 rsrc) {
+  // lane l's 16 bytes at rsrc.base + voff -> LDS byte m0 + 16 l (explicit
+  // vmcnt waits below; the compiler's counting cannot tell ring stages apart)
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(m0), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+MLA_DEV u32x4 pp_rsrc(const void* base, long bytes) {
+  const unsigned long a = (unsigned long)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane((unsigned)(bytes > 0x7fffffffL ? 0x7fffffffL : bytes));
+  r[3] = 0x00020000u;
+  return r;
+}
+}  // namespace
+
+__global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[PP_NST * PP_STG];
+  const unsigned lds_base = (unsigned)(unsigned long)(__attribute__((address_space(3))) char*)lds;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lg = lane >> 5;
+  const bool second = w >= 4;  // rotated phase
+  const int nqt = (p.T + PP_BQ - 1) / PP_BQ;
+  const int HB = p.H * p.B;
+  const int qt = nqt - 1 - (int)(blockIdx.x / HB);  // longest query tiles first
+  const int rem = blockIdx.x % HB;
+  const int h = rem % p.H, b = rem / p.H;
+  const int q0 = qt * PP_BQ;
+  const long rowbase = (long)b * p.T;
+  const long HS = p.H;
+
+  // this wave's 32 queries as MFMA B fragments: features 16 s + 8 lg .. +8;
+  // the rotary features (s >= 8) are rotated by the RoPE row of the position
+  bf16x8 qf[12];
+  {
+    const int qrow = min(q0 + 32 * w + lr, p.T - 1);
+    const bf16_t* qp = p.q + ((rowbase + qrow) * HS + h) * 192 + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 12; ++s) {
+      u32x4 v = *(const u32x4*)(qp + 16 * s);
+      if (s >= 8) v = rope8_bf16(v, p.rcos, p.rsin, qrow, 32, (16 * s + 8 * lg - 128) / 2);
+      qf[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  const int qlast = min(q0 + PP_BQ - 1, p.T - 1);
+  const int n_kv = qlast / 64 + 1;
+  const int qi = q0 + 32 * w + lr;
+  const int wq_first = q0 + 32 * w, wq_last = wq_first + 31;
+
+  // ---- loaders.  Wave w moves content-key rows 8 w .. 8 w + 7 (two DMAs of
+  // 4 rows x 256 B), rotary-key rows 8 w .. 8 w + 7 (one DMA of 8 rows x
+  // 128 B) and value rows 8 w .. 8 w + 7 (two DMAs).  LDS chunk swizzles:
+  // 256-byte rows XOR the 16-byte chunk with (row & 15), 128-byte rows with
+  // ((row >> 1) & 7).
+  const int KSTR = (int)(HS * 512);  // bytes between consecutive keys in kv
+  int kc_vo[2], v_vo[2], kr_vo;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 4 * (2 * w + i) + (lane >> 4);
+    const int c = (lane & 15) ^ (row & 15);
+    kc_vo[i] = row * KSTR + 16 * c;
+    v_vo[i] = row * KSTR + 256 + 16 * c;
+  }
+  {
+    const int row = 8 * w + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    kr_vo = row * 128 + 16 * c;
+  }
+  const u32x4 rkv = pp_rsrc(p.kv + (rowbase * HS + h) * 256, (long)p.T * KSTR);
+  const u32x4 rkr = pp_rsrc(p.kr + rowbase * 64, (long)p.T * 128);
+#define PP_ISSUE(tt)                                                                         \
+  do {                                                                                       \
+    const unsigned sb_ = lds_base + ((tt) % PP_NST) * PP_STG;                                \
+    const int kk_ = 64 * (tt);                                                               \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                            \
+      pp_dma16(sb_ + 1024 * (2 * w + i), kc_vo[i] + kk_ * KSTR, rkv);                        \
+    pp_dma16(sb_ + PP_KC + 1024 * w, kr_vo + kk_ * 128, rkr);                                \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                            \
+      pp_dma16(sb_ + PP_KC + PP_KR + 1024 * (2 * w + i), v_vo[i] + kk_ * KSTR, rkv);         \
+  } while (0)
+
+  // ---- fragment offsets inside a stage (tile-invariant).
+  // K fragment (s, mb): key row 32 mb + lr.  s < 8: content chunk 2 s + lg;
+  // s >= 8: rotary chunk 2 (s - 8) + lg.  (row & 15) = (lr & 15) and
+  // ((row >> 1) & 7) = ((lr >> 1) & 7) for both mb.
+  int kc_off[8], kr_off[4];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kc_off[s] = lr * 256 + 16 * ((2 * s + lg) ^ (lr & 15));
+#pragma unroll
+  for (int s = 0; s < 4; ++s) kr_off[s] = PP_KC + lr * 128 + 16 * ((2 * s + lg) ^ ((lr >> 1) & 7));
+  // V^T fragment (k-step ks = 2 mb + ih, feature block d), read r = 0, 1:
+  // in 16-lane group G, lane s16 addresses key row 32 mb + 16 ih + 8 r +
+  // 4 (G >> 1) + (s16 >> 2) and features 32 d + 16 (G & 1) + 4 (s16 & 3).
+  // Row & 15 drops the 32 mb + 16 ih part, so the offset is tile-invariant
+  // per (d, r) up to the immediate (32 mb + 16 ih) * 256.
+  int v_off[4][2];
+  {
+    const int G = lane >> 4, s16 = lane & 15;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = 8 * r + 4 * (G >> 1) + (s16 >> 2);
+        const int fb = 2 * (32 * d + 16 * (G & 1) + 4 * (s16 & 3));  // byte in row
+        v_off[d][r] = PP_KC + PP_KR + row * 256 + 16 * ((fb >> 4) ^ (row & 15)) + (fb & 15);
+      }
+  }
+
+  floatx16 O[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) O[d][e] = 0.f;
+  floatx16 S[2];
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = p.scale_log2;
+
+#define PP_QK(tt)                                                                            \
+  do {                                                                                       \
+    const char* sb_ = lds + ((tt) % PP_NST) * PP_STG;                                        \
+    _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                         \
+      _Pragma("unroll") for (int e = 0; e < 16; ++e) S[mb][e] = 0.f;                         \
+    constexpr int RQ = 6;                                                                    \
+    bf16x8 fk[RQ];                                                                           \
+    _Pragma("unroll") for (int u = 0; u < RQ; ++u) fk[u] = PP_KFRAG(sb_, u);                 \
+    _Pragma("unroll") for (int x = 0; x < 24; ++x) {                                         \
+      S[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[x % RQ], qf[x >> 1], S[x & 1], 0, 0, 0); \
+      if (x + RQ < 24) fk[x % RQ] = PP_KFRAG(sb_, x + RQ);                                   \
+    }                                                                                        \
+    __builtin_amdgcn_sched_group_barrier(0x100, RQ, 0);                                      \
+    _Pragma("unroll") for (int x = 0; x < 24; ++x) {                                         \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+      if (x + RQ < 24) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    \
+    }                                                                                        \
+  } while (0)
+  // fragment x = 2 s + mb
+#define PP_KFRAG(sb, x)                                                                      \
+  (*(const bf16x8*)((sb) + (((x) >> 1) < 8 ? kc_off[((x) >> 1) & 7] + 8192 * ((x) & 1)     \
+                                          : kr_off[((x) >> 1) & 3] + 4096 * ((x) & 1))))
+
+  // transposed V^T fragment y = 4 ks + d (ks = 2 mb + ih): two 4-key reads
+#define PP_VREAD(sb, y, dst)                                                                 \
+  do {                                                                                       \
+    const char* vb_ = (sb) + (32 * ((y) >> 3) + 16 * (((y) >> 2) & 1)) * 256;                \
+    (dst)[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                                      \
+        (__attribute__((address_space(3))) s16x4*)(vb_ + v_off[(y) & 3][0]));                \
+    (dst)[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                                      \
+        (__attribute__((address_space(3))) s16x4*)(vb_ + v_off[(y) & 3][1]));                \
+  } while (0)
+  // softmax of tile tt (scores in S) and O += V^T . P^T
+#define PP_SMPV(tt)                                                                          \
+  do {                                                                                       \
+    const int kv0_ = 64 * (tt);                                                              \
+    float tmax = -INFINITY;                                                                  \
+    if (kv0_ + 63 > wq_first) {                                                              \
+      _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                       \
+        _Pragma("unroll") for (int e = 0; e < 16; ++e) {                                     \
+          const int key = kv0_ + 32 * mb + 8 * (e >> 2) + 4 * lg + (e & 3);                  \
+          if (key > qi) S[mb][e] = -INFINITY;                                                \
+          tmax = fmaxf(tmax, S[mb][e]);                                                      \
+        }                                                                                    \
+    } else {                                                                                 \
+      _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                       \
+        _Pragma("unroll") for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, S[mb][e]);         \
+    }                                                                                        \
+    {                                                                                        \
+      const auto x32_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),              \
+                                                         __float_as_uint(tmax), false, false); \
+      tmax = fmaxf(__uint_as_float(x32_[0]), __uint_as_float(x32_[1])) * sl2;               \
+    }                                                                                        \
+    const bool raise_ = tmax > m_run + PP_LAZY;                                              \
+    const float m_new_ = raise_ ? tmax : m_run;                                              \
+    if (__any(raise_)) {                                                                     \
+      const float alpha_ = __builtin_amdgcn_exp2f(m_run - m_new_);                           \
+      l_run *= alpha_;                                                                       \
+      _Pragma("unroll") for (int d = 0; d < 4; ++d)                                          \
+        _Pragma("unroll") for (int e = 0; e < 16; ++e) O[d][e] *= alpha_;                    \
+    }                                                                                        \
+    m_run = m_new_;                                                                          \
+    float psum_ = 0.f;                                                                       \
+    _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                         \
+      _Pragma("unroll") for (int e = 0; e < 16; ++e) {                                       \
+        const float pv_ = __builtin_amdgcn_exp2f(fmaf(S[mb][e], sl2, -m_new_));              \
+        S[mb][e] = pv_;                                                                      \
+        psum_ += pv_;                                                                        \
+      }                                                                                      \
+    l_run += psum_;                                                                          \
+    const char* sb_ = lds + ((tt) % PP_NST) * PP_STG;                                        \
+    /* fragment y = 4 ks + d; a ring of 3 keeps the transposed reads 2 ahead */             \
+    s16x4 tv_[3][2];                                                                         \
+    _Pragma("unroll") for (int y = 0; y < 2; ++y) PP_VREAD(sb_, y, tv_[y]);                  \
+    bf16x8 pf_;                                                                              \
+    _Pragma("unroll") for (int y = 0; y < 16; ++y) {                                         \
+      const int ks = y >> 2, d = y & 3;                                                      \
+      if (d == 0) {                                                                          \
+        _Pragma("unroll") for (int m = 0; m < 8; ++m)                                        \
+          pf_[m] = (__bf16)S[ks >> 1][8 * (ks & 1) + m];                                     \
+      }                                                                                      \
+      if (y + 2 < 16) PP_VREAD(sb_, y + 2, tv_[(y + 2) % 3]);                                \
+      const s16x4 lo_ = tv_[y % 3][0], hi_ = tv_[y % 3][1];                                  \
+      const bf16x8 a_ = __builtin_bit_cast(                                                  \
+          bf16x8, s16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]});    \
+      O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, pf_, O[d], 0, 0, 0);                \
+    }                                                                                        \
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                       \
+    _Pragma("unroll") for (int y = 0; y < 16; ++y) {                                         \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+      if (y + 2 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                     \
+    }                                                                                        \
+  } while (0)
+
+  // Prologue: tile 0 landed (NST = 3 keeps one tile in flight per segment).
+  // Segment boundaries: the first half crosses one after PV(k), the second
+  // half after QK(k); both halves meet the same n_kv - 1 barriers.  At a
+  // boundary a wave first makes its own loads of the next tile land, then
+  // (after the barrier) issues its loads of the tile NST - 2 ahead into the
+  // buffer whose last reader (PV of the second half) finished before it.
+  for (int tt = 0; tt < PP_NST - 2 && tt < n_kv; ++tt) PP_ISSUE(tt);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (PP_NST - 2 < n_kv) PP_ISSUE(PP_NST - 2);
+  for (int k = 0; k < n_kv; ++k) {
+    // The fragment offsets are loop-invariant, and left alone the compiler
+    // hoists every (offset + immediate) sum out of the loop (over 50 live
+    // registers); marking them as redefined here keeps those sums inside the
+    // loop, where they fold into the reads' offset fields.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(kc_off[i]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(kr_off[i]));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) asm volatile("" : "+v"(v_off[d][0]), "+v"(v_off[d][1]));
+    const bool live = 64 * k <= wq_last;
+    const bool more = k + 1 < n_kv;
+    if (live) PP_QK(k);
+    if (second && more) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (k + PP_NST - 1 < n_kv) PP_ISSUE(k + PP_NST - 1);
+    }
+    if (live) PP_SMPV(k);
+    if (!second && more) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (k + PP_NST - 1 < n_kv) PP_ISSUE(k + PP_NST - 1);
+    }
+  }
+#undef PP_ISSUE
+#undef PP_QK
+#undef PP_KFRAG
+#undef PP_SMPV
+#undef PP_VREAD
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (qi < p.T) {
+    const float inv = 1.f / l_tot;
+    bf16_t* op = p.out + (rowbase + qi) * (HS * 128) + (long)h * 128 + 4 * lg;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 v;
+        v[0] = pack2bf(O[d][4 * i + 0] * inv, O[d][4 * i + 1] * inv);
+        v[1] = pack2bf(O[d][4 * i + 2] * inv, O[d][4 * i + 3] * inv);
+        *(u32x2*)(op + 32 * d + 8 * i) = v;
+      }
+  }
+}
+
+bool flash_pp_ok(const FlashParams& p) { return (long)(p.T + 64) * p.H * 512 < 0x7fffffffL; }
+
+hipError_t flash_prefill_pp_bf16(const FlashParams& p, hipStream_t s) {
+  if (!flash_pp_ok(p)) return hipErrorInvalidValue;
+  const int nqt = (p.T + PP_BQ - 1) / PP_BQ;
+  hipLaunchKernelGGL(flash_pp_kernel, dim3(nqt * p.H * p.B), dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -92,23 +92,37 @@ __global__ __launch_bounds__(512) void flash_prefill_kernel(FlashParams p) {
   const int n_kv = qlast / 64 + 1;
 
   // loaders: K tile = 64 rows x 24 chunks (3 per thread); V tile = 32 key
-  // pairs x 16 chunks (one pair per thread)
+  // pairs x 16 chunks (one pair per thread).  Source pointers are formed once
+  // for key offset 0 and advanced by the tile's first key; only the last tile
+  // (keys past T - 1) takes the clamped path.
+  const long krow_stride = HS * 256;  // elements between consecutive keys in kv
+  const bf16_t* kp0[3];
+  long kstep[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int e = tid + 512 * i, row = e / KCH, c = e % KCH;
+    kp0[i] = c < 16 ? p.kv + ((rowbase + row) * HS + h) * 256 + 8 * c : p.kr + (rowbase + row) * 64 + 8 * (c - 16);
+    kstep[i] = c < 16 ? krow_stride : 64;
+  }
+  const int vkp = tid & 31, vc = tid >> 5;
+  const bf16_t* vp0 = p.kv + ((rowbase + 2 * vkp) * HS + h) * 256 + 128 + 8 * vc;
   u32x4 rk[3], rv[2];
 #define FP_LOAD(kv0)                                                                      \
   do {                                                                                    \
-    _Pragma("unroll") for (int i = 0; i < 3; ++i) {                                       \
-      const int e = tid + 512 * i, row = e / KCH, c = e % KCH;                            \
-      const long key = rowbase + min((kv0) + row, p.T - 1);                               \
-      const bf16_t* src = c < 16 ? p.kv + (key * HS + h) * 256 + 8 * c                    \
-                                 : p.kr + key * 64 + 8 * (c - 16);                        \
-      rk[i] = *(const u32x4*)src;                                                         \
-    }                                                                                     \
-    {                                                                                     \
-      const int kp = tid & 31, c = tid >> 5;                                              \
-      const long k0 = rowbase + min((kv0) + 2 * kp, p.T - 1);                             \
-      const long k1 = rowbase + min((kv0) + 2 * kp + 1, p.T - 1);                         \
-      rv[0] = *(const u32x4*)(p.kv + (k0 * HS + h) * 256 + 128 + 8 * c);                  \
-      rv[1] = *(const u32x4*)(p.kv + (k1 * HS + h) * 256 + 128 + 8 * c);                  \
+    if ((kv0) + 64 <= p.T) {                                                              \
+      _Pragma("unroll") for (int i = 0; i < 3; ++i)                                       \
+        rk[i] = *(const u32x4*)(kp0[i] + (long)(kv0) * kstep[i]);                          \
+      rv[0] = *(const u32x4*)(vp0 + (long)(kv0) * krow_stride);                            \
+      rv[1] = *(const u32x4*)(vp0 + (long)((kv0) + 1) * krow_stride);                      \
+    } else {                                                                              \
+      _Pragma("unroll") for (int i = 0; i < 3; ++i) {                                     \
+        const int e = tid + 512 * i, row = e / KCH;                                       \
+        rk[i] = *(const u32x4*)(kp0[i] + (long)(min((kv0) + row, p.T - 1) - row) * kstep[i]); \
+      }                                                                                   \
+      const int k0_ = min((kv0) + 2 * vkp, p.T - 1) - 2 * vkp;                            \
+      const int k1_ = min((kv0) + 2 * vkp + 1, p.T - 1) - 2 * vkp;                        \
+      rv[0] = *(const u32x4*)(vp0 + (long)k0_ * krow_stride);                              \
+      rv[1] = *(const u32x4*)(vp0 + (long)k1_ * krow_stride);                              \
     }                                                                                     \
   } while (0)
 #define FP_STORE(buf)                                                                     \
@@ -118,10 +132,9 @@ __global__ __launch_bounds__(512) void flash_prefill_kernel(FlashParams p) {
       Ks[buf][row * KCH + kphys(c, row)] = rk[i];                                         \
     }                                                                                     \
     uint32_t* vt32 = (uint32_t*)&Vt[buf][0];                                              \
-    const int kp = tid & 31, c = tid >> 5;                                                \
-    const int pos = vpos(2 * kp);                                                         \
+    const int pos = vpos(2 * vkp);                                                        \
     _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                       \
-      const int dv = 8 * c + i;                                                           \
+      const int dv = 8 * vc + i;                                                          \
       const uint32_t w0 = rv[0][i >> 1], w1 = rv[1][i >> 1];                              \
       const uint32_t val = (i & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))                    \
                                    : ((w0 & 0xffffu) | (w1 << 16));                       \
@@ -140,6 +153,16 @@ __global__ __launch_bounds__(512) void flash_prefill_kernel(FlashParams p) {
   const int qi = q0 + 32 * w + lr;
   const int wq_first = q0 + 32 * w, wq_last = wq_first + 31;
 
+  // Fragment byte offsets inside a stage (tile-invariant).  K fragment
+  // (s, mb): row 32 mb + lr, chunk 2 s + lg at kphys(); the row's (row >> 1)
+  // & 7 equals (lr >> 1) & 7, so the position depends on s & 3 only.
+  int k_off[4], v_off[4];
+#pragma unroll
+  for (int s3 = 0; s3 < 4; ++s3) {
+    k_off[s3] = (lr * KCH + (((2 * s3 + lg) ^ (lr >> 1)) & 7)) * 16;
+    v_off[s3] = (lr * 8 + ((2 * s3 + lg) ^ vswz(lr))) * 16;  // V^T row dv = 32 d + lr, k-step s3
+  }
+
   FP_LOAD(0);
   FP_STORE(0);
   __syncthreads();
@@ -152,14 +175,24 @@ __global__ __launch_bounds__(512) void flash_prefill_kernel(FlashParams p) {
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) S[mb][e] = 0.f;
+      // 24 K fragments (x = 2 s + mb), read RQ ahead of their MFMA
+      const char* kb = (const char*)&Ks[cur][0];
+      constexpr int RQ = 8;
+#define FP_KFRAG(x) (*(const bf16x8*)(kb + k_off[((x) >> 1) & 3] + 32 * KCH * 16 * ((x) & 1) + 128 * ((x) >> 3)))
+      bf16x8 fk[RQ];
 #pragma unroll
-      for (int s = 0; s < 12; ++s) {
+      for (int u = 0; u < RQ; ++u) fk[u] = FP_KFRAG(u);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const int row = 32 * mb + lr;
-          const bf16x8 a = __builtin_bit_cast(bf16x8, Ks[cur][row * KCH + kphys(2 * s + lg, row)]);
-          S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], S[mb], 0, 0, 0);
-        }
+      for (int x = 0; x < 24; ++x) {
+        S[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[x % RQ], qf[x >> 1], S[x & 1], 0, 0, 0);
+        if (x + RQ < 24) fk[x % RQ] = FP_KFRAG(x + RQ);
+      }
+#undef FP_KFRAG
+      __builtin_amdgcn_sched_group_barrier(0x100, RQ, 0);
+#pragma unroll
+      for (int x = 0; x < 24; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (x + RQ < 24) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       // scores in log2 units: sl2 * S; masked keys (after the query) -> -inf
       const bool diag = kv0 + 63 > wq_first;
@@ -202,6 +235,11 @@ __global__ __launch_bounds__(512) void flash_prefill_kernel(FlashParams p) {
           psum += pv;
         }
       l_run += psum;
+      // 16 V^T fragments (y = 4 ks + d), all read ahead of the MFMAs
+      const char* vb = (const char*)&Vt[cur][0];
+      bf16x8 fv[16];
+#pragma unroll
+      for (int y = 0; y < 16; ++y) fv[y] = *(const bf16x8*)(vb + v_off[y >> 2] + 32 * 128 * (y & 3));
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -211,11 +249,7 @@ __global__ __launch_bounds__(512) void flash_prefill_kernel(FlashParams p) {
           for (int m = 0; m < 8; ++m) pf[m] = (__bf16)S[mb][8 * ih + m];
           const int ks = 2 * mb + ih;
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const int dv = 32 * d + lr;
-            const bf16x8 a = __builtin_bit_cast(bf16x8, Vt[cur][dv * 8 + ((2 * ks + lg) ^ vswz(dv))]);
-            O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, O[d], 0, 0, 0);
-          }
+          for (int d = 0; d < 4; ++d) O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[4 * ks + d], pf, O[d], 0, 0, 0);
         }
     }
     if (t + 1 < n_kv) FP_STORE(cur ^ 1);

@@ -147,6 +147,9 @@ struct FlashParams {
   float scale_log2;  // softmax scale * log2(e)
 };
 hipError_t flash_prefill_bf16(const FlashParams& p, hipStream_t s);
+// ping-pong form (flash_pp.hip); needs (T + 64) * H * 512 < 2^31
+bool flash_pp_ok(const FlashParams& p);
+hipError_t flash_prefill_pp_bf16(const FlashParams& p, hipStream_t s);
 
 // bf16 decode over the full per-head cache (one query per sequence).
 struct DecodeFullParams {

@@ -418,7 +418,8 @@ int prefill_core(const mla_dims* d, const mla_weights* w, const void* x, int B, 
     f.q = (const bf16_t*)b.q; f.kv = (const bf16_t*)b.kv; f.kr = (const bf16_t*)b.kr;
     f.out = (bf16_t*)b.o; f.B = B; f.T = T; f.H = H; f.rcos = rc; f.rsin = rs;
     f.scale_log2 = d->softmax_scale * 1.4426950408889634f;
-    LAUNCH("flash_prefill", flash_prefill_bf16(f, st));
+    if (flash_pp_ok(f)) LAUNCH("flash_prefill", flash_prefill_pp_bf16(f, st));
+    else LAUNCH("flash_prefill", flash_prefill_bf16(f, st));
   } else {
     AttnGenericParams a;
     memset(&a, 0, sizeof a);
