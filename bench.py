@@ -27,6 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+WARM_S = 0.25                  # minimum untimed warm-up per workload, seconds
+CPU_SAMPLE_S = 10.0            # minimum CPU-baseline sample, seconds
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 
 KIMI = dict(d_model=7168, n_heads=64, q_lora_rank=1536, kv_lora_rank=512, qk_nope_dim=128,
@@ -98,11 +100,27 @@ def make_weights(torch, dev, k, seed):
     return d, w, g
 
 
+def warm(torch, fn, warmup, min_s=WARM_S):
+    """Untimed warm-up: `warmup` calls, continued until the GPU has run the
+    workload for at least `min_s` seconds.  The MI355X clocks settle about
+    20 ms into a sustained run (a prefill step measured 670 us in the first
+    batch and 543 us from the second batch on); a few-step warm-up would time
+    that ramp instead of the steady state."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < min_s:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def timed(torch, fn, steps, warmup, flush=None):
     """Warm up, then time `steps` calls with HIP events on the current stream
     (per-step events when a cache flush runs between steps)."""
-    for _ in range(warmup):
-        fn()
+    if warmup > 0:
+        warm(torch, fn, warmup)
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     if flush is None:
@@ -155,9 +173,7 @@ def bench_prefill(torch, mla, dev, steps, warmup, k=KIMI, B=1, T=2048):
     out = torch.empty_like(x)
     ws = torch.empty(mla.prefill_workspace_size(d, B, T), dtype=torch.uint8, device=dev)
     fn = lambda: mla.mla_prefill(d, w, x, rope, out=out, workspace=ws)  # noqa: E731
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm(torch, fn, warmup)
     ms, wall, kern, ms_ev = timed_profiled(torch, mla, fn, steps)
     flops = prefill_kernel_flops(B, T, k)
     for n, v in kern.items():
@@ -181,9 +197,7 @@ def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000)
     out = torch.empty_like(x)
     ws = torch.empty(mla.decode_workspace_size(d, B, L_cap), dtype=torch.uint8, device=dev)
     fn = lambda: mla.mla_decode_fullcache(d, w, x, P, kc, vc, rope, out=out, workspace=ws)  # noqa: E731
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm(torch, fn, warmup)
     ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush)
     L = P + 1
     cache_bytes = B * H * L * (192 + 128) * 2
@@ -208,9 +222,7 @@ def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=819
     out = torch.empty_like(x)
     ws = torch.empty(mla.decode_workspace_size(d, B, L_cap), dtype=torch.uint8, device=dev)
     fn = lambda: mla.mla_decode_latentcache(d, w, x, P, cc, rope, out=out, workspace=ws)  # noqa: E731
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm(torch, fn, warmup)
     ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush)
     L = P + 1
     cache_bytes = B * L * 576 * 2
@@ -237,9 +249,7 @@ def bench_block(torch, mla, dev, d, w, steps, warmup, B=1, T=4096):
     out = torch.empty_like(x)
     ws = torch.empty(mla.block_workspace_size(d, B, T), dtype=torch.uint8, device=dev)
     fn = lambda: mla.dense_block_fwd(d, w, blk, x, rope, out=out, workspace=ws)  # noqa: E731
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm(torch, fn, warmup)
     ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps)
     fl = prefill_kernel_flops(B, T)
     flops = sum(fl.values()) + 2.0 * B * T * D * F * 3
@@ -267,13 +277,17 @@ def cpu_baseline(k=KIMI, B=1, T=2048):
     dims = ref.KIMI_K2
     x, w = synth.prefill_inputs(dims, B, T, 1002, bf16=True)
     mw = ref.MLAWeights(**w)
+    n = 0
     t0 = time.perf_counter()
-    ref.mla_prefill(dims, mw, x, dtype=np.float32)
-    dt = time.perf_counter() - t0
+    while n == 0 or time.perf_counter() - t0 < CPU_SAMPLE_S:
+        ref.mla_prefill(dims, mw, x, dtype=np.float32)
+        n += 1
+    dt = (time.perf_counter() - t0) / n
     flops = sum(prefill_kernel_flops(B, T, k).values())
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"one whole step of the headline workload (B={B}, T={T}) by the NumPy oracle in float32"}
+            "seconds_per_step": dt, "steps": n,
+            "sample": f"{n} whole steps of the headline workload (B={B}, T={T}) by the NumPy oracle "
+                      f"in float32, repeated for at least {CPU_SAMPLE_S:.0f} s"}
 
 
 def main():
@@ -346,6 +360,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "mfma_frac_step": value / MFMA_BF16_PEAK_TFS,
         "roofline": roofline,
+        "ms_per_step_with_kernel_events": r["ms_with_kernel_events"],
         "kernels": kern,
     }
     if not args.no_secondary:
