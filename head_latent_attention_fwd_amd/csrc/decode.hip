@@ -24,6 +24,7 @@
 //                   MFMA product whose weight operand is transposed into LDS.
 #include "common.h"
 #include "kernels.h"
+#include "stream_sum.h"
 
 namespace mla {
 
@@ -46,13 +47,40 @@ __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullParams p) {
   __shared__ float sc[DF_CHUNK_MAX];
   __shared__ float ob[16][129];
   __shared__ float red[8];
+  __shared__ u32x4 qs[24];  // the query, summed from its partial blocks (fused form)
   const int tid = threadIdx.x;
   const int split = blockIdx.x, bh = blockIdx.y;
   const int j0 = split * p.chunk;
   const int j1 = min(p.L, j0 + p.chunk);
   const int n = j1 - j0;
-  const bf16_t* K = p.k_cache + (long)bh * p.L_cap * 192;
-  const bf16_t* V = p.v_cache + (long)bh * p.L_cap * 128;
+  bf16_t* Kw = p.k_cache + (long)bh * p.L_cap * 192;
+  bf16_t* Vw = p.v_cache + (long)bh * p.L_cap * 128;
+  const bf16_t* K = Kw;
+  const bf16_t* V = Vw;
+
+  if (p.qpart || (p.kvpart && j0 <= p.L - 1 && p.L - 1 < j1)) {
+    const int b = bh / p.H, h = bh - b * p.H;
+    if (p.qpart && tid < 48) {
+      // 4 query features per thread, rounded to bf16 as the stored query is
+      const floatx4 v = stream_sum4(p.qpart, p.qsi, b, h * 192 + 4 * tid);
+      ((u32x2*)qs)[tid] = u32x2{pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
+    }
+    if (p.kvpart && j0 <= p.L - 1 && p.L - 1 < j1) {
+      // the new token's key [K^C | k^R] and value go to slot L-1 of the caches
+      const long P = p.L - 1;
+      if (tid >= 64 && tid < 128) {
+        const int e = tid - 64;  // K^C features 4 e (e < 32), else V features 4 (e - 32)
+        const floatx4 v = stream_sum4(p.kvpart, p.kvsi, b, h * 256 + 4 * e);
+        const u32x2 o = {pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
+        if (e < 32) *(u32x2*)(Kw + P * 192 + 4 * e) = o;
+        else *(u32x2*)(Vw + P * 128 + 4 * (e - 32)) = o;
+      } else if (tid >= 128 && tid < 136) {
+        const int c = tid - 128;
+        *(u32x4*)(Kw + P * 192 + 128 + 8 * c) = *(const u32x4*)(p.kr + (long)b * 64 + 8 * c);
+      }
+    }
+    __syncthreads();  // slot L-1 written (workgroup scope) before the key loop reads it
+  }
 
   // phase 1: scores.  8 lanes per key; lane g8 holds query chunks g8, g8+8, g8+16
   const int g8 = tid & 7, grp = tid >> 3;
@@ -60,7 +88,7 @@ __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullParams p) {
   float qf[24];
 #pragma unroll
   for (int c = 0; c < 3; ++c) {
-    u32x4 v = *(const u32x4*)(qp + 64 * c + 8 * g8);
+    u32x4 v = p.qpart ? qs[8 * c + g8] : *(const u32x4*)(qp + 64 * c + 8 * g8);
     // chunk 2 holds rotary features 8*g8 .. +8: rotate by the token's position
     if (c == 2) v = rope8_bf16(v, p.rcos, p.rsin, p.L - 1, 32, 4 * g8);
 #pragma unroll
@@ -268,16 +296,11 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
   const int head = 16 * w + l16;
   const int ntiles = j1 > j0 ? (j1 - j0 + LT - 1) / LT : 0;
 
+  // [q~ | roped q^R] of this head, laid out like a cache row
   bf16x8 qf[18];
 #pragma unroll
-  for (int s = 0; s < 18; ++s) {
-    const int f = 32 * s + 8 * g4;
-    const bf16_t* src = f < 512 ? p.q_abs + ((long)b * p.H + head) * 512 + f
-                                : p.q + ((long)b * p.H + head) * 192 + 128 + (f - 512);
-    u32x4 v = *(const u32x4*)src;
-    if (f >= 512) v = rope8_bf16(v, p.rcos, p.rsin, p.L - 1, 32, (f - 512) / 2);
-    qf[s] = __builtin_bit_cast(bf16x8, v);
-  }
+  for (int s = 0; s < 18; ++s)
+    qf[s] = *(const bf16x8*)(p.q_abs + ((long)b * p.H + head) * 576 + 32 * s + 8 * g4);
   const char* cb = (const char*)(p.cache + ((long)b * p.L_cap + j0) * 576);
 
   // DMA k of this wave fills LDS bytes [1024 (w * DMA_PER_WAVE + k), +1024) of
@@ -476,27 +499,100 @@ hipError_t decode_latent_bf16(const DecodeLatentParams& p, hipStream_t s) {
 
 // ------------------------------------------------------------------------
 // query absorption: q~[b,h,k] = sum_c q[b,h,c] * W_UK,h[c,k], c < 128, k < 512
-// (the key rows of head h in kv_b_proj, rows h*256 + c).  Workgroup = (h,
-// 64 latent features, 64 sequences); W_UK,h tile [128 c][64 k] is stored
-// transposed in LDS so that the MFMA B operand is c-contiguous.
+// (the key rows of head h in kv_b_proj, rows h*256 + c), written with the
+// roped rotary query into qa[b][h][576] = [q~ (512) | RoPE(q^R, L-1) (64)], the
+// same layout as a latent-cache row.  Workgroup = (h, 256 latent features,
+// 64 sequences); the W_UK,h tile [128 c][256 k] is stored transposed in LDS
+// so that the MFMA B operand is c-contiguous.  The query comes either as
+// bf16 q [B][H][192] or as the q up-projection's weight-stream partial blocks
+// (summed here in workgroup order).
 // ------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void absorb_q_kernel(const bf16_t* __restrict__ q,
-                                                       const bf16_t* __restrict__ w_ukv,
-                                                       bf16_t* __restrict__ q_abs, int B, int H) {
-  __shared__ u32x4 Wt[64 * 16];    // [k 64][c 128] -> 16 chunks per row, swizzled
+namespace {
+constexpr int AB_N = 64;  // latent features per workgroup
+}
+
+// 8 consecutive query features f .. f+7 of head h for R rows b[r] (rows with
+// ok[r] false give zeros), as packed bf16
+template <int R>
+MLA_DEV void absorb_q8(const AbsorbParams& p, int h, const int (&b)[R], const bool (&ok)[R], int f,
+                       u32x4 (&o)[R]) {
+  if (!p.qpart) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      o[r] = ok[r] ? *(const u32x4*)(p.q + ((long)b[r] * p.H + h) * 192 + f) : u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  floatx4 v[R][2];
+  stream_sum8_rows<R>(p.qpart, p.qsi, b, ok, h * 192 + f, v);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    o[r] = u32x4{pack2bf(v[r][0][0], v[r][0][1]), pack2bf(v[r][0][2], v[r][0][3]),
+                 pack2bf(v[r][1][0], v[r][1][1]), pack2bf(v[r][1][2], v[r][1][3])};
+}
+
+__global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
+  __shared__ u32x4 Wt[AB_N * 16];  // [k AB_N][c 128] -> 16 chunks per row, swizzled
   __shared__ u32x4 Qs[64 * 16];    // [b 64][c 128]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
-  const int h = blockIdx.x, n0 = blockIdx.y * 64, b0 = blockIdx.z * 64;
-  // W tile: 128 c x 64 k = 1024 chunks of 8 k; item = (c pair, k chunk): 64 x 8 = 512
+  const int h = blockIdx.x, n0 = blockIdx.y * AB_N, b0 = blockIdx.z * 64;
+  // W tile: 128 c x AB_N k; item = (c pair, k chunk of 8): 64 x AB_N / 8,
+  // all of a thread's loads in flight together
   uint32_t* wt32 = (uint32_t*)Wt;
+  constexpr int WIT = 64 * AB_N / 8 / 256;
+  u32x4 wa_[WIT], wb_[WIT];
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
+  for (int it = 0; it < WIT; ++it) {
     const int e = tid + 256 * it;
-    const int cp = e & 63, kc = e >> 6;  // c pair 0..63, k chunk 0..7
-    const bf16_t* src = w_ukv + ((long)h * 256 + 2 * cp) * 512 + n0 + 8 * kc;
-    const u32x4 a = *(const u32x4*)src;
-    const u32x4 bb = *(const u32x4*)(src + 512);
+    const int cp = e & 63, kc = e >> 6;
+    const bf16_t* src = p.w_ukv + ((long)h * 256 + 2 * cp) * 512 + n0 + 8 * kc;
+    wa_[it] = *(const u32x4*)src;
+    wb_[it] = *(const u32x4*)(src + 512);
+  }
+  // Q tile: 64 rows x 16 chunks of the content query (rows past B are zero);
+  // a thread's four rows share chunk c, so their partial loads go together
+  {
+    const int c = tid & 15;
+    int rb[4];
+    bool ok[4];
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rb[i] = b0 + (tid >> 4) + 16 * i;
+      ok[i] = rb[i] < p.B;
+    }
+    absorb_q8<4>(p, h, rb, ok, 8 * c, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 4) + 16 * i;
+      Qs[r * 16 + (c ^ (r & 7))] = v[i];
+    }
+  }
+  // rotary query of these rows, roped at position L-1 (64 rows x 8 chunks)
+  if (blockIdx.y == 0) {
+    const int c = tid & 7;
+    int rb[2];
+    bool ok[2];
+    u32x4 v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      rb[i] = b0 + (tid >> 3) + 32 * i;
+      ok[i] = rb[i] < p.B;
+    }
+    absorb_q8<2>(p, h, rb, ok, 128 + 8 * c, v);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (ok[i])
+        *(u32x4*)(p.qa + ((long)rb[i] * p.H + h) * 576 + 512 + 8 * c) =
+            rope8_bf16(v[i], p.rcos, p.rsin, p.L - 1, 32, 4 * c);
+  }
+  // transpose the W tile into LDS last: its loads, issued first, have landed
+  // by the time the query sums (issued after them) have
+#pragma unroll
+  for (int it = 0; it < WIT; ++it) {
+    const int e = tid + 256 * it;
+    const int cp = e & 63, kc = e >> 6;  // c pair 0..63, k chunk
+    const u32x4 a = wa_[it], bb = wb_[it];
 #pragma unroll
     for (int q2 = 0; q2 < 8; ++q2) {
       const int k = 8 * kc + q2;
@@ -507,39 +603,39 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const bf16_t* __restrict_
       wt32[(k * 128 + ph) >> 1] = val;
     }
   }
-  // Q tile: 64 rows x 16 chunks
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int e = tid + 256 * it;
-    const int r = e >> 4, c = e & 15;
-    const int bb = min(b0 + r, B - 1);
-    Qs[r * 16 + (c ^ (r & 7))] = *(const u32x4*)(q + ((long)bb * H + h) * 192 + 8 * c);
-  }
   __syncthreads();
-  // wave w: rows 32*(w>>1), cols 32*(w&1)
-  const int rm = 32 * (w >> 1), cn = 32 * (w & 1);
-  floatx16 acc;
+  // wave w: rows 32 (w >> 1), columns AB_N / 2 (w & 1) + 32 j
+  constexpr int NJ = AB_N / 64;
+  const int rm = 32 * (w >> 1), cn = (AB_N / 2) * (w & 1);
+  floatx16 acc[NJ];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const int ra = rm + lr, rbk = cn + lr;
+    const int ra = rm + lr;
     const bf16x8 a = __builtin_bit_cast(bf16x8, Qs[ra * 16 + ((2 * s + lg) ^ (ra & 7))]);
-    const bf16x8 bv = __builtin_bit_cast(bf16x8, Wt[rbk * 16 + (((2 * s + lg) ^ (rbk & 7)) & 15)]);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int rbk = cn + 32 * j + lr;
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, Wt[rbk * 16 + (((2 * s + lg) ^ (rbk & 7)) & 15)]);
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[j], 0, 0, 0);
+    }
   }
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int row = b0 + rm + 8 * (e >> 2) + 4 * lg + (e & 3);
-    const int col = n0 + cn + lr;
-    if (row < B) q_abs[((long)row * H + h) * 512 + col] = f2bf(acc[e]);
-  }
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = b0 + rm + 8 * (e >> 2) + 4 * lg + (e & 3);
+      const int col = n0 + cn + 32 * j + lr;
+      if (row < p.B) p.qa[((long)row * p.H + h) * 576 + col] = f2bf(acc[j][e]);
+    }
 }
 
-hipError_t absorb_q_bf16(const bf16_t* q, const bf16_t* w_ukv, bf16_t* q_abs, int B, int H,
-                         hipStream_t s) {
-  hipLaunchKernelGGL(absorb_q_kernel, dim3(H, 8, (B + 63) / 64), dim3(256), 0, s, q, w_ukv, q_abs,
-                     B, H);
+hipError_t absorb_q_bf16(const AbsorbParams& p, hipStream_t s) {
+  if (p.H <= 0 || p.B <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(absorb_q_kernel, dim3(p.H, 512 / AB_N, (p.B + 63) / 64), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

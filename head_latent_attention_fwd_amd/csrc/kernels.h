@@ -92,6 +92,9 @@ template <typename T> struct LatentNormParams {
   T* latent_cache; int L_cap;
   // optional full key cache [B][H][L_cap][dqk]: k^R copied to every head
   T* k_cache; int n_heads; int dqk; int d_nope;
+  // stream != 0: `part` holds the weight-streaming GEMM's partial blocks
+  // (StreamInfo si), summed here instead of the nsplit fp32 slices
+  int stream; StreamInfo si;
 };
 template <typename T> hipError_t latent_norm_rope(const LatentNormParams<T>& p, hipStream_t s);
 
@@ -154,8 +157,15 @@ hipError_t flash_prefill_pp_bf16(const FlashParams& p, hipStream_t s);
 // bf16 decode over the full per-head cache (one query per sequence).
 struct DecodeFullParams {
   const bf16_t* q;       // [B][H][192] (rope part rotated here, at position L-1)
-  const bf16_t* k_cache; // [B][H][L_cap][192]
-  const bf16_t* v_cache; // [B][H][L_cap][128]
+  bf16_t* k_cache;       // [B][H][L_cap][192]
+  bf16_t* v_cache;       // [B][H][L_cap][128]
+  // Optional fused inputs of a decode step (NULL: q is read from `q` and
+  // slot L-1 of the caches is already written): the q and kv up-projections
+  // as weight-stream partial blocks (summed here, in workgroup order) and the
+  // roped shared key kr [B][64].  The workgroup whose key range holds slot
+  // L-1 writes that slot of both caches before reading them.
+  const float* qpart; StreamInfo qsi;
+  const float* kvpart; StreamInfo kvsi; const bf16_t* kr;
   bf16_t* out;           // [B][H*128]
   float* part;           // split partials: [B*H][nsplit][128 + 2]
   const float* rcos; const float* rsin;  // RoPE table, row L-1 used
@@ -166,8 +176,7 @@ hipError_t decode_full_bf16(const DecodeFullParams& p, hipStream_t s);
 
 // bf16 absorbed decode over the latent cache.
 struct DecodeLatentParams {
-  const bf16_t* q_abs;   // [B][H][512]  absorbed query (W_UK folded in)
-  const bf16_t* q;       // [B][H][192]  (rope part at offset 128, rotated here)
+  const bf16_t* q_abs;   // [B][H][576]  [absorbed query q~ (W_UK folded in) | roped q^R]
   const bf16_t* cache;   // [B][L_cap][576]
   float* part;           // [B][nsplit][H][516]: m, l, pad, pad, o~[512]
   bf16_t* o_lat;         // [B][H][512]  merged latent output
@@ -178,8 +187,16 @@ struct DecodeLatentParams {
 hipError_t decode_latent_bf16(const DecodeLatentParams& p, hipStream_t s);
 
 // bf16 query absorption q~[b,h,:] = q_nope[b,h,:] . W_UK,h  (W_UK,h = rows
-// h*256 .. h*256+127 of kv_b_proj, each of 512 latent features)
-hipError_t absorb_q_bf16(const bf16_t* q, const bf16_t* w_ukv, bf16_t* q_abs, int B, int H,
-                         hipStream_t s);
+// h*256 .. h*256+127 of kv_b_proj, each of 512 latent features), written with
+// the rotary query roped at position L-1: qa[b][h] = [q~ (512) | q^R (64)].
+struct AbsorbParams {
+  const bf16_t* q;                    // [B][H][192], or NULL with qpart
+  const float* qpart; StreamInfo qsi; // q as weight-stream partial blocks
+  const bf16_t* w_ukv;                // [H*256][512]
+  bf16_t* qa;                         // [B][H][576]
+  const float* rcos; const float* rsin;
+  int B, H, L;
+};
+hipError_t absorb_q_bf16(const AbsorbParams& p, hipStream_t s);
 
 }  // namespace mla

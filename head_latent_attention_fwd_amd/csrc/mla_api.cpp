@@ -172,9 +172,10 @@ struct ProjBufs {
   void* q;      // [M][H*dqk]
   void* kv;     // [M][H*(dn+dv)]   (NULL when not needed)
   void* o;      // [M][H*dv]
-  void* upart;  // fp32 split-K partials of the small-M up-projections (or NULL)
+  void* upart;  // fp32 split-K partials of the small-M q up-projection (or NULL)
   size_t upart_floats;
-  void* cred;   // fp32 [M][N1]: the down-projection summed over its stream partials (decode)
+  void* ukvpart;  // ... and of the kv up-projection (its own buffer, so that both
+  size_t ukvpart_floats;  // can stay unsummed until the attention kernel reads them)
 };
 
 void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, ProjBufs* b) {
@@ -207,26 +208,24 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
   b->q = c.take((size_t)M * H * dqk * es);
   b->kv = need_kv ? c.take((size_t)M * H * (d->qk_nope_dim + d->v_head_dim) * es) : nullptr;
   b->o = c.take((size_t)M * H * d->v_head_dim * es);
-  b->upart = nullptr;
-  b->upart_floats = 0;
-  b->cred = b->decode ? c.take((size_t)M * N1 * 4) : nullptr;
+  b->upart = b->ukvpart = nullptr;
+  b->upart_floats = b->ukvpart_floats = 0;
   if (splitk && d->dtype == MLA_BF16) {
     // partials of the q and kv up-projections when M is small (decode)
-    size_t need = 0;
     const int shapes[2][2] = {{H * dqk, d->q_lora_rank},
                               {H * (d->qk_nope_dim + d->v_head_dim), d->kv_lora_rank}};
-    for (auto& sh : shapes) {
-      const int S = skinny_splits(sh[1]);
-      size_t n = (size_t)S * M * sh[0];
-      if (S > 1 && n > need) need = n;
+    for (int i = 0; i < 2; ++i) {
+      if (i == 1 && !need_kv) break;
+      const int S = skinny_splits(shapes[i][1]);
+      size_t need = S > 1 ? (size_t)S * M * shapes[i][0] : 0;
       if (M <= 64) {
-        const size_t sf = stream_part_floats(stream_info(M, sh[0], sh[1]));
+        const size_t sf = stream_part_floats(stream_info(M, shapes[i][0], shapes[i][1]));
         if (sf > need) need = sf;
       }
-    }
-    if (need) {
-      b->upart = c.take(need * 4);
-      b->upart_floats = need;
+      if (!need) continue;
+      void* buf = c.take(need * 4);
+      if (i == 0) { b->upart = buf; b->upart_floats = need; }
+      else { b->ukvpart = buf; b->ukvpart_floats = need; }
     }
   }
 }
@@ -266,13 +265,35 @@ int gemm_bf16_out(const char* name, GemmParams g, void* part, size_t part_floats
   return MLA_OK;
 }
 
+// Weight-streaming product whose partial blocks are left unsummed for the
+// consuming kernel; false (nothing launched) when the shape or the partial
+// buffer does not allow it.
+bool gemm_stream_deferred(const char* name, const GemmParams& g, void* part, size_t part_floats,
+                          hipStream_t st, StreamInfo* si, int* rc) {
+  si->G = 0;
+  *rc = MLA_OK;
+  if (!part || g.M > 64 || !stream_ok(g)) return false;
+  const StreamInfo s = stream_info(g.M, g.N, g.K);
+  if (stream_part_floats(s) > part_floats) return false;
+  *si = s;
+  *rc = [&]() -> int {
+    LAUNCH(name, gemm_stream_bf16(g, (float*)part, s, st));
+    return MLA_OK;
+  }();
+  return true;
+}
+
 // ---------------------------------------------------- shared launch steps
 // Down-projections, latent norms and RoPE, query up-projection (roped) and,
 // if kv is given, the kv up-projection.  Rows m = b*rowsT + t at position
-// t + pos0.
+// t + pos0.  With `defer` (decode), the q and kv up-projections may stay as
+// weight-stream partials (b.upart, b.ukvpart) for the attention kernels to
+// sum; defer[0] / defer[1] then hold their StreamInfo (G = 0: materialised
+// in b.q / b.kv as usual).
 int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int M, int rowsT,
                     int pos0, const float* rc, const float* rs, const ProjBufs& b,
-                    void* latent_cache, int L_cap, hipStream_t st) {
+                    void* latent_cache, int L_cap, hipStream_t st, StreamInfo* defer = nullptr) {
+  if (defer) defer[0].G = defer[1].G = 0;
   const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
   const int dqk = dn + dr, ql = d->q_lora_rank, kl = d->kv_lora_rank;
   const int N1 = ql + kl + dr, D = d->d_model;
@@ -285,13 +306,12 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
     g.M = M; g.N = N1; g.K = D;
     g.split_stride = (long)M * N1;
     bool streamed = false;
+    StreamInfo si{};
     if (b.decode && stream_ok(g)) {
-      // decode: balanced weight stream; its partials are summed by a wide
-      // reduction (one thread per 4 outputs) before the per-row norms
-      const StreamInfo si = stream_info(M, N1, D);
+      // decode: balanced weight stream; the latent-norm kernel sums its
+      // partial blocks
+      si = stream_info(M, N1, D);
       LAUNCH("gemm_down", gemm_stream_bf16(g, (float*)b.part, si, st));
-      LAUNCH("stream_reduce", stream_reduce<float>((const float*)b.part, si, M, N1, (float*)b.cred, N1,
-                                                   nullptr, 0, st));
       streamed = true;
     } else if (b.decode) {
       LAUNCH("gemm_down", gemm_skinny_bf16(g, false, st));  // decode: K-sliced weight stream
@@ -302,8 +322,9 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
     }
     LatentNormParams<bf16_t> n;
     memset(&n, 0, sizeof n);
-    n.part = (const float*)(streamed ? b.cred : b.part); n.nsplit = streamed ? 1 : b.S;
+    n.part = (const float*)b.part; n.nsplit = b.S;
     n.split_stride = (long)M * N1; n.ld_part = N1;
+    n.stream = streamed ? 1 : 0; n.si = si;
     n.M = M; n.q_lora = ql; n.kv_lora = kl; n.d_rope = dr;
     n.g_q = (const bf16_t*)w->g_q; n.g_kv = (const bf16_t*)w->g_kv; n.eps = d->rms_eps;
     n.cq = (bf16_t*)b.cq; n.ld_cq = ql; n.ckv = (bf16_t*)b.ckv; n.ld_ckv = kl;
@@ -318,7 +339,9 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
     q.M = M; q.N = H * dqk; q.K = ql;
     // the query's rotary part is rotated by the attention kernels as they
     // load it (each 16-byte fragment holds four whole RoPE pairs)
-    int r_ = gemm_bf16_out("gemm_q_up", q, b.upart, b.upart_floats, st);
+    int r_ = MLA_OK;
+    if (!(defer && gemm_stream_deferred("gemm_q_up", q, b.upart, b.upart_floats, st, &defer[0], &r_)))
+      r_ = gemm_bf16_out("gemm_q_up", q, b.upart, b.upart_floats, st);
     if (r_) return r_;
     if (b.kv) {
       GemmParams k = gp_base();
@@ -326,7 +349,8 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
       k.B = (const bf16_t*)w->w_ukv; k.ldb = kl;
       k.C = b.kv; k.ldc = (long)H * (dn + dv);
       k.M = M; k.N = H * (dn + dv); k.K = kl;
-      r_ = gemm_bf16_out("gemm_kv_up", k, b.upart, b.upart_floats, st);
+      if (!(defer && gemm_stream_deferred("gemm_kv_up", k, b.ukvpart, b.ukvpart_floats, st, &defer[1], &r_)))
+        r_ = gemm_bf16_out("gemm_kv_up", k, b.ukvpart, b.ukvpart_floats, st);
       if (r_) return r_;
     }
     return MLA_OK;
@@ -487,7 +511,7 @@ size_t decode_layout(const mla_dims* d, int B, int L_cap, int form, void* ws, De
   const int H = d->n_heads, kl = d->kv_lora_rank;
   const size_t es = esize(d);
   carve_proj(c, d, B, form == 0, true, &pl->pb);
-  pl->q_abs = c.take((size_t)B * H * kl * es);
+  pl->q_abs = c.take((size_t)B * H * (kl + d->qk_rope_dim) * es);  // bf16: [q~ | roped q^R]
   pl->o_lat = c.take((size_t)B * H * kl * es);
   // upper bounds of the split counts chosen for any live length L <= L_cap
   const int want_f = (512 + B * H - 1) / (B * H);
@@ -663,13 +687,23 @@ int mla_decode_fullcache(const mla_dims* d, const mla_weights* w, const void* x,
   hipStream_t st = (hipStream_t)stream;
   const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
   const ProjBufs& b = pl.pb;
-  if ((r = run_projections(d, w, x, B, 1, P, rc, rs, b, nullptr, L_cap, st))) return r;
+  StreamInfo def[2];
+  if ((r = run_projections(d, w, x, B, 1, P, rc, rs, b, nullptr, L_cap, st,
+                           d->dtype == MLA_BF16 ? def : nullptr)))
+    return r;
   if (d->dtype == MLA_BF16) {
-    LAUNCH("scatter_cache", scatter_full_cache<bf16_t>((const bf16_t*)b.kv, (const bf16_t*)b.kr, (bf16_t*)k_cache,
-                                      (bf16_t*)v_cache, B, 1, P, L_cap, H, dn, dr, dv, st));
+    // fused form: the attention kernel sums q and the new slot's k/v from the
+    // stream partials and writes slot P itself
+    const bool fused_kv = def[1].G > 0;
+    if (!fused_kv)
+      LAUNCH("scatter_cache", scatter_full_cache<bf16_t>((const bf16_t*)b.kv, (const bf16_t*)b.kr, (bf16_t*)k_cache,
+                                        (bf16_t*)v_cache, B, 1, P, L_cap, H, dn, dr, dv, st));
     DecodeFullParams a;
-    a.q = (const bf16_t*)b.q; a.k_cache = (const bf16_t*)k_cache;
-    a.v_cache = (const bf16_t*)v_cache; a.out = (bf16_t*)b.o; a.part = (float*)pl.apart;
+    a.q = (const bf16_t*)b.q; a.k_cache = (bf16_t*)k_cache;
+    a.v_cache = (bf16_t*)v_cache; a.out = (bf16_t*)b.o; a.part = (float*)pl.apart;
+    a.qpart = def[0].G > 0 ? (const float*)b.upart : nullptr; a.qsi = def[0];
+    a.kvpart = fused_kv ? (const float*)b.ukvpart : nullptr; a.kvsi = def[1];
+    a.kr = (const bf16_t*)b.kr;
     a.rcos = rc; a.rsin = rs;
     a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
     a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
@@ -714,11 +748,19 @@ int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* 
   const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
   const int kl = d->kv_lora_rank, dqk = dn + dr;
   const ProjBufs& b = pl.pb;
+  // q is summed by its own reduction here: spread over the absorption
+  // kernel's 512 workgroups, the partial sums measured slower than that
   if ((r = run_projections(d, w, x, B, 1, P, rc, rs, b, latent_cache, L_cap, st))) return r;
   if (d->dtype == MLA_BF16) {
-    LAUNCH("absorb_q", absorb_q_bf16((const bf16_t*)b.q, (const bf16_t*)w->w_ukv, (bf16_t*)pl.q_abs, B, H, st));
+    // [q~ | roped q^R] per head
+    AbsorbParams ab;
+    ab.q = (const bf16_t*)b.q;
+    ab.qpart = nullptr; ab.qsi = StreamInfo{};
+    ab.w_ukv = (const bf16_t*)w->w_ukv; ab.qa = (bf16_t*)pl.q_abs;
+    ab.rcos = rc; ab.rsin = rs; ab.B = B; ab.H = H; ab.L = P + 1;
+    LAUNCH("absorb_q", absorb_q_bf16(ab, st));
     DecodeLatentParams a;
-    a.q_abs = (const bf16_t*)pl.q_abs; a.q = (const bf16_t*)b.q;
+    a.q_abs = (const bf16_t*)pl.q_abs;
     a.cache = (const bf16_t*)latent_cache; a.part = (float*)pl.apart;
     a.o_lat = (bf16_t*)pl.o_lat;
     a.rcos = rc; a.rsin = rs;

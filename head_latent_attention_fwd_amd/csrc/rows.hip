@@ -17,6 +17,7 @@
 // (2i, 2i+1) by t * base^(-2i/d_rope).
 #include "common.h"
 #include "kernels.h"
+#include "stream_sum.h"
 
 namespace mla {
 
@@ -46,19 +47,46 @@ MLA_DEV floatx4 sum_splits4(const float* __restrict__ p, long stride, int nsplit
   return acc;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void latent_norm_rope_kernel(LatentNormParams<T> p) {
+template <int NT>
+MLA_DEV float block_sum(float v, float* red) {
+  v = warp_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) t += red[i];
+  return t;
+}
+
+// One workgroup of NT threads per row: sum the down-projection partials of
+// the row in a fixed order (deterministic) -- either nsplit fp32 K-slices or
+// the weight-streaming GEMM's partial blocks -- then the two RMSNorms and the
+// RoPE of the shared key, with the optional cache writes.
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T> p) {
   extern __shared__ float row[];  // [q_lora + kv_lora + d_rope]
-  __shared__ float red[4];
+  __shared__ float red[NT / 64];
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
   const int N1 = p.q_lora + p.kv_lora + p.d_rope;
   float sq = 0.f, skv = 0.f;
-  // sum the split-K partials of this row in a fixed order (deterministic);
   // 4 columns per thread and iteration, all splits' loads in flight together
   const bool vec = (N1 % 4 == 0) && (p.ld_part % 4 == 0) && (p.split_stride % 4 == 0);
-  if (vec) {
-    for (int c4 = tid; c4 < N1 / 4; c4 += 256) {
+  if (p.stream) {
+    for (int c4 = tid; c4 < N1 / 4; c4 += NT) {
+      const floatx4 v = stream_sum4(p.part, p.si, m, 4 * c4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 4 * c4 + q;
+        row[c] = v[q];
+        if (c < p.q_lora) sq += v[q] * v[q];
+        else if (c < p.q_lora + p.kv_lora) skv += v[q] * v[q];
+      }
+    }
+  } else if (vec) {
+    for (int c4 = tid; c4 < N1 / 4; c4 += NT) {
       const floatx4 v = sum_splits4(p.part + (long)m * p.ld_part + 4 * c4, p.split_stride, p.nsplit);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -69,7 +97,7 @@ __global__ __launch_bounds__(256) void latent_norm_rope_kernel(LatentNormParams<
       }
     }
   } else {
-    for (int c = tid; c < N1; c += 256) {
+    for (int c = tid; c < N1; c += NT) {
       float v = 0.f;
       for (int s = 0; s < p.nsplit; ++s)
         v += p.part[(long)s * p.split_stride + (long)m * p.ld_part + c];
@@ -78,8 +106,8 @@ __global__ __launch_bounds__(256) void latent_norm_rope_kernel(LatentNormParams<
       else if (c < p.q_lora + p.kv_lora) skv += v * v;
     }
   }
-  const float tq = block_sum256(sq, red);
-  const float tkv = block_sum256(skv, red);
+  const float tq = block_sum<NT>(sq, red);
+  const float tkv = block_sum<NT>(skv, red);
   const float rq = 1.0f / sqrtf(tq / (float)p.q_lora + p.eps);
   const float rkv = 1.0f / sqrtf(tkv / (float)p.kv_lora + p.eps);
 
@@ -90,16 +118,16 @@ __global__ __launch_bounds__(256) void latent_norm_rope_kernel(LatentNormParams<
                ? p.latent_cache + ((long)bseq * p.L_cap + pos) * (p.kv_lora + p.d_rope)
                : nullptr;
 
-  for (int c = tid; c < p.q_lora; c += 256)
+  for (int c = tid; c < p.q_lora; c += NT)
     p.cq[(long)m * p.ld_cq + c] = from_f<T>(to_f<T>(p.g_q[c]) * (row[c] * rq));
-  for (int c = tid; c < p.kv_lora; c += 256) {
+  for (int c = tid; c < p.kv_lora; c += NT) {
     T y = from_f<T>(to_f<T>(p.g_kv[c]) * (row[p.q_lora + c] * rkv));
     p.ckv[(long)m * p.ld_ckv + c] = y;
     if (lat) lat[c] = y;
   }
   const int npairs = p.d_rope / 2;
   const float* kp = row + p.q_lora + p.kv_lora;
-  for (int i = tid; i < npairs; i += 256) {
+  for (int i = tid; i < npairs; i += NT) {
     float cs = p.rcos[(long)pos * p.n_pairs + i], sn = p.rsin[(long)pos * p.n_pairs + i];
     float a = kp[2 * i], b = kp[2 * i + 1];
     T y0 = from_f<T>(a * cs - b * sn), y1 = from_f<T>(a * sn + b * cs);
@@ -122,7 +150,13 @@ __global__ __launch_bounds__(256) void latent_norm_rope_kernel(LatentNormParams<
 template <typename T>
 hipError_t latent_norm_rope(const LatentNormParams<T>& p, hipStream_t s) {
   size_t shm = (size_t)(p.q_lora + p.kv_lora + p.d_rope) * sizeof(float);
-  hipLaunchKernelGGL(latent_norm_rope_kernel<T>, dim3(p.M), dim3(256), shm, s, p);
+  if (p.stream && (p.q_lora + p.kv_lora + p.d_rope) % 4) return hipErrorInvalidValue;
+  // few rows (decode): a wide workgroup keeps the partial loads of a row in
+  // flight together
+  if (p.M <= 64)
+    hipLaunchKernelGGL((latent_norm_rope_kernel<T, 1024>), dim3(p.M), dim3(1024), shm, s, p);
+  else
+    hipLaunchKernelGGL((latent_norm_rope_kernel<T, 256>), dim3(p.M), dim3(256), shm, s, p);
   return hipGetLastError();
 }
 template hipError_t latent_norm_rope<float>(const LatentNormParams<float>&, hipStream_t);
@@ -147,9 +181,57 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T* __restrict__
     y[m * ldy + c] = from_f<T>(to_f<T>(g[c]) * (rowbuf[c] * r));
 }
 
+// bf16 rows of up to 8192 features: each thread keeps its (at most four)
+// 16-byte chunks of the row in registers between the sum of squares and the
+// scaled store, so the row is read once with coalesced 16-byte loads.
+constexpr int RMS_VEC_CH = 4;  // chunks of 8 per thread: D <= 256 * 8 * 4
+__global__ __launch_bounds__(256) void rmsnorm_rows_bf16_kernel(const bf16_t* __restrict__ x, long ldx,
+                                                                const bf16_t* __restrict__ g,
+                                                                bf16_t* __restrict__ y, long ldy, int D,
+                                                                float eps) {
+  __shared__ float red[4];
+  const long m = blockIdx.x;
+  const int nch = D / 8;
+  u32x4 v[RMS_VEC_CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < RMS_VEC_CH; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nch) {
+      v[i] = *(const u32x4*)(x + m * ldx + 8 * c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a = lo_bf(v[i][q]), b = hi_bf(v[i][q]);
+        ss += a * a + b * b;
+      }
+    }
+  }
+  const float r = 1.0f / sqrtf(block_sum256(ss, red) / (float)D + eps);
+#pragma unroll
+  for (int i = 0; i < RMS_VEC_CH; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nch) {
+      const u32x4 gv = *(const u32x4*)(g + 8 * c);
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = pack2bf(lo_bf(gv[q]) * (lo_bf(v[i][q]) * r), hi_bf(gv[q]) * (hi_bf(v[i][q]) * r));
+      *(u32x4*)(y + m * ldy + 8 * c) = o;
+    }
+  }
+}
+
 template <typename T>
 hipError_t rmsnorm_rows(const T* x, long ldx, const T* g, T* y, long ldy, int M, int D, float eps,
                         hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    const bool vec = D % 8 == 0 && D <= 256 * 8 * RMS_VEC_CH && ldx % 8 == 0 && ldy % 8 == 0 &&
+                     ((uintptr_t)x | (uintptr_t)g | (uintptr_t)y) % 16 == 0;
+    if (vec) {
+      hipLaunchKernelGGL(rmsnorm_rows_bf16_kernel, dim3(M), dim3(256), 0, s, x, ldx, g, y, ldy, D, eps);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL(rmsnorm_rows_kernel<T>, dim3(M), dim3(256), (size_t)D * sizeof(float), s, x,
                      ldx, g, y, ldy, D, eps);
   return hipGetLastError();

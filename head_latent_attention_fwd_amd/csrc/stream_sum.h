@@ -12,14 +12,20 @@ constexpr int SU_K = 128;  // k per unit
 // first unit of workgroup w: units are dealt out as equal contiguous runs
 MLA_DEV inline int su_start(const StreamInfo& s, int w) { return (int)(((long)w * s.U) / s.G); }
 
+// Workgroups [wa, wb] hold the units of 128-column block nb.
+MLA_DEV inline void su_span(const StreamInfo& s, int nb, int& wa, int& wb) {
+  const int ua = nb * s.KS, ub = ua + s.KS - 1;
+  wa = (int)(((long)(ua + 1) * s.G - 1) / s.U);  // workgroup holding unit ua
+  wb = (int)(((long)(ub + 1) * s.G - 1) / s.U);  // ... and unit ub
+}
+
 // Sum of C[m][n .. n+3] over the partial slots of n's 128-column block, in
 // workgroup order (deterministic).  Slot (w, j) is workgroup w's j-th block
 // ([Mp][128] fp32).  Loads are issued 8 slots at a time.
 MLA_DEV inline floatx4 stream_sum4(const float* __restrict__ part, const StreamInfo& s, int m, int n) {
   const int nb = n / SU_N, nl = n - nb * SU_N;
-  const int ua = nb * s.KS, ub = ua + s.KS - 1;
-  const int wa = (int)(((long)(ua + 1) * s.G - 1) / s.U);  // workgroup holding unit ua
-  const int wb = (int)(((long)(ub + 1) * s.G - 1) / s.U);  // ... and unit ub
+  int wa, wb;
+  su_span(s, nb, wa, wb);
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int w0 = wa; w0 <= wb; w0 += 8) {
     floatx4 v[8];
@@ -37,6 +43,42 @@ MLA_DEV inline floatx4 stream_sum4(const float* __restrict__ part, const StreamI
     for (int q = 0; q < 8; ++q) acc += v[q];
   }
   return acc;
+}
+
+// R rows m[r] (ok[r] false: skipped, result zero) of the 8 columns n .. n+7
+// (n % 8 == 0, so one 128-column block), summed over the block's partial
+// slots in workgroup order like stream_sum4; the loads of 4 slots x R rows
+// are issued together.
+template <int R>
+MLA_DEV inline void stream_sum8_rows(const float* __restrict__ part, const StreamInfo& s, const int (&m)[R],
+                                     const bool (&ok)[R], int n, floatx4 (&out)[R][2]) {
+  const int nb = n / SU_N, nl = n - nb * SU_N;
+  int wa, wb;
+  su_span(s, nb, wa, wb);
+#pragma unroll
+  for (int r = 0; r < R; ++r) out[r][0] = out[r][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int w0 = wa; w0 <= wb; w0 += 4) {
+    floatx4 v[4][R][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int w = w0 + q;
+      const int j = w <= wb && su_start(s, w) / s.KS != nb ? 1 : 0;
+      const float* base = part + (long)(2 * w + j) * s.Mp * SU_N + nl;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const bool go = w <= wb && ok[r];
+        v[q][r][0] = go ? *(const floatx4*)(base + (long)m[r] * SU_N) : floatx4{0.f, 0.f, 0.f, 0.f};
+        v[q][r][1] = go ? *(const floatx4*)(base + (long)m[r] * SU_N + 4) : floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        out[r][0] += v[q][r][0];
+        out[r][1] += v[q][r][1];
+      }
+  }
 }
 
 }  // namespace mla
