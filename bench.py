@@ -42,10 +42,13 @@ def prefill_kernel_flops(B, T, k=KIMI):
     H = k["n_heads"]
     dqk = k["qk_nope_dim"] + k["qk_rope_dim"]
     n1 = k["q_lora_rank"] + k["kv_lora_rank"] + k["qk_rope_dim"]
+    q_up = 2.0 * M * H * dqk * k["q_lora_rank"]
+    kv_up = 2.0 * M * H * (k["qk_nope_dim"] + k["v_head_dim"]) * k["kv_lora_rank"]
     return {
         "gemm_down": 2.0 * M * n1 * k["d_model"],
-        "gemm_q_up": 2.0 * M * H * dqk * k["q_lora_rank"],
-        "gemm_kv_up": 2.0 * M * H * (k["qk_nope_dim"] + k["v_head_dim"]) * k["kv_lora_rank"],
+        "gemm_q_up": q_up,
+        "gemm_kv_up": kv_up,
+        "gemm_qkv_up": q_up + kv_up,  # both up-projections in one launch
         "flash_prefill": 2.0 * H * B * (T * (T + 1) / 2) * (dqk + k["v_head_dim"]),
         "gemm_o_proj": 2.0 * M * k["d_model"] * H * k["v_head_dim"],
     }
@@ -180,7 +183,7 @@ def bench_prefill(torch, mla, dev, steps, warmup, k=KIMI, B=1, T=2048):
         if n in flops:
             v["gflop"] = flops[n] / 1e9
             v["tflops"] = flops[n] / (v["avg_ms"] * 1e-3) / 1e12
-    total = sum(flops.values())
+    total = sum(v for n, v in flops.items() if n != "gemm_qkv_up")
     return {"ms": ms, "ms_with_kernel_events": ms_ev, "wall_s": wall, "flops": total, "kernels": kern, "w": w, "d": d}
 
 
@@ -252,7 +255,7 @@ def bench_block(torch, mla, dev, d, w, steps, warmup, B=1, T=4096):
     warm(torch, fn, warmup)
     ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps)
     fl = prefill_kernel_flops(B, T)
-    flops = sum(fl.values()) + 2.0 * B * T * D * F * 3
+    flops = sum(v for n, v in fl.items() if n != "gemm_qkv_up") + 2.0 * B * T * D * F * 3
     fl["gemm_swiglu"] = 2.0 * B * T * D * F * 2
     fl["gemm_w2_resid"] = 2.0 * B * T * D * F
     for n, v in kern.items():
@@ -283,7 +286,7 @@ def cpu_baseline(k=KIMI, B=1, T=2048):
         ref.mla_prefill(dims, mw, x, dtype=np.float32)
         n += 1
     dt = (time.perf_counter() - t0) / n
-    flops = sum(prefill_kernel_flops(B, T, k).values())
+    flops = sum(v for n, v in prefill_kernel_flops(B, T, k).items() if n != "gemm_qkv_up")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds_per_step": dt, "steps": n,
             "sample": f"{n} whole steps of the headline workload (B={B}, T={T}) by the NumPy oracle "

@@ -69,8 +69,41 @@ MLA_DEV u32x4 gemm_rsrc(const void* base) {
   return r;
 }
 
+// One launch may carry two independent products (same tile shape and
+// epilogue, no batch or K split): workgroups [0, tiles0) of the logical order
+// compute product 0, the rest product 1.
+struct GemmGroup {
+  GemmParams p[2];
+  int n;               // 1 or 2 products
+  int tiles0, tiles1;  // tiles of each product
+};
+
+// Logical (product, tile) of workgroup b.  The dispatcher hands workgroup b
+// to XCD b % 8, in order; each XCD gets a contiguous range of each product's
+// tiles, product 0's first, so every XCD runs the same mix and the longer
+// product (placed first by the caller) starts first.
+MLA_DEV void gemm_tile_of(const GemmGroup& g, int b, int& prob, int& lt) {
+  if (g.n == 1) {
+    prob = 0;
+    lt = xcd_remap(b, g.tiles0);
+    return;
+  }
+  const int total = g.tiles0 + g.tiles1;
+  const int x = b % 8, slot = b / 8;
+  const int before = x * (total / 8) + min(x, total % 8);  // workgroups on XCDs < x
+  const int s0 = x * (g.tiles0 / 8) + min(x, g.tiles0 % 8);
+  const int n0 = g.tiles0 / 8 + (x < g.tiles0 % 8 ? 1 : 0);
+  if (slot < n0) {
+    prob = 0;
+    lt = s0 + slot;
+  } else {
+    prob = 1;
+    lt = (before - s0) + (slot - n0);
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, bool DMA>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmGroup gg) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -96,9 +129,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
   const int wid = tid >> 6;
   const int wm = wid / WN, wn = wid % WN;
 
-  // ---- tile coordinates (XCD-aware, grouped along M) ----
-  const int ntiles = p.tiles_m * p.tiles_n;
-  const int lin = xcd_remap(blockIdx.x, ntiles);
+  // ---- product and tile coordinates (XCD-aware, grouped along M) ----
+  int prob, lin;
+  gemm_tile_of(gg, blockIdx.x, prob, lin);
+  const GemmParams& p = gg.p[prob];
   constexpr int GM = 8;
   const int group = lin / (GM * p.tiles_n);
   const int first_m = group * GM;
@@ -481,35 +515,57 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-static hipError_t launch_cfg(GemmParams p, hipStream_t s) {
-  p.tiles_m = (p.M + BM - 1) / BM;
-  p.tiles_n = (p.N + BN - 1) / BN;  // SwiGLU: N counts both W1 and W3 columns
-  dim3 grid(p.tiles_m * p.tiles_n, p.batch * p.ksplit);
-  // direct-to-LDS pipeline: whole k stages, byte offsets within 2^31, B2
-  // rows starting on a 16-row boundary
+// direct-to-LDS pipeline: whole k stages, byte offsets within 2^31, B2 rows
+// starting on a 16-row boundary
+template <int BM, int EPI>
+static bool dma_ok(const GemmParams& p) {
   const long rowsA = p.M, rowsB = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
-  const bool dma = BM >= 128 && p.kchunk % GEMM_DMA_SK(BM) == 0 && p.K % GEMM_DMA_SK(BM) == 0 &&
-                   rowsA * p.lda * 2 < 0x7fffffffL && rowsB * p.ldb * 2 < 0x7fffffffL &&
-                   (p.b_split <= 0 || p.b_split % 16 == 0);
+  return BM >= 128 && p.kchunk % GEMM_DMA_SK(BM) == 0 && p.K % GEMM_DMA_SK(BM) == 0 &&
+         rowsA * p.lda * 2 < 0x7fffffffL && rowsB * p.ldb * 2 < 0x7fffffffL &&
+         (p.b_split <= 0 || p.b_split % 16 == 0);
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+static hipError_t launch_cfg(const GemmParams* ps, int n, hipStream_t s) {
+  GemmGroup g;
+  g.n = n;
+  bool dma = true;
+  for (int i = 0; i < n; ++i) {
+    g.p[i] = ps[i];
+    g.p[i].tiles_m = (ps[i].M + BM - 1) / BM;
+    g.p[i].tiles_n = (ps[i].N + BN - 1) / BN;  // SwiGLU: N counts both W1 and W3 columns
+    dma = dma && dma_ok<BM, EPI>(ps[i]);
+  }
+  if (n == 1) g.p[1] = g.p[0];
+  g.tiles0 = g.p[0].tiles_m * g.p[0].tiles_n;
+  g.tiles1 = n == 2 ? g.p[1].tiles_m * g.p[1].tiles_n : 0;
+  dim3 grid(g.tiles0 + g.tiles1, ps[0].batch * ps[0].ksplit);
   if constexpr (BM >= 128) {
     if (dma) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI, true>), grid, dim3(WM * WN * 64), 0, s, p);
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI, true>), grid, dim3(WM * WN * 64), 0, s, g);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI, false>), grid, dim3(WM * WN * 64), 0, s, p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI, false>), grid, dim3(WM * WN * 64), 0, s, g);
   return hipGetLastError();
+}
+template <int BM, int BN, int WM, int WN, int EPI>
+static hipError_t launch_cfg(GemmParams p, hipStream_t s) {
+  return launch_cfg<BM, BN, WM, WN, EPI>(&p, 1, s);
 }
 
 template <int EPI>
-static hipError_t launch_epi(GemmParams p, int cfg, hipStream_t s) {
+static hipError_t launch_epi(const GemmParams* ps, int n, int cfg, hipStream_t s) {
   switch (cfg) {
-    case GEMM_CFG_256x256: return launch_cfg<256, 256, 2, 4, EPI>(p, s);
-    case GEMM_CFG_128x128: return launch_cfg<128, 128, 2, 2, EPI>(p, s);
-    case GEMM_CFG_64x128: return launch_cfg<64, 128, 1, 2, EPI>(p, s);
+    case GEMM_CFG_256x256: return launch_cfg<256, 256, 2, 4, EPI>(ps, n, s);
+    case GEMM_CFG_128x128: return launch_cfg<128, 128, 2, 2, EPI>(ps, n, s);
+    case GEMM_CFG_64x128: return launch_cfg<64, 128, 1, 2, EPI>(ps, n, s);
     default: return hipErrorInvalidValue;
   }
+}
+template <int EPI>
+static hipError_t launch_epi(GemmParams p, int cfg, hipStream_t s) {
+  return launch_epi<EPI>(&p, 1, cfg, s);
 }
 
 // Tile config and split-K count by a wave-quantisation cost model: a launch
@@ -545,6 +601,26 @@ GemmPlan gemm_plan(int M, int N, int K, int batch, int max_split) {
 }
 
 int gemm_pick_cfg(int M, int N, int K, int batch) { return gemm_plan(M, N, K, batch, 1).cfg; }
+
+hipError_t gemm_bf16_pair(GemmParams a, GemmParams b, int epi, int cfg, hipStream_t s) {
+  GemmParams ps[2] = {a, b};
+  for (auto& p : ps) {
+    if (p.batch > 1 || p.ksplit > 1) return hipErrorInvalidValue;
+    p.batch = p.ksplit = 1;
+    if (p.kchunk <= 0) p.kchunk = p.K;
+  }
+  const int bm = cfg == GEMM_CFG_256x256 ? 256 : cfg == GEMM_CFG_128x128 ? 128 : 64;
+  const int bn = cfg == GEMM_CFG_256x256 ? 256 : 128;
+  // the per-XCD split of the two tile ranges needs at least 8 tiles of each
+  const long t0 = (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+  const long t1 = (long)((b.M + bm - 1) / bm) * ((b.N + bn - 1) / bn);
+  if (t0 < 8 || t1 < 8) return hipErrorInvalidValue;
+  switch (epi) {
+    case EPI_F32: return launch_epi<EPI_F32>(ps, 2, cfg, s);
+    case EPI_BF16: return launch_epi<EPI_BF16>(ps, 2, cfg, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s) {
   if (p.batch <= 0) p.batch = 1;

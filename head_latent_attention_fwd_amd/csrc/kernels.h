@@ -34,6 +34,10 @@ struct GemmPlan { int cfg, ksplit, kchunk; };
 GemmPlan gemm_plan(int M, int N, int K, int batch, int max_split);
 int gemm_pick_cfg(int M, int N, int K, int batch);
 hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s);
+// Two independent products in one launch (same epilogue and tile config,
+// no batch or K split, at least 8 tiles each); product a's tiles are
+// scheduled first on every XCD, so a should be the one with the longer K.
+hipError_t gemm_bf16_pair(GemmParams a, GemmParams b, int epi, int cfg, hipStream_t s);
 
 // Weight-streaming product for M <= 64 rows (decode): K is cut into 512-wide
 // slices; more than one slice writes fp32 partials [slices][M][ldc]

@@ -340,15 +340,31 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
     // the query's rotary part is rotated by the attention kernels as they
     // load it (each 16-byte fragment holds four whole RoPE pairs)
     int r_ = MLA_OK;
+    GemmParams k = gp_base();
+    k.A = (const bf16_t*)b.ckv; k.lda = kl;
+    k.B = (const bf16_t*)w->w_ukv; k.ldb = kl;
+    k.C = b.kv; k.ldc = (long)H * (dn + dv);
+    k.M = M; k.N = H * (dn + dv); k.K = kl;
+    if (b.kv && M > 64) {
+      // prefill: both up-projections in one launch when they take the same
+      // tile shape, the q tiles (longer K) scheduled first on every XCD, so
+      // the kv tiles fill the CUs the q product's last partial wave leaves idle
+      const int cfg = gemm_pick_cfg(M, q.N, q.K, 1);
+      if (cfg == gemm_pick_cfg(M, k.N, k.K, 1) && cfg == GEMM_CFG_256x256) {
+        hipError_t e;
+        {
+          ProfScope ps_("gemm_qkv_up", st);
+          e = gemm_bf16_pair(q, k, EPI_BF16, cfg, st);
+        }
+        if (e == hipSuccess) return MLA_OK;
+        if (e != hipErrorInvalidValue) return fail(MLA_ERR_HIP, "gemm_bf16_pair failed: %s", hipGetErrorString(e));
+        (void)hipGetLastError();
+      }
+    }
     if (!(defer && gemm_stream_deferred("gemm_q_up", q, b.upart, b.upart_floats, st, &defer[0], &r_)))
       r_ = gemm_bf16_out("gemm_q_up", q, b.upart, b.upart_floats, st);
     if (r_) return r_;
     if (b.kv) {
-      GemmParams k = gp_base();
-      k.A = (const bf16_t*)b.ckv; k.lda = kl;
-      k.B = (const bf16_t*)w->w_ukv; k.ldb = kl;
-      k.C = b.kv; k.ldc = (long)H * (dn + dv);
-      k.M = M; k.N = H * (dn + dv); k.K = kl;
       if (!(defer && gemm_stream_deferred("gemm_kv_up", k, b.ukvpart, b.ukvpart_floats, st, &defer[1], &r_)))
         r_ = gemm_bf16_out("gemm_kv_up", k, b.ukvpart, b.ukvpart_floats, st);
       if (r_) return r_;
