@@ -73,6 +73,23 @@ def test_prefill_kimi_full_size_sampled_rows():
     assert_close(from_dev(got)[:, rows], want, TOL_BF16, "kimi prefill T=2048 sampled rows")
 
 
+def test_prefill_kimi_ragged_T2000_sampled_rows():
+    """Kimi K2 widths at T=2000: 256-row tiles with a ragged last row tile in
+    every GEMM, the 256 x 224 output-projection tiles among them, and a
+    ragged last query tile in the attention kernel."""
+    od = ref.KIMI_K2
+    B, T = 1, 2000
+    log(f"[prefill kimi ragged] B={B} T={T} bf16")
+    x, w = synth.prefill_inputs(od, B, T, 1012, bf16=True)
+    rows = sorted(set([0, 255, 256, 1791, 1792, 1900, 1983, 1984, T - 2, T - 1] +
+                      list(np.random.default_rng(6).choice(T, 12, replace=False))))
+    want = ref.mla_prefill(od, oracle_weights(w), x.astype(np.float64), rows=rows)
+    d = dims_of(mla, od, "bf16")
+    got = mla.mla_prefill(d, weights_to_dev(w, "bf16", DEV), to_dev(x, "bf16", DEV), _rope(od, T))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got)[:, rows], want, TOL_BF16, "kimi prefill T=2000 sampled rows")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_prefill_writes_caches(dt):
     od = ref.TINY if dt == "f32" else KIMI_NARROW
@@ -342,6 +359,23 @@ def test_dense_block_kimi_sampled_rows():
                               to_dev(x, "bf16", DEV), _rope(od, T))
     torch.cuda.synchronize()
     assert_close(from_dev(got)[:, rows], want, TOL_BF16, "kimi block sampled rows")
+
+
+def test_dense_block_kimi_T2048_sampled_rows():
+    """Kimi K2 block at T=2048: the o_proj and W2 products take the 256 x 224
+    tile kernel with its residual epilogue."""
+    od = ref.KIMI_K2
+    B, T = 1, 2048
+    log(f"[block kimi T=2048] B={B} T={T} bf16")
+    x, w, blk = synth.block_inputs(od, B, T, 1015, bf16=True)
+    rows = [0, 1, 255, 256, 1000, 1791, 2046, T - 1]
+    bw = ref.BlockWeights(attn=oracle_weights(w), **{k: np.asarray(v, np.float64) for k, v in blk.items()})
+    want = ref.dense_block(od, bw, x.astype(np.float64), rows=rows)
+    d = dims_of(mla, od, "bf16")
+    got = mla.dense_block_fwd(d, weights_to_dev(w, "bf16", DEV), weights_to_dev(blk, "bf16", DEV),
+                              to_dev(x, "bf16", DEV), _rope(od, T))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got)[:, rows], want, TOL_BF16, "kimi block T=2048 sampled rows")
 
 
 def test_rope_table_matches_definition():
