@@ -9,9 +9,10 @@ whole step and, for the dominant kernel, against the bf16 MFMA peak.
 One step = one mla_prefill call (down-projections + norms + RoPE, up-
 projections, flash attention, o_proj) on inputs already resident in HBM.
 Secondary lines (same JSON object, key "secondary") time the full-cache
-decode (B=64, P=1000), the absorbed latent-cache decode (B=32, P=8192) and
-the dense block (B=1, T=4096) with the same weights, against the HBM or MFMA
-roofline.  The CPU baseline times the float32 oracle on the host cores.
+decode (B=64, P=1000), the absorbed latent-cache decode (B=32, P=8192), the
+same over a ragged batch (B=32, per-sequence positions uniform in
+[0, 8192]) and the dense block (B=1, T=4096) with the same weights, against
+the HBM or MFMA roofline.  The CPU baseline times the float32 oracle on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -238,6 +239,37 @@ def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=819
             "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None}
 
 
+def bench_decode_latent_ragged(torch, mla, dev, d, w, steps, warmup, flush, B=32, P_max=8192):
+    """Absorbed latent decode over a ragged batch: per-sequence positions drawn
+    uniformly from [0, P_max] (seeded), one decode step per call."""
+    k = KIMI
+    L_cap = P_max + 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(1006)
+    cc = torch.randn(B, L_cap, 576, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    x = torch.randn(B, k["d_model"], generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    import numpy as np
+    pos_host = np.random.default_rng(1006).integers(0, P_max + 1, size=B)
+    pos_host[0] = P_max
+    pos = torch.tensor(pos_host, dtype=torch.int32, device=dev)
+    rope = mla.mla_rope_table(L_cap, 64, 10000.0, dev)
+    out = torch.empty_like(x)
+    ws = torch.empty(mla.decode_workspace_size(d, B, L_cap), dtype=torch.uint8, device=dev)
+    fn = lambda: mla.mla_decode_latentcache_ragged(d, w, x, pos, P_max, cc, rope, out=out, workspace=ws)  # noqa: E731
+    warm(torch, fn, warmup)
+    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush)
+    keys = int(pos_host.sum()) + B
+    cache_bytes = keys * 576 * 2
+    nbytes = cache_bytes + mla_param_count() * 2 + B * 576 * 2 + 2 * B * k["d_model"] * 2
+    if "decode_latent" in kern:
+        kern["decode_latent"]["gbs"] = cache_bytes / (kern["decode_latent"]["avg_ms"] * 1e-3) / 1e9
+    return {"workload": f"MLA decode, absorbed latent cache, ragged batch, bf16, B={B}, positions uniform "
+                        f"in [0, {P_max}] (mean {pos_host.mean():.0f}, {keys} keys in all)",
+            "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev, "tokens_per_s": B / (ms * 1e-3),
+            "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None}
+
+
 def bench_block(torch, mla, dev, d, w, steps, warmup, B=1, T=4096):
     k = KIMI
     g = torch.Generator(device=dev)
@@ -300,7 +332,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode_full", "decode_latent", "block", "copy"])
+    ap.add_argument("--only", choices=["prefill", "decode_full", "decode_latent", "decode_latent_ragged",
+                                       "block", "copy"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -337,6 +370,8 @@ def main():
         d, w, _ = make_weights(torch, dev, KIMI, 1002)
         fn = {"decode_full": lambda: bench_decode_full(torch, mla, dev, d, w, args.steps, args.warmup, flush),
               "decode_latent": lambda: bench_decode_latent(torch, mla, dev, d, w, args.steps, args.warmup, flush),
+              "decode_latent_ragged": lambda: bench_decode_latent_ragged(torch, mla, dev, d, w, args.steps,
+                                                                         args.warmup, flush),
               "block": lambda: bench_block(torch, mla, dev, d, w, args.steps, args.warmup)}[args.only]
         print(json.dumps(fn()))
         return
@@ -370,6 +405,7 @@ def main():
         sec = {}
         for name, fn in (("decode_fullcache", lambda: bench_decode_full(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
                          ("decode_latentcache", lambda: bench_decode_latent(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
+                         ("decode_latentcache_ragged", lambda: bench_decode_latent_ragged(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
                          ("dense_block", lambda: bench_block(torch, mla, dev, r["d"], r["w"], max(3, args.steps // 4), 2))):
             log(f"[bench] {name}")
             try:

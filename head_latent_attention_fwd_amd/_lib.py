@@ -78,6 +78,10 @@ def load():
                                        _I, _P, _P, _SZ, _P]
     L.mla_decode_latentcache.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _I, _I, _P, _P, _P,
                                          _I, _P, _P, _SZ, _P]
+    L.mla_decode_fullcache_ragged.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _P, _I, _I, _P,
+                                              _P, _P, _P, _I, _P, _P, _SZ, _P]
+    L.mla_decode_latentcache_ragged.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _P, _I, _I,
+                                                _P, _P, _P, _I, _P, _P, _SZ, _P]
     L.dense_block_workspace_size.argtypes = [_DP, _I, _I]
     L.dense_block_workspace_size.restype = _SZ
     L.dense_block_fwd.argtypes = [_DP, ctypes.POINTER(BlockWeights), _P, _I, _I, _P, _P, _I, _P, _P,
@@ -91,7 +95,8 @@ def load():
     L.mla_last_error.argtypes = []
     L.mla_last_error.restype = ctypes.c_char_p
     for name in ("mla_rope_table", "mla_prefill", "mla_decode_fullcache",
-                 "mla_decode_latentcache", "dense_block_fwd"):
+                 "mla_decode_latentcache", "mla_decode_fullcache_ragged",
+                 "mla_decode_latentcache_ragged", "dense_block_fwd"):
         getattr(L, name).restype = _I
     _lib = L
     return L
@@ -276,6 +281,66 @@ def mla_decode_latentcache(d: Dims, w: dict, x, P, latent_cache, rope, out=None,
                                     B, int(P), L_cap, lc, rc, rs, rows,
                                     ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
                                     ws.numel(), _stream(dev)))
+    return out
+
+
+def _positions(positions, B, P_max, L_cap, dev):
+    """Device int32 [B] per-sequence positions and their host upper bound."""
+    pp = _tensor(positions, "positions", (B,), torch.int32, dev)
+    P_max = int(P_max)
+    if not 0 <= P_max < L_cap:
+        raise ValueError(f"P_max={P_max} outside [0, L_cap={L_cap})")
+    return pp, P_max
+
+
+def mla_decode_fullcache_ragged(d: Dims, w: dict, x, positions, P_max, k_cache, v_cache, rope,
+                                out=None, workspace=None):
+    """Decode over a ragged batch: sequence b's new token sits at
+    positions[b] (device int32 [B], each <= P_max); slot positions[b] of its
+    cache rows is overwritten and keys 0..positions[b] are attended.
+    x [B, d] -> out [B, d]."""
+    L = load()
+    dev = x.device
+    B = x.shape[0]
+    _tensor(x, "x", (B, d.d_model), d.torch_dtype, dev)
+    L_cap = k_cache.shape[2]
+    kc = _tensor(k_cache, "k_cache", (B, d.n_heads, L_cap, d.qk_nope_dim + d.qk_rope_dim), d.torch_dtype, dev)
+    vc = _tensor(v_cache, "v_cache", (B, d.n_heads, L_cap, d.v_head_dim), d.torch_dtype, dev)
+    pp, P_max = _positions(positions, B, P_max, L_cap, dev)
+    wt = _weights(d, w, dev)
+    rc, rs, rows = _rope(rope, P_max + 1, d, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _tensor(out, "out", x.shape, d.torch_dtype, dev)
+    ws = _ws(decode_workspace_size(d, B, L_cap), dev, workspace)
+    _check(L.mla_decode_fullcache_ragged(ctypes.byref(d), ctypes.byref(wt), ctypes.c_void_p(x.data_ptr()),
+                                         B, pp, P_max, L_cap, kc, vc, rc, rs, rows,
+                                         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                         ws.numel(), _stream(dev)))
+    return out
+
+
+def mla_decode_latentcache_ragged(d: Dims, w: dict, x, positions, P_max, latent_cache, rope,
+                                  out=None, workspace=None):
+    """Absorbed decode over the latent cache for a ragged batch (positions as
+    in mla_decode_fullcache_ragged).  x [B, d] -> out [B, d]."""
+    L = load()
+    dev = x.device
+    B = x.shape[0]
+    _tensor(x, "x", (B, d.d_model), d.torch_dtype, dev)
+    L_cap = latent_cache.shape[1]
+    lc = _tensor(latent_cache, "latent_cache", (B, L_cap, d.kv_lora_rank + d.qk_rope_dim), d.torch_dtype, dev)
+    pp, P_max = _positions(positions, B, P_max, L_cap, dev)
+    wt = _weights(d, w, dev)
+    rc, rs, rows = _rope(rope, P_max + 1, d, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _tensor(out, "out", x.shape, d.torch_dtype, dev)
+    ws = _ws(decode_workspace_size(d, B, L_cap), dev, workspace)
+    _check(L.mla_decode_latentcache_ragged(ctypes.byref(d), ctypes.byref(wt), ctypes.c_void_p(x.data_ptr()),
+                                           B, pp, P_max, L_cap, lc, rc, rs, rows,
+                                           ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                           ws.numel(), _stream(dev)))
     return out
 
 

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnGenericParams p) 
 #pragma unroll
   for (int k = 0; k < GEN_MAX; ++k) o[k] = 0.f;
   float m = -INFINITY, l = 0.f;
-  const int jmax = min(p.Tk - 1, i + p.causal_offset);
+  const int jmax = p.seq_pos ? min(p.Tk - 1, seq_position(p.seq_pos, b, 0, p.pos_max))
+                            : min(p.Tk - 1, i + p.causal_offset);
   for (int j = 0; j <= jmax; ++j) {
     const float* kn = p.k_nope + (long)b * p.kn_b + (long)j * p.kn_j + (long)h * p.kn_h;
     const float* kr = p.k_rope + (long)b * p.kr_b + (long)j * p.kr_j + (long)h * p.kr_h;

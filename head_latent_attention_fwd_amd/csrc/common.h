@@ -67,6 +67,13 @@ MLA_DEV int xcd_remap(int b, int nblocks) {
 
 #define MLA_LDS __attribute__((address_space(3)))
 
+// Position of sequence b in a decode step: the caller's per-sequence table
+// (device int32, each entry clamped into [0, pmax] so that no value can
+// address outside the cache) or, without a table, the uniform position.
+MLA_DEV int seq_position(const int* __restrict__ pos, int b, int uniform, int pmax) {
+  return pos ? min(max(pos[b], 0), pmax) : uniform;
+}
+
 // RoPE of 8 consecutive bf16 features (4 pairs (2i, 2i+1), pair index
 // pair0 + i) at table row `pos`: (a, b) -> (a cos - b sin, a sin + b cos),
 // computed in fp32 and rounded back to bf16.

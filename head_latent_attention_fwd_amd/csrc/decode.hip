@@ -50,33 +50,34 @@ __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullParams p) {
   __shared__ u32x4 qs[24];  // the query, summed from its partial blocks (fused form)
   const int tid = threadIdx.x;
   const int split = blockIdx.x, bh = blockIdx.y;
+  // live length of this sequence: keys 0 .. P, P its new token's position
+  const int P = seq_position(p.seq_pos, bh / p.H, p.L - 1, p.L - 1);
   const int j0 = split * p.chunk;
-  const int j1 = min(p.L, j0 + p.chunk);
-  const int n = j1 - j0;
+  const int j1 = min(P + 1, j0 + p.chunk);
+  const int n = j1 - j0;  // <= 0: a split past this sequence's keys (empty partial)
   bf16_t* Kw = p.k_cache + (long)bh * p.L_cap * 192;
   bf16_t* Vw = p.v_cache + (long)bh * p.L_cap * 128;
   const bf16_t* K = Kw;
   const bf16_t* V = Vw;
 
-  if (p.qpart || (p.kvpart && j0 <= p.L - 1 && p.L - 1 < j1)) {
+  if (p.qpart || (p.kvpart && j0 <= P && P < j1)) {
     const int b = bh / p.H, h = bh - b * p.H;
     if (p.qpart && tid < 48) {
       // 4 query features per thread, rounded to bf16 as the stored query is
       const floatx4 v = stream_sum4(p.qpart, p.qsi, b, h * 192 + 4 * tid);
       ((u32x2*)qs)[tid] = u32x2{pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
     }
-    if (p.kvpart && j0 <= p.L - 1 && p.L - 1 < j1) {
-      // the new token's key [K^C | k^R] and value go to slot L-1 of the caches
-      const long P = p.L - 1;
+    if (p.kvpart && j0 <= P && P < j1) {
+      // the new token's key [K^C | k^R] and value go to slot P of the caches
       if (tid >= 64 && tid < 128) {
         const int e = tid - 64;  // K^C features 4 e (e < 32), else V features 4 (e - 32)
         const floatx4 v = stream_sum4(p.kvpart, p.kvsi, b, h * 256 + 4 * e);
         const u32x2 o = {pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
-        if (e < 32) *(u32x2*)(Kw + P * 192 + 4 * e) = o;
-        else *(u32x2*)(Vw + P * 128 + 4 * (e - 32)) = o;
+        if (e < 32) *(u32x2*)(Kw + (long)P * 192 + 4 * e) = o;
+        else *(u32x2*)(Vw + (long)P * 128 + 4 * (e - 32)) = o;
       } else if (tid >= 128 && tid < 136) {
         const int c = tid - 128;
-        *(u32x4*)(Kw + P * 192 + 128 + 8 * c) = *(const u32x4*)(p.kr + (long)b * 64 + 8 * c);
+        *(u32x4*)(Kw + (long)P * 192 + 128 + 8 * c) = *(const u32x4*)(p.kr + (long)b * 64 + 8 * c);
       }
     }
     __syncthreads();  // slot L-1 written (workgroup scope) before the key loop reads it
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullParams p) {
   for (int c = 0; c < 3; ++c) {
     u32x4 v = p.qpart ? qs[8 * c + g8] : *(const u32x4*)(qp + 64 * c + 8 * g8);
     // chunk 2 holds rotary features 8*g8 .. +8: rotate by the token's position
-    if (c == 2) v = rope8_bf16(v, p.rcos, p.rsin, p.L - 1, 32, 4 * g8);
+    if (c == 2) v = rope8_bf16(v, p.rcos, p.rsin, P, 32, 4 * g8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       qf[8 * c + 2 * i] = lo_bf(v[i]);
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
   const int l16 = lane & 15, g4 = lane >> 4;
   const int split = blockIdx.x, b = blockIdx.y;
   const int j0 = split * p.chunk;
-  const int j1 = min(p.L, j0 + p.chunk);
+  const int j1 = min(seq_position(p.seq_pos, b, p.L - 1, p.L - 1) + 1, j0 + p.chunk);
   const int head = 16 * w + l16;
   const int ntiles = j1 > j0 ? (j1 - j0 + LT - 1) / LT : 0;
 
@@ -584,7 +585,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
     for (int i = 0; i < 2; ++i)
       if (ok[i])
         *(u32x4*)(p.qa + ((long)rb[i] * p.H + h) * 576 + 512 + 8 * c) =
-            rope8_bf16(v[i], p.rcos, p.rsin, p.L - 1, 32, 4 * c);
+            rope8_bf16(v[i], p.rcos, p.rsin, seq_position(p.seq_pos, rb[i], p.L - 1, p.L - 1), 32, 4 * c);
   }
   // transpose the W tile into LDS last: its loads, issued first, have landed
   // by the time the query sums (issued after them) have

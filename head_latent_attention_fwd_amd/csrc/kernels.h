@@ -99,6 +99,9 @@ template <typename T> struct LatentNormParams {
   // stream != 0: `part` holds the weight-streaming GEMM's partial blocks
   // (StreamInfo si), summed here instead of the nsplit fp32 slices
   int stream; StreamInfo si;
+  // optional per-sequence positions (decode, rope_T = 1): row m is at
+  // position seq_pos[m] clamped into [0, pos_max] instead of rope_pos0
+  const int* seq_pos; int pos_max;
 };
 template <typename T> hipError_t latent_norm_rope(const LatentNormParams<T>& p, hipStream_t s);
 
@@ -112,15 +115,17 @@ hipError_t rope_table(int n_pos, int n_pairs, double base, float* cos_out, float
 // fp32-path elementwise helpers
 hipError_t rope_inplace_f32(float* x, long ldx, int M, int ncols, int head_dim, int rope_start,
                             const float* rcos, const float* rsin, int n_pairs, int rope_T,
-                            int rope_pos0, hipStream_t s);
+                            int rope_pos0, hipStream_t s, const int* seq_pos = nullptr,
+                            int pos_max = 0);
 hipError_t swiglu_f32(const float* g, const float* u, float* h, long n, hipStream_t s);
 
 // Scatter the per-head keys/values of new tokens into the full cache.
-// kv [M][H][d_nope + d_v] (row m = b * T + t), kr [M][d_rope]; slot t + pos0.
+// kv [M][H][d_nope + d_v] (row m = b * T + t), kr [M][d_rope]; slot t + pos0,
+// or (decode, T = 1) slot seq_pos[b] clamped into [0, pos_max].
 template <typename T>
 hipError_t scatter_full_cache(const T* kv, const T* kr, T* k_cache, T* v_cache, int Bn, int T_,
                               int pos0, int L_cap, int H, int d_nope, int d_rope, int d_v,
-                              hipStream_t s);
+                              hipStream_t s, const int* seq_pos = nullptr, int pos_max = 0);
 
 // Sum fp32 split partials [nsplit][M][N] into T out [M][ldo].
 template <typename T>
@@ -139,6 +144,9 @@ struct AttnGenericParams {
   int B, Tq, Tk, H, d_nope, d_rope, d_v;
   int causal_offset;  // query i sees keys j <= i + causal_offset
   float scale;
+  // optional (decode, Tq = 1): sequence b sees keys j <= seq_pos[b] clamped
+  // into [0, pos_max]
+  const int* seq_pos; int pos_max;
 };
 hipError_t attn_generic_f32(const AttnGenericParams& p, hipStream_t s);
 
@@ -175,6 +183,9 @@ struct DecodeFullParams {
   const float* rcos; const float* rsin;  // RoPE table, row L-1 used
   int B, H, L, L_cap, nsplit, chunk;
   float scale_log2;
+  // optional per-sequence positions: sequence b's new token sits at
+  // seq_pos[b] (clamped into [0, L - 1]) and attends over that many + 1 keys
+  const int* seq_pos;
 };
 hipError_t decode_full_bf16(const DecodeFullParams& p, hipStream_t s);
 
@@ -187,6 +198,7 @@ struct DecodeLatentParams {
   const float* rcos; const float* rsin;  // RoPE table, row L-1 used
   int B, H, L, L_cap, nsplit, chunk;
   float scale_log2;
+  const int* seq_pos;  // optional per-sequence positions, as for DecodeFullParams
 };
 hipError_t decode_latent_bf16(const DecodeLatentParams& p, hipStream_t s);
 
@@ -200,6 +212,7 @@ struct AbsorbParams {
   bf16_t* qa;                         // [B][H][576]
   const float* rcos; const float* rsin;
   int B, H, L;
+  const int* seq_pos;                 // optional: row b roped at seq_pos[b] (clamped to [0, L-1])
 };
 hipError_t absorb_q_bf16(const AbsorbParams& p, hipStream_t s);
 

@@ -292,7 +292,8 @@ bool gemm_stream_deferred(const char* name, const GemmParams& g, void* part, siz
 // in b.q / b.kv as usual).
 int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int M, int rowsT,
                     int pos0, const float* rc, const float* rs, const ProjBufs& b,
-                    void* latent_cache, int L_cap, hipStream_t st, StreamInfo* defer = nullptr) {
+                    void* latent_cache, int L_cap, hipStream_t st, StreamInfo* defer = nullptr,
+                    const int* seq_pos = nullptr, int pos_max = 0) {
   if (defer) defer[0].G = defer[1].G = 0;
   const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
   const int dqk = dn + dr, ql = d->q_lora_rank, kl = d->kv_lora_rank;
@@ -325,6 +326,7 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
     n.part = (const float*)b.part; n.nsplit = b.S;
     n.split_stride = (long)M * N1; n.ld_part = N1;
     n.stream = streamed ? 1 : 0; n.si = si;
+    n.seq_pos = seq_pos; n.pos_max = pos_max;
     n.M = M; n.q_lora = ql; n.kv_lora = kl; n.d_rope = dr;
     n.g_q = (const bf16_t*)w->g_q; n.g_kv = (const bf16_t*)w->g_kv; n.eps = d->rms_eps;
     n.cq = (bf16_t*)b.cq; n.ld_cq = ql; n.ckv = (bf16_t*)b.ckv; n.ld_ckv = kl;
@@ -388,6 +390,7 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
   n.kr = (float*)b.kr; n.ld_kr = dr;
   n.rcos = rc; n.rsin = rs; n.n_pairs = dr / 2; n.rope_T = rowsT; n.rope_pos0 = pos0;
   n.latent_cache = (float*)latent_cache; n.L_cap = L_cap;
+  n.seq_pos = seq_pos; n.pos_max = pos_max;
   LAUNCH("latent_norm_rope", latent_norm_rope<float>(n, st));
   GemmF32Params q;
   memset(&q, 0, sizeof q);
@@ -396,7 +399,7 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
   q.b_is_nk = 1;
   LAUNCH("gemm_q_up", gemm_f32(q, st));
   LAUNCH("rope_q", rope_inplace_f32((float*)b.q, (long)H * dqk, M, H * dqk, dqk, dn, rc, rs, dr / 2, rowsT,
-                          pos0, st));
+                          pos0, st, seq_pos, pos_max));
   if (b.kv) {
     GemmF32Params k;
     memset(&k, 0, sizeof k);
@@ -685,10 +688,13 @@ size_t mla_decode_workspace_size(const mla_dims* d, int B, int L_cap) {
   return s0 > s1 ? s0 : s1;
 }
 
-int mla_decode_fullcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
-                         int L_cap, void* k_cache, void* v_cache, const float* rc, const float* rs,
-                         int rope_rows, void* out, void* ws, size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
+// Full-cache decode step.  P is the new tokens' position, or with seq_pos
+// (device, per sequence) an upper bound of the positions: the split plan,
+// the workspace and the argument checks use it.
+static int decode_full_impl(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
+                            const int* seq_pos, int L_cap, void* k_cache, void* v_cache,
+                            const float* rc, const float* rs, int rope_rows, void* out, void* ws,
+                            size_t ws_bytes, void* stream) {
   int r = check_decode_args(d, w, x, B, P, L_cap, rc, rs, rope_rows, out, ws);
   if (r) return r;
   if (!k_cache || !v_cache) return fail(MLA_ERR_NULL, "k_cache/v_cache is NULL");
@@ -705,7 +711,7 @@ int mla_decode_fullcache(const mla_dims* d, const mla_weights* w, const void* x,
   const ProjBufs& b = pl.pb;
   StreamInfo def[2];
   if ((r = run_projections(d, w, x, B, 1, P, rc, rs, b, nullptr, L_cap, st,
-                           d->dtype == MLA_BF16 ? def : nullptr)))
+                           d->dtype == MLA_BF16 ? def : nullptr, seq_pos, P)))
     return r;
   if (d->dtype == MLA_BF16) {
     // fused form: the attention kernel sums q and the new slot's k/v from the
@@ -713,7 +719,7 @@ int mla_decode_fullcache(const mla_dims* d, const mla_weights* w, const void* x,
     const bool fused_kv = def[1].G > 0;
     if (!fused_kv)
       LAUNCH("scatter_cache", scatter_full_cache<bf16_t>((const bf16_t*)b.kv, (const bf16_t*)b.kr, (bf16_t*)k_cache,
-                                        (bf16_t*)v_cache, B, 1, P, L_cap, H, dn, dr, dv, st));
+                                        (bf16_t*)v_cache, B, 1, P, L_cap, H, dn, dr, dv, st, seq_pos, P));
     DecodeFullParams a;
     a.q = (const bf16_t*)b.q; a.k_cache = (bf16_t*)k_cache;
     a.v_cache = (bf16_t*)v_cache; a.out = (bf16_t*)b.o; a.part = (float*)pl.apart;
@@ -723,10 +729,11 @@ int mla_decode_fullcache(const mla_dims* d, const mla_weights* w, const void* x,
     a.rcos = rc; a.rsin = rs;
     a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
     a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    a.seq_pos = seq_pos;
     LAUNCH("decode_full", decode_full_bf16(a, st));
   } else {
     LAUNCH("scatter_cache", scatter_full_cache<float>((const float*)b.kv, (const float*)b.kr, (float*)k_cache,
-                                     (float*)v_cache, B, 1, P, L_cap, H, dn, dr, dv, st));
+                                     (float*)v_cache, B, 1, P, L_cap, H, dn, dr, dv, st, seq_pos, P));
     const int dqk = dn + dr;
     AttnGenericParams a;
     memset(&a, 0, sizeof a);
@@ -739,15 +746,35 @@ int mla_decode_fullcache(const mla_dims* d, const mla_weights* w, const void* x,
     a.out = (float*)b.o; a.o_row = (long)H * dv; a.o_head = dv;
     a.B = B; a.Tq = 1; a.Tk = P + 1; a.H = H; a.d_nope = dn; a.d_rope = dr; a.d_v = dv;
     a.causal_offset = P; a.scale = d->softmax_scale;
+    a.seq_pos = seq_pos; a.pos_max = P;
     LAUNCH("attn_generic", attn_generic_f32(a, st));
   }
   return run_oproj(d, w->w_o, b.o, B, nullptr, out, pl.opart, pl.opart_floats, pl.S2, st);
 }
 
-int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
-                           int L_cap, void* latent_cache, const float* rc, const float* rs,
-                           int rope_rows, void* out, void* ws, size_t ws_bytes, void* stream) {
+int mla_decode_fullcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
+                         int L_cap, void* k_cache, void* v_cache, const float* rc, const float* rs,
+                         int rope_rows, void* out, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
+  return decode_full_impl(d, w, x, B, P, nullptr, L_cap, k_cache, v_cache, rc, rs, rope_rows, out,
+                          ws, ws_bytes, stream);
+}
+
+int mla_decode_fullcache_ragged(const mla_dims* d, const mla_weights* w, const void* x, int B,
+                                const int* positions, int P_max, int L_cap, void* k_cache,
+                                void* v_cache, const float* rc, const float* rs, int rope_rows,
+                                void* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!positions) return fail(MLA_ERR_NULL, "positions is NULL");
+  return decode_full_impl(d, w, x, B, P_max, positions, L_cap, k_cache, v_cache, rc, rs, rope_rows,
+                          out, ws, ws_bytes, stream);
+}
+
+// Latent-cache decode step; P and seq_pos as for decode_full_impl.
+static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
+                              const int* seq_pos, int L_cap, void* latent_cache, const float* rc,
+                              const float* rs, int rope_rows, void* out, void* ws, size_t ws_bytes,
+                              void* stream) {
   int r = check_decode_args(d, w, x, B, P, L_cap, rc, rs, rope_rows, out, ws);
   if (r) return r;
   if (!latent_cache) return fail(MLA_ERR_NULL, "latent_cache is NULL");
@@ -766,14 +793,15 @@ int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* 
   const ProjBufs& b = pl.pb;
   // q is summed by its own reduction here: spread over the absorption
   // kernel's 512 workgroups, the partial sums measured slower than that
-  if ((r = run_projections(d, w, x, B, 1, P, rc, rs, b, latent_cache, L_cap, st))) return r;
+  if ((r = run_projections(d, w, x, B, 1, P, rc, rs, b, latent_cache, L_cap, st, nullptr, seq_pos, P)))
+    return r;
   if (d->dtype == MLA_BF16) {
     // [q~ | roped q^R] per head
     AbsorbParams ab;
     ab.q = (const bf16_t*)b.q;
     ab.qpart = nullptr; ab.qsi = StreamInfo{};
     ab.w_ukv = (const bf16_t*)w->w_ukv; ab.qa = (bf16_t*)pl.q_abs;
-    ab.rcos = rc; ab.rsin = rs; ab.B = B; ab.H = H; ab.L = P + 1;
+    ab.rcos = rc; ab.rsin = rs; ab.B = B; ab.H = H; ab.L = P + 1; ab.seq_pos = seq_pos;
     LAUNCH("absorb_q", absorb_q_bf16(ab, st));
     DecodeLatentParams a;
     a.q_abs = (const bf16_t*)pl.q_abs;
@@ -782,6 +810,7 @@ int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* 
     a.rcos = rc; a.rsin = rs;
     a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
     a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    a.seq_pos = seq_pos;
     LAUNCH("decode_latent", decode_latent_bf16(a, st));
     // O_h = o~_h W_UV,h^T, batched over heads
     GemmParams g = gp_base();
@@ -816,6 +845,7 @@ int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* 
     a.out = (float*)pl.o_lat; a.o_row = (long)H * kl; a.o_head = kl;
     a.B = B; a.Tq = 1; a.Tk = P + 1; a.H = H; a.d_nope = kl; a.d_rope = dr; a.d_v = kl;
     a.causal_offset = P; a.scale = d->softmax_scale;
+    a.seq_pos = seq_pos; a.pos_max = P;
     LAUNCH("attn_generic", attn_generic_f32(a, st));
     // O_h = o~_h . W_UV,h^T
     GemmF32Params u;
@@ -828,6 +858,24 @@ int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* 
     LAUNCH("gemm_uv", gemm_f32(u, st));
   }
   return run_oproj(d, w->w_o, b.o, B, nullptr, out, pl.opart, pl.opart_floats, pl.S2, st);
+}
+
+int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
+                           int L_cap, void* latent_cache, const float* rc, const float* rs,
+                           int rope_rows, void* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  return decode_latent_impl(d, w, x, B, P, nullptr, L_cap, latent_cache, rc, rs, rope_rows, out, ws,
+                            ws_bytes, stream);
+}
+
+int mla_decode_latentcache_ragged(const mla_dims* d, const mla_weights* w, const void* x, int B,
+                                  const int* positions, int P_max, int L_cap, void* latent_cache,
+                                  const float* rc, const float* rs, int rope_rows, void* out,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!positions) return fail(MLA_ERR_NULL, "positions is NULL");
+  return decode_latent_impl(d, w, x, B, P_max, positions, L_cap, latent_cache, rc, rs, rope_rows,
+                            out, ws, ws_bytes, stream);
 }
 
 size_t dense_block_workspace_size(const mla_dims* d, int B, int T) {

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
   const float rkv = 1.0f / sqrtf(tkv / (float)p.kv_lora + p.eps);
 
   const int t = m % p.rope_T;
-  const int pos = t + p.rope_pos0;
+  const int pos = p.seq_pos ? seq_position(p.seq_pos, m, 0, p.pos_max) : t + p.rope_pos0;
   const int bseq = m / p.rope_T;
   T* lat = p.latent_cache
                ? p.latent_cache + ((long)bseq * p.L_cap + pos) * (p.kv_lora + p.d_rope)
@@ -264,14 +264,16 @@ hipError_t rope_table(int n_pos, int n_pairs, double base, float* cos_out, float
 // In-place RoPE of the rotary columns of each head (fp32 path).
 __global__ void rope_inplace_f32_kernel(float* x, long ldx, int M, int nheads, int head_dim,
                                         int rope_start, const float* rcos, const float* rsin,
-                                        int n_pairs, int rope_T, int rope_pos0) {
+                                        int n_pairs, int rope_T, int rope_pos0, const int* seq_pos,
+                                        int pos_max) {
   const int np = (head_dim - rope_start) / 2;
   long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= (long)M * nheads * np) return;
   int i = (int)(e % np);
   int h = (int)((e / np) % nheads);
   long m = e / ((long)np * nheads);
-  int pos = (int)(m % rope_T) + rope_pos0;
+  const int pos = seq_pos ? seq_position(seq_pos, (int)(m / rope_T), 0, pos_max)
+                          : (int)(m % rope_T) + rope_pos0;
   float* v = x + m * ldx + (long)h * head_dim + rope_start + 2 * i;
   float c = rcos[(long)pos * n_pairs + i], s = rsin[(long)pos * n_pairs + i];
   float a = v[0], b = v[1];
@@ -281,13 +283,13 @@ __global__ void rope_inplace_f32_kernel(float* x, long ldx, int M, int nheads, i
 
 hipError_t rope_inplace_f32(float* x, long ldx, int M, int ncols, int head_dim, int rope_start,
                             const float* rcos, const float* rsin, int n_pairs, int rope_T,
-                            int rope_pos0, hipStream_t s) {
+                            int rope_pos0, hipStream_t s, const int* seq_pos, int pos_max) {
   int nheads = ncols / head_dim;
   long n = (long)M * nheads * ((head_dim - rope_start) / 2);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(rope_inplace_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      x, ldx, M, nheads, head_dim, rope_start, rcos, rsin, n_pairs, rope_T,
-                     rope_pos0);
+                     rope_pos0, seq_pos, pos_max);
   return hipGetLastError();
 }
 
@@ -308,7 +310,8 @@ hipError_t swiglu_f32(const float* g, const float* u, float* h, long n, hipStrea
 template <typename T>
 __global__ void scatter_full_cache_kernel(const T* __restrict__ kv, const T* __restrict__ kr,
                                           T* __restrict__ kc, T* __restrict__ vc, int T_, int pos0,
-                                          int L_cap, int H, int dn, int dr, int dv, long total) {
+                                          int L_cap, int H, int dn, int dr, int dv, long total,
+                                          const int* __restrict__ seq_pos, int pos_max) {
   long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= total) return;
   const int W = dn + dr + dv;
@@ -316,7 +319,7 @@ __global__ void scatter_full_cache_kernel(const T* __restrict__ kv, const T* __r
   int h = (int)((e / W) % H);
   long m = e / ((long)W * H);
   long b = m / T_;
-  int slot = (int)(m % T_) + pos0;
+  const int slot = seq_pos ? seq_position(seq_pos, (int)b, 0, pos_max) : (int)(m % T_) + pos0;
   long base = ((b * H + h) * L_cap + slot);
   const T* src = kv + (m * H + h) * (dn + dv);
   if (c < dn) kc[base * (dn + dr) + c] = src[c];
@@ -327,17 +330,20 @@ __global__ void scatter_full_cache_kernel(const T* __restrict__ kv, const T* __r
 template <typename T>
 hipError_t scatter_full_cache(const T* kv, const T* kr, T* k_cache, T* v_cache, int Bn, int T_,
                               int pos0, int L_cap, int H, int d_nope, int d_rope, int d_v,
-                              hipStream_t s) {
+                              hipStream_t s, const int* seq_pos, int pos_max) {
   long total = (long)Bn * T_ * H * (d_nope + d_rope + d_v);
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(scatter_full_cache_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256),
-                     0, s, kv, kr, k_cache, v_cache, T_, pos0, L_cap, H, d_nope, d_rope, d_v, total);
+                     0, s, kv, kr, k_cache, v_cache, T_, pos0, L_cap, H, d_nope, d_rope, d_v, total,
+                     seq_pos, pos_max);
   return hipGetLastError();
 }
 template hipError_t scatter_full_cache<float>(const float*, const float*, float*, float*, int, int,
-                                              int, int, int, int, int, int, hipStream_t);
+                                              int, int, int, int, int, int, hipStream_t, const int*,
+                                              int);
 template hipError_t scatter_full_cache<bf16_t>(const bf16_t*, const bf16_t*, bf16_t*, bf16_t*, int,
-                                               int, int, int, int, int, int, int, hipStream_t);
+                                               int, int, int, int, int, int, int, hipStream_t,
+                                               const int*, int);
 
 template <typename T>
 __global__ void reduce_splits_kernel(const float* __restrict__ part, int nsplit, long stride, int M,

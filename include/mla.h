@@ -149,6 +149,32 @@ int mla_decode_latentcache(const mla_dims *dims, const mla_weights *w, const voi
                            const float *rope_sin, int rope_rows, void *out, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* ---- Decode over a ragged batch (both cache forms) ----
+ * As mla_decode_fullcache / mla_decode_latentcache, but sequence b's new
+ * token sits at its own position positions[b] ([MP]'s decode mode per
+ * sequence: it writes slot positions[b] and attends over the
+ * positions[b] + 1 keys 0 .. positions[b] of its own cache rows).
+ *   positions : DEVICE int32 [B], read by the kernels (it may be written by
+ *               earlier work on the same stream).  Each entry is clamped into
+ *               [0, P_max], so no value can address outside the cache; a
+ *               value outside that range gives the result of the clamped
+ *               position.
+ *   P_max     : host upper bound of the positions, 0 <= P_max < L_cap, used
+ *               for the argument checks (rope_rows > P_max), the workspace
+ *               and the split plan (mla_decode_workspace_size is unchanged).
+ * Ownership, asynchrony and errors as for the uniform forms; a NULL
+ * positions pointer returns MLA_ERR_NULL. */
+int mla_decode_fullcache_ragged(const mla_dims *dims, const mla_weights *w, const void *x, int B,
+                                const int *positions, int P_max, int L_cap, void *k_cache,
+                                void *v_cache, const float *rope_cos, const float *rope_sin,
+                                int rope_rows, void *out, void *workspace, size_t workspace_bytes,
+                                void *stream);
+int mla_decode_latentcache_ragged(const mla_dims *dims, const mla_weights *w, const void *x,
+                                  int B, const int *positions, int P_max, int L_cap,
+                                  void *latent_cache, const float *rope_cos, const float *rope_sin,
+                                  int rope_rows, void *out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* ---- Dense transformer block ([DB]) ----
  * out = x' + SwiGLU(RMSNorm(x'; g_ffn)), x' = x + MLA(RMSNorm(x; g_attn)),
  * SwiGLU(z) = (silu(z W1^T) * (z W3^T)) W2^T.  x, out [B, T, d]; causal

@@ -442,6 +442,35 @@ def mla_decode_latentcache(dims: MLADims, w: MLAWeights, x_new: np.ndarray, P: i
     return out, cc
 
 
+def mla_decode_fullcache_ragged(dims: MLADims, w: MLAWeights, x_new: np.ndarray, positions,
+                                k_cache: np.ndarray, v_cache: np.ndarray, dtype=np.float64):
+    """Decode over a ragged batch with the full cache: sequence b's new token
+    sits at its own position positions[b] ([MP]'s decode mode, applied to
+    each sequence on its own: the sequences of a batch share no state).
+    Returns (out [B, d], k_cache', v_cache')."""
+    outs, kcs, vcs = [], [], []
+    for b, P in enumerate(positions):
+        o, kc, vc = mla_decode_fullcache(dims, w, x_new[b:b + 1], int(P), k_cache[b:b + 1],
+                                         v_cache[b:b + 1], dtype)
+        outs.append(o)
+        kcs.append(kc)
+        vcs.append(vc)
+    return np.concatenate(outs), np.concatenate(kcs), np.concatenate(vcs)
+
+
+def mla_decode_latentcache_ragged(dims: MLADims, w: MLAWeights, x_new: np.ndarray, positions,
+                                  latent_cache: np.ndarray, dtype=np.float64):
+    """Absorbed latent-cache decode over a ragged batch, one sequence at a
+    time at its own position (as mla_decode_fullcache_ragged).
+    Returns (out [B, d], latent_cache')."""
+    outs, ccs = [], []
+    for b, P in enumerate(positions):
+        o, cc = mla_decode_latentcache(dims, w, x_new[b:b + 1], int(P), latent_cache[b:b + 1], dtype)
+        outs.append(o)
+        ccs.append(cc)
+    return np.concatenate(outs), np.concatenate(ccs)
+
+
 def dense_block(dims: MLADims, bw: BlockWeights, x: np.ndarray, rows=None,
                 dtype=np.float64):
     """Dense transformer block of [DB]: x_attn = RMSNorm(x); x' = x + MLA(x_attn);

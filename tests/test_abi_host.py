@@ -122,6 +122,30 @@ def test_bad_shapes_rejected():
     assert st == -2
 
 
+def test_ragged_decode_arguments_rejected():
+    """Per-sequence positions: a NULL table, P_max outside the cache and a
+    rope table not covering P_max are rejected before any HIP call."""
+    L = _lib()
+    d = tiny()
+    w = _w()
+    st = L.mla_decode_fullcache_ragged(ctypes.byref(d), ctypes.byref(w), FAKE, 2, None, 5, 16, FAKE,
+                                       FAKE, FAKE, FAKE, 64, FAKE, FAKE, 1 << 40, None)
+    assert st == -1 and "positions" in L.mla_last_error().decode()
+    st = L.mla_decode_latentcache_ragged(ctypes.byref(d), ctypes.byref(w), FAKE, 2, None, 5, 16, FAKE,
+                                         FAKE, FAKE, 64, FAKE, FAKE, 1 << 40, None)
+    assert st == -1
+    for P_max in (-1, 16):
+        st = L.mla_decode_fullcache_ragged(ctypes.byref(d), ctypes.byref(w), FAKE, 2, FAKE, P_max, 16,
+                                           FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, 1 << 40, None)
+        assert st == -2
+        st = L.mla_decode_latentcache_ragged(ctypes.byref(d), ctypes.byref(w), FAKE, 2, FAKE, P_max, 16,
+                                             FAKE, FAKE, FAKE, 64, FAKE, FAKE, 1 << 40, None)
+        assert st == -2
+    st = L.mla_decode_latentcache_ragged(ctypes.byref(d), ctypes.byref(w), FAKE, 2, FAKE, 10, 16, FAKE,
+                                         FAKE, FAKE, 10, FAKE, FAKE, 1 << 40, None)  # rope rows 10 <= P_max
+    assert st == -2
+
+
 def test_unsupported_rejected():
     L = _lib()
     d = kimi()

@@ -224,6 +224,97 @@ def test_decode_latentcache_kimi_full_size_sampled():
     assert_close(got, want, TOL_BF16, "decode latent B=32 P=8192 sampled")
 
 
+# ------------------------------------------------------------ ragged decode
+def _pos_dev(positions):
+    return torch.tensor(positions, dtype=torch.int32, device=DEV)
+
+
+@pytest.mark.parametrize("case", [
+    ("tiny_f32", ref.TINY, [0, 3, 20, 9], 24, "f32", 71),
+    ("kimi_narrow_bf16", KIMI_NARROW, [0, 1, 300, 127, 319], 320, "bf16", 72),
+    ("kimi_bf16_splits", ref.KIMI_K2, [0, 4999, 2500], 5001, "bf16", 73),
+])
+def test_decode_fullcache_ragged(case):
+    """Per-sequence positions with the full cache: each sequence against the
+    oracle's decode at its own position, the written slot of each, and the
+    cache rows past each position left untouched."""
+    name, od, pos, L_cap, dt, seed = case
+    B, P_max = len(pos), max(pos)
+    log(f"[decode full ragged {name}] positions={pos} L_cap={L_cap} dtype={dt}")
+    x, w, kc, vc = synth.decode_full_inputs(od, B, P_max, L_cap, seed, bf16=(dt == "bf16"))
+    d = dims_of(mla, od, dt)
+    kd, vd = bits_to_dev(kc, dt, DEV), bits_to_dev(vc, dt, DEV)
+    got = mla.mla_decode_fullcache_ragged(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), _pos_dev(pos),
+                                          P_max, kd, vd, _rope(od, P_max + 1))
+    torch.cuda.synchronize()
+    kf = synth.as_f32(kc, dt == "bf16").astype(np.float64)
+    vf = synth.as_f32(vc, dt == "bf16").astype(np.float64)
+    want, kc2, vc2 = ref.mla_decode_fullcache_ragged(od, oracle_weights(w), x.astype(np.float64), pos, kf, vf)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(from_dev(got), want, tol, name)
+    kdf, vdf = from_dev(kd), from_dev(vd)
+    for b, P in enumerate(pos):
+        assert_close(kdf[b, :, P], kc2[b, :, P], tol, f"{name} key slot {P}")
+        assert_close(vdf[b, :, P], vc2[b, :, P], tol, f"{name} value slot {P}")
+        if P + 1 < L_cap:
+            np.testing.assert_array_equal(kdf[b, :, P + 1:], kf[b, :, P + 1:].astype(np.float32))
+
+
+@pytest.mark.parametrize("case", [
+    ("tiny_f32", ref.TINY, [5, 0, 20], 24, "f32", 81),
+    ("kimi_narrow_bf16", KIMI_NARROW, [0, 700, 31, 32], 701, "bf16", 82),
+    ("kimi_bf16_splits", ref.KIMI_K2, [8192, 5, 4000], 8193, "bf16", 83),
+])
+def test_decode_latentcache_ragged(case):
+    name, od, pos, L_cap, dt, seed = case
+    B, P_max = len(pos), max(pos)
+    log(f"[decode latent ragged {name}] positions={pos} L_cap={L_cap} dtype={dt}")
+    x, w, cc = synth.decode_latent_inputs(od, B, P_max, L_cap, seed, bf16=(dt == "bf16"))
+    d = dims_of(mla, od, dt)
+    cd = bits_to_dev(cc, dt, DEV)
+    got = mla.mla_decode_latentcache_ragged(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), _pos_dev(pos),
+                                            P_max, cd, _rope(od, P_max + 1))
+    torch.cuda.synchronize()
+    cf = synth.as_f32(cc, dt == "bf16").astype(np.float64)
+    want, cc2 = ref.mla_decode_latentcache_ragged(od, oracle_weights(w), x.astype(np.float64), pos, cf)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(from_dev(got), want, tol, name)
+    cdf = from_dev(cd)
+    for b, P in enumerate(pos):
+        assert_close(cdf[b, P], cc2[b, P], tol, f"{name} latent slot {P}")
+
+
+@pytest.mark.parametrize("form", ["full", "latent"])
+def test_ragged_decode_uniform_and_clamped(form):
+    """Equal positions give the uniform entry point's result bit for bit;
+    positions outside [0, P_max] act as the clamped positions."""
+    od, B, P, L_cap, dt = KIMI_NARROW, 3, 40, 48, "bf16"
+    log(f"[decode ragged uniform/clamp {form}]")
+    d = dims_of(mla, od, dt)
+    if form == "full":
+        x, w, kc, vc = synth.decode_full_inputs(od, B, P, L_cap, 91, bf16=True)
+        wd = weights_to_dev(w, dt, DEV)
+        run_u = lambda: mla.mla_decode_fullcache(d, wd, to_dev(x, dt, DEV), P, bits_to_dev(kc, dt, DEV),
+                                                 bits_to_dev(vc, dt, DEV), _rope(od, P + 1))
+        run_r = lambda pos, pm: mla.mla_decode_fullcache_ragged(d, wd, to_dev(x, dt, DEV), _pos_dev(pos), pm,
+                                                                bits_to_dev(kc, dt, DEV), bits_to_dev(vc, dt, DEV),
+                                                                _rope(od, pm + 1))
+    else:
+        x, w, cc = synth.decode_latent_inputs(od, B, P, L_cap, 92, bf16=True)
+        wd = weights_to_dev(w, dt, DEV)
+        run_u = lambda: mla.mla_decode_latentcache(d, wd, to_dev(x, dt, DEV), P, bits_to_dev(cc, dt, DEV),
+                                                   _rope(od, P + 1))
+        run_r = lambda pos, pm: mla.mla_decode_latentcache_ragged(d, wd, to_dev(x, dt, DEV), _pos_dev(pos), pm,
+                                                                  bits_to_dev(cc, dt, DEV), _rope(od, pm + 1))
+    u = from_dev(run_u())
+    r = from_dev(run_r([P] * B, P))
+    np.testing.assert_array_equal(r, u)
+    c1 = from_dev(run_r([P + 7, -5, 3], P))
+    c2 = from_dev(run_r([P, 0, 3], P))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(c1, c2)
+
+
 def _spike_scale(od, w, x_b, P, cf_b, pos, floor_rows):
     """Power of two that lifts row `pos`'s score, for its best head, at least
     12 (natural-log units) above every score in `floor_rows`; oracle steps."""

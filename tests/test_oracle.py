@@ -368,6 +368,47 @@ def test_prefill_last_row_equals_decode():
     pin_prefill_last_row_equals_decode(MICRO_EQ, 16)
 
 
+def pin_ragged_decode(dims=MICRO, seed=21):
+    """Per-sequence positions: sequence b's result (output and cache rows) is
+    that of a prefill of its own T_b = P_b + 1 tokens -- last output row,
+    first T_b cache slots -- whatever the other sequences' lengths, in both
+    cache forms; with equal positions it is the uniform decode step."""
+    w = _weights(dims, seed)
+    Ts = [1, 4, 7]
+    L_cap = 8
+    B = len(Ts)
+    xs = [_x((1, T, dims.d_model), seed + 1 + i) for i, T in enumerate(Ts)]
+    K = np.full((B, dims.n_heads, L_cap, dims.q_head_dim), 1e3)
+    V = np.full((B, dims.n_heads, L_cap, dims.v_head_dim), -1e3)
+    C = np.full((B, L_cap, dims.kv_lora_rank + dims.qk_rope_dim), 7.0)
+    want, Kw, Vw, Cw = [], K.copy(), V.copy(), C.copy()
+    for b, (T, x) in enumerate(zip(Ts, xs)):
+        out, p = ref.mla_prefill(dims, _mw(w), x, return_intermediates=True)
+        Kb, Vb = ref.full_cache_entries(dims, p)
+        Cb = ref.latent_cache_entries(dims, p)
+        K[b, :, :T - 1], V[b, :, :T - 1], C[b, :T - 1] = Kb[0, :, :T - 1], Vb[0, :, :T - 1], Cb[0, :T - 1]
+        Kw[b, :, :T], Vw[b, :, :T], Cw[b, :T] = Kb[0], Vb[0], Cb[0]
+        want.append(out[0, -1])
+    x_new = np.stack([x[0, -1] for x in xs])
+    pos = [T - 1 for T in Ts]
+    of, kc, vc = ref.mla_decode_fullcache_ragged(dims, _mw(w), x_new, pos, K, V)
+    ol, cc = ref.mla_decode_latentcache_ragged(dims, _mw(w), x_new, pos, C)
+    _close(of, np.stack(want), 1e-11)
+    _close(ol, np.stack(want), 1e-11)
+    _close(kc, Kw, 1e-12)
+    _close(vc, Vw, 1e-12)
+    _close(cc, Cw, 1e-12)
+    # equal positions: the uniform step
+    of2, _, _ = ref.mla_decode_fullcache_ragged(dims, _mw(w), x_new, [5, 5, 5], K, V)
+    of3, _, _ = ref.mla_decode_fullcache(dims, _mw(w), x_new, 5, K, V)
+    _close(of2, of3, 1e-12)
+
+
+def test_ragged_decode():
+    pin_ragged_decode()
+    pin_ragged_decode(MICRO_EQ, 22)
+
+
 def pin_block_residual():
     """With o_proj and W2 zero the block is the identity on x (exactly)."""
     d = MICRO
@@ -399,7 +440,7 @@ def test_rows_subset_matches_full():
 ALL_PINS = [pin_parameter_counts, pin_cache_sizes, pin_rmsnorm, pin_rope, pin_silu,
             pin_softmax_and_mix, pin_causality, pin_brute_prefill, pin_brute_decode_full,
             pin_brute_decode_latent, pin_brute_block, pin_absorbed_equals_unabsorbed,
-            pin_prefill_last_row_equals_decode, pin_block_residual,
+            pin_prefill_last_row_equals_decode, pin_block_residual, pin_ragged_decode,
             lambda: pin_brute_prefill(MICRO_EQ), lambda: pin_brute_decode_latent(MICRO_EQ),
             lambda: pin_absorbed_equals_unabsorbed(MICRO, 15)]
 
