@@ -59,6 +59,8 @@ MLA_DEV void pp_dma16(unsigned m0, int voff, u32x4 rsrc) {
       : "s"(m0), "v"(voff), "s"(rsrc)
       : "memory", "m0");
 }
+// chunk swizzle of a value-tile row
+MLA_DEV int pp_vswz(int row) { return (row & 3) << 2; }
 MLA_DEV u32x4 pp_rsrc(const void* base, long bytes) {
   const unsigned long a = (unsigned long)base;
   u32x4 r;
@@ -108,16 +110,20 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
   // ---- loaders.  Wave w moves content-key rows 8 w .. 8 w + 7 (two DMAs of
   // 4 rows x 256 B), rotary-key rows 8 w .. 8 w + 7 (one DMA of 8 rows x
   // 128 B) and value rows 8 w .. 8 w + 7 (two DMAs).  LDS chunk swizzles:
-  // 256-byte rows XOR the 16-byte chunk with (row & 15), 128-byte rows with
-  // ((row >> 1) & 7).
+  // content-key rows (256 B) XOR the 16-byte chunk with (row & 15), so the
+  // 16 rows of a fragment read hit 16 chunk positions; rotary-key rows
+  // (128 B) with ((row >> 1) & 7); value rows (256 B) with 4 (row & 3): a
+  // transposed value read covers 4 consecutive rows x the same 4 logical
+  // chunks per half-wave, and row & 15 would put all four rows on the same 4
+  // chunk positions (a 4-way bank conflict), while 4 (row & 3) gives each
+  // row its own group of 4.
   const int KSTR = (int)(HS * 512);  // bytes between consecutive keys in kv
   int kc_vo[2], v_vo[2], kr_vo;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 4 * (2 * w + i) + (lane >> 4);
-    const int c = (lane & 15) ^ (row & 15);
-    kc_vo[i] = row * KSTR + 16 * c;
-    v_vo[i] = row * KSTR + 256 + 16 * c;
+    kc_vo[i] = row * KSTR + 16 * ((lane & 15) ^ (row & 15));
+    v_vo[i] = row * KSTR + 256 + 16 * ((lane & 15) ^ pp_vswz(row));
   }
   {
     const int row = 8 * w + (lane >> 3);
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
   // V^T fragment (k-step ks = 2 mb + ih, feature block d), read r = 0, 1:
   // in 16-lane group G, lane s16 addresses key row 32 mb + 16 ih + 8 r +
   // 4 (G >> 1) + (s16 >> 2) and features 32 d + 16 (G & 1) + 4 (s16 & 3).
-  // Row & 15 drops the 32 mb + 16 ih part, so the offset is tile-invariant
+  // The value swizzle depends on row & 3 only, so the offset is tile-invariant
   // per (d, r) up to the immediate (32 mb + 16 ih) * 256.
   int v_off[4][2];
   {
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
       for (int r = 0; r < 2; ++r) {
         const int row = 8 * r + 4 * (G >> 1) + (s16 >> 2);
         const int fb = 2 * (32 * d + 16 * (G & 1) + 4 * (s16 & 3));  // byte in row
-        v_off[d][r] = PP_KC + PP_KR + row * 256 + 16 * ((fb >> 4) ^ (row & 15)) + (fb & 15);
+        v_off[d][r] = PP_KC + PP_KR + row * 256 + 16 * ((fb >> 4) ^ pp_vswz(row)) + (fb & 15);
       }
   }
 
