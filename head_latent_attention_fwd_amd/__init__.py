@@ -4,8 +4,8 @@ The computation lives in ``libmla.so`` (hand-written HIP kernels for gfx950
 behind the C ABI of ``include/mla.h``); this package is its Python binding.
 """
 from ._lib import (  # noqa: F401
-    BLOCK_NAMES, MLA_BF16, MLA_F32, W_NAMES, BlockWeights, Dims, MLAError, Weights,
-    block_workspace_size,
+    BIAS_NAMES, BLOCK_NAMES, MLA_BF16, MLA_F32, W_NAMES, BlockWeights, Dims, MLAError, Weights,
+    bias_shapes, block_workspace_size,
     decode_workspace_size, dense_block_fwd, load, make_dims, mla_decode_fullcache,
     mla_decode_fullcache_ragged, mla_decode_latentcache, mla_decode_latentcache_ragged, mla_prefill,
     mla_profile_enable, mla_profile_summary, mla_rope_table, prefill_workspace_size, weight_shapes,

@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 
 MLA_F32, MLA_BF16 = 0, 1
 W_NAMES = ("w_dq", "g_q", "w_uqr", "w_dkvr", "g_kv", "w_ukv", "w_o")
+# optional biases of the attention_bias variant (absent = no bias)
+BIAS_NAMES = ("b_dq", "b_dkvr", "b_o")
 BLOCK_NAMES = ("g_attn", "g_ffn", "w1", "w3", "w2")
 
 
@@ -44,7 +46,7 @@ class Dims(ctypes.Structure):
 
 
 class Weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in W_NAMES]
+    _fields_ = [(n, ctypes.c_void_p) for n in W_NAMES + BIAS_NAMES]
 
 
 class BlockWeights(ctypes.Structure):
@@ -144,9 +146,18 @@ def _tensor(t, name, shape, dtype, device=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def bias_shapes(d: Dims) -> dict:
+    """Shapes of the optional attention_bias biases."""
+    return {"b_dq": (d.q_lora_rank,), "b_dkvr": (d.kv_lora_rank + d.qk_rope_dim,), "b_o": (d.d_model,)}
+
+
 def _weights(d: Dims, w: dict, device) -> Weights:
     shapes = weight_shapes(d)
-    return Weights(*[_tensor(w[n], n, shapes[n], d.torch_dtype, device) for n in W_NAMES])
+    bshapes = bias_shapes(d)
+    ptrs = [_tensor(w[n], n, shapes[n], d.torch_dtype, device) for n in W_NAMES]
+    ptrs += [_tensor(w[n], n, bshapes[n], d.torch_dtype, device) if w.get(n) is not None else None
+             for n in BIAS_NAMES]
+    return Weights(*ptrs)
 
 
 def _rope(rope, rows_needed, d: Dims, device):

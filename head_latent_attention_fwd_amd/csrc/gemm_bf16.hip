@@ -502,6 +502,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmGroup gg) {
           v[2 * q + 1] += hi_bf(r[q]);
         }
       }
+      if (EPI != EPI_SWIGLU && p.bias) {
+        // o_proj of the attention_bias variant: y = x W^T + b
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (col + q < out_cols) v[q] += bf2f(p.bias[col + q]);
+      }
       u32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = pack2bf(v[2 * q], v[2 * q + 1]);

@@ -1,4 +1,4 @@
-// fp32 GEMM for the float32 path (any M, N, K): C = R + A . op(B).
+// fp32 GEMM for the float32 path (any M, N, K): C = R + A . op(B) (+ bias).
 //
 // The float32 configuration is the parity-precision form of the method
 // (the tiny MLA workload and arbitrary head widths); it is small, so a plain
@@ -62,6 +62,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Params p) {
       if (gm < p.M && gn < p.N) {
         float v = acc[i][j];
         if (R) v += R[(long)gm * p.ldr + gn];
+        if (p.bias) v += p.bias[gn];
         C[(long)gm * p.ldc + gn] = v;
       }
     }

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
       if (row >= p.M) continue;
       if (BF16OUT) {
         bf16_t* C = (bf16_t*)p.C + (long)bidx * p.sC;
-        C[(long)row * p.ldc + c] = f2bf(acc[mb][e]);
+        C[(long)row * p.ldc + c] = f2bf(acc[mb][e] + (p.bias ? bf2f(p.bias[c]) : 0.f));
       } else {
         float* C = (float*)p.C + (long)bidx * p.sC + (long)split * p.split_stride;
         C[(long)row * p.ldc + c] = acc[mb][e];

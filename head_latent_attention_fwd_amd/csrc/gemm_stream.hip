@@ -165,7 +165,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p, StreamIn
 template <typename T>
 __global__ __launch_bounds__(256) void stream_reduce_kernel(const float* __restrict__ part, StreamInfo s,
                                                             int M, int N, T* __restrict__ out, long ldo,
-                                                            const bf16_t* __restrict__ R, long ldr) {
+                                                            const bf16_t* __restrict__ R, long ldr,
+                                                            const T* __restrict__ bias) {
   const long e4 = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (e4 >= (long)M * (N / 4)) return;
   const int m = (int)(e4 / (N / 4)), n = 4 * (int)(e4 % (N / 4));
@@ -173,6 +174,10 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(const float* __restr
   if (R) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] += bf2f(R[(long)m * ldr + n + q]);
+  }
+  if (bias) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += to_f<T>(bias[n + q]);
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) out[(long)m * ldo + n + q] = from_f<T>(v[q]);
@@ -208,17 +213,17 @@ hipError_t gemm_stream_bf16(const GemmParams& p, float* part, const StreamInfo& 
 
 template <typename T>
 hipError_t stream_reduce(const float* part, const StreamInfo& s, int M, int N, T* out, long ldo,
-                         const bf16_t* R, long ldr, hipStream_t st) {
+                         const bf16_t* R, long ldr, hipStream_t st, const T* bias) {
   const long n = (long)M * (N / 4);
   if (n == 0) return hipSuccess;
   if (N % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(stream_reduce_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part,
-                     s, M, N, out, ldo, R, ldr);
+                     s, M, N, out, ldo, R, ldr, bias);
   return hipGetLastError();
 }
 template hipError_t stream_reduce<float>(const float*, const StreamInfo&, int, int, float*, long,
-                                         const bf16_t*, long, hipStream_t);
+                                         const bf16_t*, long, hipStream_t, const float*);
 template hipError_t stream_reduce<bf16_t>(const float*, const StreamInfo&, int, int, bf16_t*, long,
-                                          const bf16_t*, long, hipStream_t);
+                                          const bf16_t*, long, hipStream_t, const bf16_t*);
 
 }  // namespace mla

@@ -27,6 +27,8 @@ struct GemmParams {
   int batch;
   long sA, sB, sC;   // batch strides in elements
   int tiles_m, tiles_n;  // filled by the launcher
+  const bf16_t* bias;    // optional per-output-column bias [N] (bf16-output
+                         // epilogues: EPI_BF16, EPI_RESID, the skinny kernel)
 };
 
 struct GemmPlan { int cfg, ksplit, kchunk; };
@@ -60,10 +62,11 @@ bool stream_ok(const GemmParams& p);  // M <= 64, K % 128 == 0, N % 4 == 0, b_sp
 StreamInfo stream_info(int M, int N, int K);
 size_t stream_part_floats(const StreamInfo& s);
 hipError_t gemm_stream_bf16(const GemmParams& p, float* part, const StreamInfo& s, hipStream_t st);
-// out[m, n] = sum of the partials (+ R[m, n] when R is not NULL)
+// out[m, n] = sum of the partials (+ R[m, n] when R is not NULL) (+ bias[n]
+// when bias is not NULL)
 template <typename T>
 hipError_t stream_reduce(const float* part, const StreamInfo& s, int M, int N, T* out, long ldo,
-                         const bf16_t* R, long ldr, hipStream_t st);
+                         const bf16_t* R, long ldr, hipStream_t st, const T* bias = nullptr);
 
 // fp32 generic GEMM: C[b] = (R ? R : 0) + A[b] . op(B[b]); op(B) = B^T when
 // b_is_nk (B stored [N, K]) else B (stored [K, N]).
@@ -73,6 +76,7 @@ struct GemmF32Params {
   int M, N, K, batch;
   long sA, sB, sC;
   int b_is_nk;
+  const float* bias;  // optional per-output-column bias [N]
 };
 hipError_t gemm_f32(const GemmF32Params& p, hipStream_t s);
 
@@ -102,6 +106,9 @@ template <typename T> struct LatentNormParams {
   // optional per-sequence positions (decode, rope_T = 1): row m is at
   // position seq_pos[m] clamped into [0, pos_max] instead of rope_pos0
   const int* seq_pos; int pos_max;
+  // optional biases of the two down-projections, added to the summed row
+  // before the norms and the RoPE: bias_q [q_lora], bias_kvr [kv_lora + d_rope]
+  const T* bias_q; const T* bias_kvr;
 };
 template <typename T> hipError_t latent_norm_rope(const LatentNormParams<T>& p, hipStream_t s);
 
@@ -127,10 +134,10 @@ hipError_t scatter_full_cache(const T* kv, const T* kr, T* k_cache, T* v_cache, 
                               int pos0, int L_cap, int H, int d_nope, int d_rope, int d_v,
                               hipStream_t s, const int* seq_pos = nullptr, int pos_max = 0);
 
-// Sum fp32 split partials [nsplit][M][N] into T out [M][ldo].
+// Sum fp32 split partials [nsplit][M][N] into T out [M][ldo] (+ bias[n]).
 template <typename T>
 hipError_t reduce_splits(const float* part, int nsplit, long split_stride, int M, int N, T* out,
-                         long ldo, hipStream_t s);
+                         long ldo, hipStream_t s, const T* bias = nullptr);
 
 // ------------------------------------------------------------ attention
 // Generic attention (fp32 path and any head widths): one wave per query.

@@ -244,7 +244,7 @@ int gemm_bf16_out(const char* name, GemmParams g, void* part, size_t part_floats
     if (part && stream_part_floats(si) <= part_floats) {
       LAUNCH(name, gemm_stream_bf16(g, (float*)part, si, st));
       LAUNCH("stream_reduce", stream_reduce<bf16_t>((const float*)part, si, g.M, g.N, (bf16_t*)g.C,
-                                                    g.ldc, nullptr, 0, st));
+                                                    g.ldc, nullptr, 0, st, g.bias));
       return MLA_OK;
     }
   }
@@ -261,7 +261,7 @@ int gemm_bf16_out(const char* name, GemmParams g, void* part, size_t part_floats
   f.split_stride = (long)g.M * g.N;
   LAUNCH(name, gemm_skinny_bf16(f, false, st));
   LAUNCH("reduce_splits", reduce_splits<bf16_t>((const float*)part, S, (long)g.M * g.N, g.M, g.N,
-                                                 (bf16_t*)g.C, g.ldc, st));
+                                                 (bf16_t*)g.C, g.ldc, st, g.bias));
   return MLA_OK;
 }
 
@@ -327,6 +327,7 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
     n.split_stride = (long)M * N1; n.ld_part = N1;
     n.stream = streamed ? 1 : 0; n.si = si;
     n.seq_pos = seq_pos; n.pos_max = pos_max;
+    n.bias_q = (const bf16_t*)w->b_dq; n.bias_kvr = (const bf16_t*)w->b_dkvr;
     n.M = M; n.q_lora = ql; n.kv_lora = kl; n.d_rope = dr;
     n.g_q = (const bf16_t*)w->g_q; n.g_kv = (const bf16_t*)w->g_kv; n.eps = d->rms_eps;
     n.cq = (bf16_t*)b.cq; n.ld_cq = ql; n.ckv = (bf16_t*)b.ckv; n.ld_ckv = kl;
@@ -391,6 +392,7 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
   n.rcos = rc; n.rsin = rs; n.n_pairs = dr / 2; n.rope_T = rowsT; n.rope_pos0 = pos0;
   n.latent_cache = (float*)latent_cache; n.L_cap = L_cap;
   n.seq_pos = seq_pos; n.pos_max = pos_max;
+  n.bias_q = (const float*)w->b_dq; n.bias_kvr = (const float*)w->b_dkvr;
   LAUNCH("latent_norm_rope", latent_norm_rope<float>(n, st));
   GemmF32Params q;
   memset(&q, 0, sizeof q);
@@ -412,13 +414,15 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
 }
 
 // out[M, d] = o[M, H*dv] . W_O^T (+ R).  Split-K for small M (decode).
-int run_oproj(const mla_dims* d, const void* w_o, const void* o, int M, const void* R, void* out,
-              void* part, size_t part_floats, int S, hipStream_t st) {
+// o_proj (+ bias b_o when given) (+ residual R when given).
+int run_oproj(const mla_dims* d, const void* w_o, const void* b_o, const void* o, int M, const void* R,
+              void* out, void* part, size_t part_floats, int S, hipStream_t st) {
   const int D = d->d_model, K = d->n_heads * d->v_head_dim;
   if (d->dtype == MLA_BF16) {
     GemmParams g = gp_base();
     g.A = (const bf16_t*)o; g.lda = K; g.B = (const bf16_t*)w_o; g.ldb = K;
     g.M = M; g.N = D; g.K = K;
+    g.bias = (const bf16_t*)b_o;
     if (S > 1) {
       g.C = out; g.ldc = D;
       return gemm_bf16_out("gemm_o_proj", g, part, part_floats, st);
@@ -432,6 +436,7 @@ int run_oproj(const mla_dims* d, const void* w_o, const void* o, int M, const vo
   memset(&g, 0, sizeof g);
   g.A = (const float*)o; g.lda = K; g.B = (const float*)w_o; g.ldb = K;
   g.C = (float*)out; g.ldc = D; g.R = (const float*)R; g.ldr = D;
+  g.bias = (const float*)b_o;
   g.M = M; g.N = D; g.K = K; g.batch = 1; g.b_is_nk = 1;
   LAUNCH("gemm_o_proj", gemm_f32(g, st));
   return MLA_OK;
@@ -486,7 +491,7 @@ int prefill_core(const mla_dims* d, const mla_weights* w, const void* x, int B, 
       LAUNCH("scatter_cache", scatter_full_cache<float>((const float*)b.kv, (const float*)b.kr, (float*)k_cache,
                                        (float*)v_cache, B, T, 0, L_cap, H, dn, dr, dv, st));
   }
-  return run_oproj(d, w->w_o, b.o, M, resid, out, nullptr, 0, 1, st);
+  return run_oproj(d, w->w_o, w->b_o, b.o, M, resid, out, nullptr, 0, 1, st);
 }
 
 // --------------------------------------------------------------- decode
@@ -749,7 +754,7 @@ static int decode_full_impl(const mla_dims* d, const mla_weights* w, const void*
     a.seq_pos = seq_pos; a.pos_max = P;
     LAUNCH("attn_generic", attn_generic_f32(a, st));
   }
-  return run_oproj(d, w->w_o, b.o, B, nullptr, out, pl.opart, pl.opart_floats, pl.S2, st);
+  return run_oproj(d, w->w_o, w->b_o, b.o, B, nullptr, out, pl.opart, pl.opart_floats, pl.S2, st);
 }
 
 int mla_decode_fullcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
@@ -857,7 +862,7 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
     u.sA = kl; u.sB = (long)(dn + dv) * kl; u.sC = dv;
     LAUNCH("gemm_uv", gemm_f32(u, st));
   }
-  return run_oproj(d, w->w_o, b.o, B, nullptr, out, pl.opart, pl.opart_floats, pl.S2, st);
+  return run_oproj(d, w->w_o, w->b_o, b.o, B, nullptr, out, pl.opart, pl.opart_floats, pl.S2, st);
 }
 
 int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,

@@ -60,6 +60,14 @@ MLA_DEV float block_sum(float v, float* red) {
   return t;
 }
 
+// Bias of down-projection output column c ([q latent | kv latent | rotary
+// key]), or 0 without the attention_bias variant.
+template <typename T>
+MLA_DEV float down_bias(const LatentNormParams<T>& p, int c) {
+  if (c < p.q_lora) return p.bias_q ? to_f<T>(p.bias_q[c]) : 0.f;
+  return p.bias_kvr ? to_f<T>(p.bias_kvr[c - p.q_lora]) : 0.f;
+}
+
 // One workgroup of NT threads per row: sum the down-projection partials of
 // the row in a fixed order (deterministic) -- either nsplit fp32 K-slices or
 // the weight-streaming GEMM's partial blocks -- then the two RMSNorms and the
@@ -80,9 +88,10 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c = 4 * c4 + q;
-        row[c] = v[q];
-        if (c < p.q_lora) sq += v[q] * v[q];
-        else if (c < p.q_lora + p.kv_lora) skv += v[q] * v[q];
+        const float x = v[q] + down_bias(p, c);
+        row[c] = x;
+        if (c < p.q_lora) sq += x * x;
+        else if (c < p.q_lora + p.kv_lora) skv += x * x;
       }
     }
   } else if (vec) {
@@ -91,9 +100,10 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c = 4 * c4 + q;
-        row[c] = v[q];
-        if (c < p.q_lora) sq += v[q] * v[q];
-        else if (c < p.q_lora + p.kv_lora) skv += v[q] * v[q];
+        const float x = v[q] + down_bias(p, c);
+        row[c] = x;
+        if (c < p.q_lora) sq += x * x;
+        else if (c < p.q_lora + p.kv_lora) skv += x * x;
       }
     }
   } else {
@@ -101,6 +111,7 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
       float v = 0.f;
       for (int s = 0; s < p.nsplit; ++s)
         v += p.part[(long)s * p.split_stride + (long)m * p.ld_part + c];
+      v += down_bias(p, c);
       row[c] = v;
       if (c < p.q_lora) sq += v * v;
       else if (c < p.q_lora + p.kv_lora) skv += v * v;
@@ -347,7 +358,7 @@ template hipError_t scatter_full_cache<bf16_t>(const bf16_t*, const bf16_t*, bf1
 
 template <typename T>
 __global__ void reduce_splits_kernel(const float* __restrict__ part, int nsplit, long stride, int M,
-                                     int N, T* __restrict__ out, long ldo) {
+                                     int N, T* __restrict__ out, long ldo, const T* __restrict__ bias) {
   // 4 consecutive columns per thread (N % 4 == 0 checked by the launcher)
   long e4 = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (e4 >= (long)M * N / 4) return;
@@ -356,22 +367,22 @@ __global__ void reduce_splits_kernel(const float* __restrict__ part, int nsplit,
   const int n = (int)(e % N);
   const floatx4 v = sum_splits4(part + e, stride, nsplit);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) out[m * ldo + n + q] = from_f<T>(v[q]);
+  for (int q = 0; q < 4; ++q) out[m * ldo + n + q] = from_f<T>(v[q] + (bias ? to_f<T>(bias[n + q]) : 0.f));
 }
 
 template <typename T>
 hipError_t reduce_splits(const float* part, int nsplit, long split_stride, int M, int N, T* out,
-                         long ldo, hipStream_t s) {
+                         long ldo, hipStream_t s, const T* bias) {
   long n = (long)M * N / 4;
   if (n == 0) return hipSuccess;
   if (N % 4 || split_stride % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(reduce_splits_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     part, nsplit, split_stride, M, N, out, ldo);
+                     part, nsplit, split_stride, M, N, out, ldo, bias);
   return hipGetLastError();
 }
 template hipError_t reduce_splits<float>(const float*, int, long, int, int, float*, long,
-                                         hipStream_t);
+                                         hipStream_t, const float*);
 template hipError_t reduce_splits<bf16_t>(const float*, int, long, int, int, bf16_t*, long,
-                                          hipStream_t);
+                                          hipStream_t, const bf16_t*);
 
 }  // namespace mla

@@ -36,7 +36,8 @@
  *      w_ukv  [H*(d_nope+d_v), kv_lora]       kv up-projection; per head h rows
  *                                             h*(d_nope+d_v) + [key content | value]
  *      w_o    [d, H*d_v]                      output projection; input column h*d_v + c
- *    No biases (the pages' parameter totals hold only without them).
+ *    No biases by default (the pages' parameter totals hold only without
+ *    them); the optional attention_bias biases are described at mla_weights.
  *  - RMSNorm is g * x / sqrt(mean(x^2) + eps).  RoPE turns the consecutive
  *    pair (2i, 2i+1) of each rotary slice by angle t * theta_i; the caller
  *    passes the table R as rope_cos/rope_sin [rope_rows, d_rope/2] (float32;
@@ -94,6 +95,14 @@ typedef struct {
 
 typedef struct {
   const void *w_dq, *g_q, *w_uqr, *w_dkvr, *g_kv, *w_ukv, *w_o;
+  /* Optional biases of the attention_bias variant ([KV] module code: the
+   * query down-projection, the joint kv down-projection and o_proj take
+   * bias=config.attention_bias; the two up-projections have none).  NULL =
+   * no bias (the pinned configuration).  dtype as the weights:
+   *   b_dq [q_lora], b_dkvr [kv_lora + d_rope] (latent | rotary key), b_o [d].
+   * y = x W^T + b; the down-projection biases are added before the latent
+   * RMSNorms and the rotary key's RoPE. */
+  const void *b_dq, *b_dkvr, *b_o;
 } mla_weights;
 
 /* Dense block ([DB]): input RMSNorm gain, MLA, post-attention RMSNorm gain,

@@ -35,14 +35,14 @@ def _mat(a):
     return [[float(v) for v in row] for row in a]
 
 
-def _linear(xrow, W):
-    """y[o] = sum_i x[i] * W[o][i] (nn.Linear layout [out, in])."""
+def _linear(xrow, W, bias=None):
+    """y[o] = sum_i x[i] * W[o][i] (+ b[o]) (nn.Linear layout [out, in])."""
     out = []
-    for wrow in W:
+    for o, wrow in enumerate(W):
         s = 0.0
         for xi, wi in zip(xrow, wrow):
             s += xi * wi
-        out.append(s)
+        out.append(s if bias is None else s + bias[o])
     return out
 
 
@@ -69,10 +69,10 @@ def _rope(v, t, base):
 def _project_token(d, w, xrow, t):
     """Per-token steps 1-3.  Returns dict of per-head lists."""
     H, dn, dr, dv, r = d.n_heads, d.qk_nope_dim, d.qk_rope_dim, d.v_head_dim, d.kv_lora_rank
-    cq = _linear(xrow, w["w_dq"])
+    cq = _linear(xrow, w["w_dq"], w.get("b_dq"))
     cqh = _rmsnorm(cq, w["g_q"], d.rms_eps)
     qfull = _linear(cqh, w["w_uqr"])
-    a = _linear(xrow, w["w_dkvr"])
+    a = _linear(xrow, w["w_dkvr"], w.get("b_dkvr"))
     ckv = a[:r]
     kpe = a[r:r + dr]
     ckvh = _rmsnorm(ckv, w["g_kv"], d.rms_eps)
@@ -104,13 +104,14 @@ def _softmax_mix(scores, values):
 
 
 def _weights(w):
-    return {k: (_vec(v) if getattr(v, "ndim", 2) == 1 else _mat(v)) for k, v in w.items()}
+    return {k: (_vec(v) if getattr(v, "ndim", 2) == 1 else _mat(v)) for k, v in w.items() if v is not None}
 
 
 def prefill(d, w, x):
     """Causal MLA prefill of x [B][T][d] at positions 0..T-1 (plain nested
     lists or arrays).  ``w`` maps the weight names of the library's layout
-    (w_dq, g_q, w_uqr, w_dkvr, g_kv, w_ukv, w_o) to arrays."""
+    (w_dq, g_q, w_uqr, w_dkvr, g_kv, w_ukv, w_o, and optionally the biases
+    b_dq, b_dkvr, b_o of the attention_bias variant) to arrays."""
     W = _weights(w)
     H, dv = d.n_heads, d.v_head_dim
     scale = 1.0 / math.sqrt(d.qk_nope_dim + d.qk_rope_dim)
@@ -133,7 +134,7 @@ def prefill(d, w, x):
                     vals.append(tj["v"][h])
                 merged += _softmax_mix(scores, vals)
             assert len(merged) == H * dv
-            ob.append(_linear(merged, W["w_o"]))
+            ob.append(_linear(merged, W["w_o"], W.get("b_o")))
         out.append(ob)
     return out
 
@@ -165,7 +166,7 @@ def decode_fullcache(d, w, x_new, P, k_cache, v_cache):
                 scores.append(s * scale)
                 vals.append(V)
             merged += _softmax_mix(scores, vals)
-        out.append(_linear(merged, W["w_o"]))
+        out.append(_linear(merged, W["w_o"], W.get("b_o")))
     return out
 
 
@@ -201,7 +202,7 @@ def decode_latentcache(d, w, x_new, P, latent_cache):
                 scores.append(s * scale)
                 vals.append(kvfull[base + dn:base + dn + dv])
             merged += _softmax_mix(scores, vals)
-        out.append(_linear(merged, W["w_o"]))
+        out.append(_linear(merged, W["w_o"], W.get("b_o")))
     return out
 
 

@@ -38,7 +38,11 @@ function that uses it):
   both queries and keys, which leaves every score unchanged.
 * The softmax scale is 1/sqrt(d_nope + d_rope), also in the absorbed form.
 * The causal mask sets scores of keys j > i to -inf (exact zeros after exp).
-* No linear layer has a bias (the pages' parameter totals hold only then).
+* No linear layer has a bias in the pinned configuration (the pages'
+  parameter totals hold only then).  The module code on [KV] makes the
+  query down-projection, the joint kv down-projection and o_proj carry a bias
+  when the config asks for one (attention_bias); the optional b_dq, b_dkvr
+  and b_o below are those biases, added to the products y = x W^T + b.
 * The per-head row layouts of the fused up-projections are head-major:
   q rows h*(d_nope+d_rope) + [nope | rope], kv rows h*(d_nope+d_v) + [k | v].
 * Decode: slots 0..P-1 of a cache are history; the new token's entries are
@@ -54,7 +58,7 @@ import numpy as np
 
 __all__ = [
     "MLADims", "KIMI_K2", "TINY", "MLAWeights", "BlockWeights",
-    "weight_shapes", "block_weight_shapes", "parameter_counts",
+    "weight_shapes", "bias_shapes", "block_weight_shapes", "parameter_counts",
     "cache_values_per_position", "rms_norm", "rope_angles", "apply_rope",
     "silu", "mla_project", "attention", "mla_prefill",
     "mla_decode_fullcache", "mla_decode_latentcache", "dense_block",
@@ -168,12 +172,33 @@ class MLAWeights:
     g_kv: np.ndarray
     w_ukv: np.ndarray
     w_o: np.ndarray
+    # optional biases of the attention_bias variant ([KV] module code):
+    # q_a_proj [q_lora], kv_a_proj_with_mqa [kv_lora + d_rope], o_proj [d]
+    b_dq: np.ndarray | None = None
+    b_dkvr: np.ndarray | None = None
+    b_o: np.ndarray | None = None
 
     def check(self, dims: MLADims) -> None:
         for name, shape in weight_shapes(dims).items():
             got = getattr(self, name).shape
             if got != shape:
                 raise ValueError(f"{name}: shape {got}, expected {shape}")
+        for name, shape in bias_shapes(dims).items():
+            b = getattr(self, name)
+            if b is not None and b.shape != shape:
+                raise ValueError(f"{name}: shape {b.shape}, expected {shape}")
+
+
+def bias_shapes(dims: MLADims) -> dict:
+    """Biases of the attention_bias variant: the layers the [KV] module code
+    builds with bias=config.attention_bias (q_b_proj and kv_b_proj have
+    bias=False)."""
+    return {"b_dq": (dims.q_lora_rank,), "b_dkvr": (dims.kv_lora_rank + dims.qk_rope_dim,),
+            "b_o": (dims.d_model,)}
+
+
+def _bias(b, dtype):
+    return 0.0 if b is None else _f(b, dtype)
 
 
 @dataclass
@@ -251,13 +276,13 @@ def mla_project(dims: MLADims, w: MLAWeights, x: np.ndarray,
     B, T, _ = x.shape
     x = _f(x, dtype)
     # Query path: down-projection, latent RMSNorm, up-projection.
-    c_q = x @ _f(w.w_dq, dtype).T                                  # [B,T,q_lora]
+    c_q = x @ _f(w.w_dq, dtype).T + _bias(w.b_dq, dtype)           # [B,T,q_lora]
     c_q_hat = rms_norm(c_q, _f(w.g_q, dtype), dims.rms_eps)
     q = (c_q_hat @ _f(w.w_uqr, dtype).T).reshape(B, T, H, dn + dr)
     q_nope = q[..., :dn]                                            # Q^C
     q_pe = q[..., dn:]                                              # Q^pe
     # Joint KV down-projection, split after the product ([KV] Explanation).
-    a = x @ _f(w.w_dkvr, dtype).T                                  # [B,T,kv_lora+dr]
+    a = x @ _f(w.w_dkvr, dtype).T + _bias(w.b_dkvr, dtype)         # [B,T,kv_lora+dr]
     c_kv = a[..., :dims.kv_lora_rank]
     k_pe = a[..., dims.kv_lora_rank:]                               # [B,T,dr]
     c_kv_hat = rms_norm(c_kv, _f(w.g_kv, dtype), dims.rms_eps)
@@ -326,7 +351,7 @@ def mla_prefill(dims: MLADims, w: MLAWeights, x: np.ndarray, rows=None,
         o[b] = attention(p["q_nope"][b, qrows], p["q_rope"][b, qrows],
                          p["k_nope"][b], p["k_rope"][b], p["v"][b],
                          dims.softmax_scale, pos[qrows], pos)
-    out = _merge_heads(o) @ _f(w.w_o, dtype).T
+    out = _merge_heads(o) @ _f(w.w_o, dtype).T + _bias(w.b_o, dtype)
     if return_intermediates:
         p["o"] = o
         return out, p
@@ -382,7 +407,7 @@ def mla_decode_fullcache(dims: MLADims, w: MLAWeights, x_new: np.ndarray, P: int
             E = np.exp(S - m)
             Pr = E / np.sum(E)
             o[b, h] = Pr @ vc[b, h, :L, :]
-    out = _merge_heads(o) @ _f(w.w_o, dtype).T
+    out = _merge_heads(o) @ _f(w.w_o, dtype).T + _bias(w.b_o, dtype)
     return out, kc, vc
 
 
@@ -438,7 +463,7 @@ def mla_decode_latentcache(dims: MLADims, w: MLAWeights, x_new: np.ndarray, P: i
         Pr = E / np.sum(E, axis=-1, keepdims=True)
         o_lat[b] = Pr @ C
     o = absorbed_output(dims, w, o_lat, dtype)                       # [B,H,dv]
-    out = _merge_heads(o) @ _f(w.w_o, dtype).T
+    out = _merge_heads(o) @ _f(w.w_o, dtype).T + _bias(w.b_o, dtype)
     return out, cc
 
 

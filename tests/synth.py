@@ -61,6 +61,17 @@ def mla_weights(dims, rng, bf16: bool) -> dict:
     return w
 
 
+BIAS_STD = 0.5  # synthetic attention_bias values: the pages give none
+
+
+def attention_biases(dims, rng, bf16: bool) -> dict:
+    """Biases of the attention_bias variant: b_dq [q_lora], b_dkvr
+    [kv_lora + d_rope], b_o [d], each N(0, BIAS_STD^2)."""
+    return {"b_dq": _draw(rng, (dims.q_lora_rank,), BIAS_STD, bf16),
+            "b_dkvr": _draw(rng, (dims.kv_lora_rank + dims.qk_rope_dim,), BIAS_STD, bf16),
+            "b_o": _draw(rng, (dims.d_model,), BIAS_STD, bf16)}
+
+
 def prefill_inputs(dims, B, T, seed, bf16=True):
     rng = np.random.default_rng(seed)
     x = _draw(rng, (B, T, dims.d_model), 1.0, bf16)

@@ -315,6 +315,78 @@ def test_ragged_decode_uniform_and_clamped(form):
     np.testing.assert_array_equal(c1, c2)
 
 
+# --------------------------------------------------- attention_bias variant
+def _with_biases(w, od, seed, bf16):
+    return dict(w, **synth.attention_biases(od, np.random.default_rng(seed), bf16))
+
+
+@pytest.mark.parametrize("case", [
+    ("tiny_f32", ref.TINY, 2, 37, "f32", 101),
+    ("kimi_narrow_bf16", KIMI_NARROW, 2, 200, "bf16", 102),
+    ("kimi_bf16_T130", ref.KIMI_K2, 1, 130, "bf16", 103),
+])
+def test_prefill_attention_bias(case):
+    """q_a_proj, kv_a_proj_with_mqa and o_proj biases (prefill, with both
+    cache outputs)."""
+    name, od, B, T, dt, seed = case
+    log(f"[prefill bias {name}] B={B} T={T} dtype={dt}")
+    x, w = synth.prefill_inputs(od, B, T, seed, bf16=(dt == "bf16"))
+    w = _with_biases(w, od, seed + 1, dt == "bf16")
+    want, p = ref.mla_prefill(od, oracle_weights(w), x.astype(np.float64), return_intermediates=True)
+    d = dims_of(mla, od, dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    L_cap = T + 3
+    lc = torch.zeros(B, L_cap, od.kv_lora_rank + od.qk_rope_dim, dtype=tdt, device=DEV)
+    got = mla.mla_prefill(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), _rope(od, T), latent_cache=lc)
+    torch.cuda.synchronize()
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(from_dev(got), want, tol, name)
+    assert_close(from_dev(lc)[:, :T], ref.latent_cache_entries(od, p), tol, f"{name} latent cache")
+
+
+@pytest.mark.parametrize("form", ["full", "latent"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_decode_attention_bias(form, dt):
+    od = ref.TINY if dt == "f32" else KIMI_NARROW
+    B, P, L_cap, seed = 3, 30, 40, 104
+    log(f"[decode bias {form} {dt}] B={B} P={P}")
+    d = dims_of(mla, od, dt)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    if form == "full":
+        x, w, kc, vc = synth.decode_full_inputs(od, B, P, L_cap, seed, bf16=(dt == "bf16"))
+        w = _with_biases(w, od, seed + 1, dt == "bf16")
+        got = mla.mla_decode_fullcache(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), P,
+                                       bits_to_dev(kc, dt, DEV), bits_to_dev(vc, dt, DEV), _rope(od, P + 1))
+        want, _, _ = ref.mla_decode_fullcache(od, oracle_weights(w), x.astype(np.float64), P,
+                                              synth.as_f32(kc, dt == "bf16").astype(np.float64),
+                                              synth.as_f32(vc, dt == "bf16").astype(np.float64))
+    else:
+        x, w, cc = synth.decode_latent_inputs(od, B, P, L_cap, seed, bf16=(dt == "bf16"))
+        w = _with_biases(w, od, seed + 1, dt == "bf16")
+        got = mla.mla_decode_latentcache(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), P,
+                                         bits_to_dev(cc, dt, DEV), _rope(od, P + 1))
+        want, _ = ref.mla_decode_latentcache(od, oracle_weights(w), x.astype(np.float64), P,
+                                             synth.as_f32(cc, dt == "bf16").astype(np.float64))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got), want, tol, f"decode bias {form} {dt}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_dense_block_attention_bias(dt):
+    od = ref.TINY if dt == "f32" else KIMI_NARROW
+    B, T, seed = 1, 70, 105
+    log(f"[block bias {dt}] B={B} T={T}")
+    x, w, blk = synth.block_inputs(od, B, T, seed, bf16=(dt == "bf16"))
+    w = _with_biases(w, od, seed + 1, dt == "bf16")
+    bw = ref.BlockWeights(attn=oracle_weights(w), **{k: np.asarray(v, np.float64) for k, v in blk.items()})
+    want = ref.dense_block(od, bw, x.astype(np.float64))
+    d = dims_of(mla, od, dt)
+    got = mla.dense_block_fwd(d, weights_to_dev(w, dt, DEV), weights_to_dev(blk, dt, DEV),
+                              to_dev(x, dt, DEV), _rope(od, T))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got), want, TOL_F32 if dt == "f32" else TOL_BF16, f"block bias {dt}")
+
+
 def _spike_scale(od, w, x_b, P, cf_b, pos, floor_rows):
     """Power of two that lifts row `pos`'s score, for its best head, at least
     12 (natural-log units) above every score in `floor_rows`; oracle steps."""

@@ -296,6 +296,56 @@ def pin_brute_block(dims=MICRO, seed=12):
     _close(ref.dense_block(dims, bw, x), brute.dense_block(dims, w, blk, x))
 
 
+def _bias_weights(dims, seed):
+    w = _weights(dims, seed)
+    w.update({k: v.astype(np.float64) for k, v in
+              synth.attention_biases(dims, np.random.default_rng(seed + 100), bf16=False).items()})
+    return w
+
+
+def pin_brute_bias(dims=MICRO, seed=31):
+    """attention_bias variant: every path against the loop oracle with the
+    three biases (q_a_proj, kv_a_proj_with_mqa, o_proj) present."""
+    rng = np.random.default_rng(seed)
+    w = _bias_weights(dims, seed)
+    x = _x((2, 5, dims.d_model), seed + 1)
+    _close(ref.mla_prefill(dims, _mw(w), x), brute.prefill(dims, w, x))
+    B, P, L_cap = 2, 4, 6
+    xd = rng.standard_normal((B, dims.d_model))
+    kc = rng.standard_normal((B, dims.n_heads, L_cap, dims.q_head_dim))
+    vc = rng.standard_normal((B, dims.n_heads, L_cap, dims.v_head_dim))
+    _close(ref.mla_decode_fullcache(dims, _mw(w), xd, P, kc, vc)[0], brute.decode_fullcache(dims, w, xd, P, kc, vc))
+    cc = rng.standard_normal((B, L_cap, dims.kv_lora_rank + dims.qk_rope_dim))
+    _close(ref.mla_decode_latentcache(dims, _mw(w), xd, P, cc)[0], brute.decode_latentcache(dims, w, xd, P, cc))
+    blk = {"w1": 0.3 * rng.standard_normal((dims.d_ff, dims.d_model)),
+           "w3": 0.3 * rng.standard_normal((dims.d_ff, dims.d_model)),
+           "w2": 0.3 * rng.standard_normal((dims.d_model, dims.d_ff)),
+           "g_attn": 1 + 0.3 * rng.standard_normal(dims.d_model),
+           "g_ffn": 1 + 0.3 * rng.standard_normal(dims.d_model)}
+    xb = _x((1, 4, dims.d_model), seed + 2)
+    _close(ref.dense_block(dims, ref.BlockWeights(attn=_mw(w), **blk), xb), brute.dense_block(dims, w, blk, xb))
+
+
+def pin_bias_special_cases(dims=MICRO, seed=32):
+    """Zero biases are no biases (bit for bit); with W_O = 0 the output is
+    b_o in every row exactly."""
+    w = _weights(dims, seed)
+    x = _x((2, 4, dims.d_model), seed + 1)
+    wz = dict(w, b_dq=np.zeros(dims.q_lora_rank), b_dkvr=np.zeros(dims.kv_lora_rank + dims.qk_rope_dim),
+              b_o=np.zeros(dims.d_model))
+    np.testing.assert_array_equal(ref.mla_prefill(dims, _mw(wz), x), ref.mla_prefill(dims, _mw(w), x))
+    wb = _bias_weights(dims, seed)
+    wb["w_o"] = np.zeros_like(wb["w_o"])
+    out = ref.mla_prefill(dims, _mw(wb), x)
+    np.testing.assert_array_equal(out, np.broadcast_to(wb["b_o"], out.shape))
+
+
+def test_attention_bias_variant():
+    pin_brute_bias()
+    pin_brute_bias(MICRO_EQ, 33)
+    pin_bias_special_cases()
+
+
 def test_brute_prefill():
     pin_brute_prefill()
     pin_brute_prefill(MICRO_EQ)
@@ -441,6 +491,7 @@ ALL_PINS = [pin_parameter_counts, pin_cache_sizes, pin_rmsnorm, pin_rope, pin_si
             pin_softmax_and_mix, pin_causality, pin_brute_prefill, pin_brute_decode_full,
             pin_brute_decode_latent, pin_brute_block, pin_absorbed_equals_unabsorbed,
             pin_prefill_last_row_equals_decode, pin_block_residual, pin_ragged_decode,
+            pin_brute_bias, pin_bias_special_cases,
             lambda: pin_brute_prefill(MICRO_EQ), lambda: pin_brute_decode_latent(MICRO_EQ),
             lambda: pin_absorbed_equals_unabsorbed(MICRO, 15)]
 
@@ -514,6 +565,8 @@ MUTATIONS = {
     "absorbed_query_uses_value_rows": ("absorbed_query", _absq_value_rows),
     "absorbed_output_uses_key_rows": ("absorbed_output", _abso_key_rows),
     "mla_has_bias_terms": ("weight_shapes", lambda dims: {**_shapes(dims), "b_o": (dims.d_model,)}),
+    "attention_bias_ignored": ("_bias", lambda b, dtype: 0.0),
+    "attention_bias_subtracted": ("_bias", lambda b, dtype: 0.0 if b is None else -np.asarray(b, dtype)),
 }
 
 
