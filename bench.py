@@ -11,8 +11,9 @@ projections, flash attention, o_proj) on inputs already resident in HBM.
 Secondary lines (same JSON object, key "secondary") time the full-cache
 decode (B=64, P=1000), the absorbed latent-cache decode (B=32, P=8192), the
 same over a ragged batch (B=32, per-sequence positions uniform in
-[0, 8192]) and the dense block (B=1, T=4096) with the same weights, against
-the HBM or MFMA roofline.  The CPU baseline times the float32 oracle on the host cores.
+[0, 8192]), a chunked prefill (512 new tokens after 3584 cached positions,
+full and latent cache forms) and the dense block (B=1, T=4096) with the same
+weights, against the HBM or MFMA roofline.  The CPU baseline times the float32 oracle on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -270,6 +271,45 @@ def bench_decode_latent_ragged(torch, mla, dev, d, w, steps, warmup, flush, B=32
             "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None}
 
 
+def chunk_flops(B, T, P0, k=KIMI):
+    """Algorithmic FLOPs of a chunked-prefill step: the projections of the T
+    new tokens and causal attention of token t over P0 + t + 1 keys."""
+    H = k["n_heads"]
+    dqk = k["qk_nope_dim"] + k["qk_rope_dim"]
+    proj = 2.0 * B * T * (mla_param_count(k) - k["q_lora_rank"] - k["kv_lora_rank"])
+    keys = T * P0 + T * (T + 1) / 2
+    return proj + 2.0 * B * H * keys * (dqk + k["v_head_dim"])
+
+
+def bench_prefill_chunk(torch, mla, dev, d, w, steps, warmup, form, B=1, T=512, P0=3584):
+    """Chunked prefill: T new tokens at positions P0 .. P0+T-1 against a cache
+    of P0 positions (N(0,1) history), full or latent cache form."""
+    k = KIMI
+    L_cap = P0 + T
+    g = torch.Generator(device=dev)
+    g.manual_seed(1007)
+    H = k["n_heads"]
+    x = torch.randn(B, T, k["d_model"], generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    rope = mla.mla_rope_table(L_cap, 64, 10000.0, dev)
+    out = torch.empty_like(x)
+    ws = torch.empty(mla.chunk_workspace_size(d, B, T, L_cap), dtype=torch.uint8, device=dev)
+    if form == "full":
+        kc = torch.randn(B, H, L_cap, 192, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        vc = torch.randn(B, H, L_cap, 128, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        fn = lambda: mla.mla_prefill_chunk_fullcache(d, w, x, P0, kc, vc, rope, out=out, workspace=ws)  # noqa: E731
+    else:
+        cc = torch.randn(B, L_cap, 576, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        fn = lambda: mla.mla_prefill_chunk_latentcache(d, w, x, P0, cc, rope, out=out, workspace=ws)  # noqa: E731
+    warm(torch, fn, warmup)
+    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps)
+    flops = chunk_flops(B, T, P0)
+    return {"workload": f"chunked prefill, {form} cache, bf16, B={B}, {T} new tokens at positions "
+                        f"{P0}..{P0 + T - 1}",
+            "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev,
+            "tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+            "gflop": flops / 1e9, "kernels": kern}
+
+
 def bench_block(torch, mla, dev, d, w, steps, warmup, B=1, T=4096):
     k = KIMI
     g = torch.Generator(device=dev)
@@ -333,7 +373,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode_full", "decode_latent", "decode_latent_ragged",
-                                       "block", "copy"])
+                                       "chunk_full", "chunk_latent", "block", "copy"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -372,6 +412,8 @@ def main():
               "decode_latent": lambda: bench_decode_latent(torch, mla, dev, d, w, args.steps, args.warmup, flush),
               "decode_latent_ragged": lambda: bench_decode_latent_ragged(torch, mla, dev, d, w, args.steps,
                                                                          args.warmup, flush),
+              "chunk_full": lambda: bench_prefill_chunk(torch, mla, dev, d, w, args.steps, args.warmup, "full"),
+              "chunk_latent": lambda: bench_prefill_chunk(torch, mla, dev, d, w, args.steps, args.warmup, "latent"),
               "block": lambda: bench_block(torch, mla, dev, d, w, args.steps, args.warmup)}[args.only]
         print(json.dumps(fn()))
         return
@@ -406,6 +448,8 @@ def main():
         for name, fn in (("decode_fullcache", lambda: bench_decode_full(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
                          ("decode_latentcache", lambda: bench_decode_latent(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
                          ("decode_latentcache_ragged", lambda: bench_decode_latent_ragged(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
+                         ("prefill_chunk_fullcache", lambda: bench_prefill_chunk(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, "full")),
+                         ("prefill_chunk_latentcache", lambda: bench_prefill_chunk(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, "latent")),
                          ("dense_block", lambda: bench_block(torch, mla, dev, r["d"], r["w"], max(3, args.steps // 4), 2))):
             log(f"[bench] {name}")
             try:

@@ -84,6 +84,12 @@ def load():
                                               _P, _P, _P, _I, _P, _P, _SZ, _P]
     L.mla_decode_latentcache_ragged.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _P, _I, _I,
                                                 _P, _P, _P, _I, _P, _P, _SZ, _P]
+    L.mla_prefill_chunk_workspace_size.argtypes = [_DP, _I, _I, _I]
+    L.mla_prefill_chunk_workspace_size.restype = _SZ
+    L.mla_prefill_chunk_fullcache.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _I, _I, _I, _P, _P,
+                                              _P, _P, _I, _P, _P, _SZ, _P]
+    L.mla_prefill_chunk_latentcache.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _I, _I, _I, _P,
+                                                _P, _P, _I, _P, _P, _SZ, _P]
     L.dense_block_workspace_size.argtypes = [_DP, _I, _I]
     L.dense_block_workspace_size.restype = _SZ
     L.dense_block_fwd.argtypes = [_DP, ctypes.POINTER(BlockWeights), _P, _I, _I, _P, _P, _I, _P, _P,
@@ -98,7 +104,8 @@ def load():
     L.mla_last_error.restype = ctypes.c_char_p
     for name in ("mla_rope_table", "mla_prefill", "mla_decode_fullcache",
                  "mla_decode_latentcache", "mla_decode_fullcache_ragged",
-                 "mla_decode_latentcache_ragged", "dense_block_fwd"):
+                 "mla_decode_latentcache_ragged", "mla_prefill_chunk_fullcache",
+                 "mla_prefill_chunk_latentcache", "dense_block_fwd"):
         getattr(L, name).restype = _I
     _lib = L
     return L
@@ -350,6 +357,56 @@ def mla_decode_latentcache_ragged(d: Dims, w: dict, x, positions, P_max, latent_
     ws = _ws(decode_workspace_size(d, B, L_cap), dev, workspace)
     _check(L.mla_decode_latentcache_ragged(ctypes.byref(d), ctypes.byref(wt), ctypes.c_void_p(x.data_ptr()),
                                            B, pp, P_max, L_cap, lc, rc, rs, rows,
+                                           ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                           ws.numel(), _stream(dev)))
+    return out
+
+
+def chunk_workspace_size(d: Dims, B, T, L_cap):
+    return load().mla_prefill_chunk_workspace_size(ctypes.byref(d), B, T, L_cap)
+
+
+def mla_prefill_chunk_fullcache(d: Dims, w: dict, x, P0, k_cache, v_cache, rope, out=None, workspace=None):
+    """Chunked prefill with the full cache: x [B, T, d] holds the tokens at
+    positions P0 .. P0+T-1; cache slots 0 .. P0-1 are the history, slots
+    P0 .. P0+T-1 are written.  Returns out [B, T, d]."""
+    L = load()
+    dev = x.device
+    B, T = x.shape[0], x.shape[1]
+    _tensor(x, "x", (B, T, d.d_model), d.torch_dtype, dev)
+    L_cap = k_cache.shape[2]
+    kc = _tensor(k_cache, "k_cache", (B, d.n_heads, L_cap, d.qk_nope_dim + d.qk_rope_dim), d.torch_dtype, dev)
+    vc = _tensor(v_cache, "v_cache", (B, d.n_heads, L_cap, d.v_head_dim), d.torch_dtype, dev)
+    wt = _weights(d, w, dev)
+    rc, rs, rows = _rope(rope, int(P0) + T, d, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _tensor(out, "out", x.shape, d.torch_dtype, dev)
+    ws = _ws(chunk_workspace_size(d, B, T, L_cap), dev, workspace)
+    _check(L.mla_prefill_chunk_fullcache(ctypes.byref(d), ctypes.byref(wt), ctypes.c_void_p(x.data_ptr()),
+                                         B, T, int(P0), L_cap, kc, vc, rc, rs, rows,
+                                         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                         ws.numel(), _stream(dev)))
+    return out
+
+
+def mla_prefill_chunk_latentcache(d: Dims, w: dict, x, P0, latent_cache, rope, out=None, workspace=None):
+    """Chunked prefill with the latent cache [B, L_cap, kv_lora + d_rope]
+    (positions as in mla_prefill_chunk_fullcache).  Returns out [B, T, d]."""
+    L = load()
+    dev = x.device
+    B, T = x.shape[0], x.shape[1]
+    _tensor(x, "x", (B, T, d.d_model), d.torch_dtype, dev)
+    L_cap = latent_cache.shape[1]
+    lc = _tensor(latent_cache, "latent_cache", (B, L_cap, d.kv_lora_rank + d.qk_rope_dim), d.torch_dtype, dev)
+    wt = _weights(d, w, dev)
+    rc, rs, rows = _rope(rope, int(P0) + T, d, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _tensor(out, "out", x.shape, d.torch_dtype, dev)
+    ws = _ws(chunk_workspace_size(d, B, T, L_cap), dev, workspace)
+    _check(L.mla_prefill_chunk_latentcache(ctypes.byref(d), ctypes.byref(wt), ctypes.c_void_p(x.data_ptr()),
+                                           B, T, int(P0), L_cap, lc, rc, rs, rows,
                                            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
                                            ws.numel(), _stream(dev)))
     return out

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
   const int qt = nqt - 1 - (int)(blockIdx.x / HB);  // longest query tiles first
   const int rem = blockIdx.x % HB;
   const int h = rem % p.H, b = rem / p.H;
-  const int q0 = qt * PP_BQ;
+  const int q0 = qt * PP_BQ;  // first query row of the tile (query positions are P0 + row)
   const long rowbase = (long)b * p.T;
   const long HS = p.H;
 
@@ -98,14 +98,16 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
 #pragma unroll
     for (int s = 0; s < 12; ++s) {
       u32x4 v = *(const u32x4*)(qp + 16 * s);
-      if (s >= 8) v = rope8_bf16(v, p.rcos, p.rsin, qrow, 32, (16 * s + 8 * lg - 128) / 2);
+      if (s >= 8) v = rope8_bf16(v, p.rcos, p.rsin, p.P0 + qrow, 32, (16 * s + 8 * lg - 128) / 2);
       qf[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  const int qlast = min(q0 + PP_BQ - 1, p.T - 1);
+  // positions: this lane's query and the wave's first / last query
+  const int qlast = p.P0 + min(q0 + PP_BQ - 1, p.T - 1);
   const int n_kv = qlast / 64 + 1;
-  const int qi = q0 + 32 * w + lr;
-  const int wq_first = q0 + 32 * w, wq_last = wq_first + 31;
+  const int qrow_l = q0 + 32 * w + lr;  // query row in the chunk
+  const int qi = p.P0 + qrow_l;
+  const int wq_first = p.P0 + q0 + 32 * w, wq_last = wq_first + 31;
 
   // ---- loaders.  Wave w moves content-key rows 8 w .. 8 w + 7 (two DMAs of
   // 4 rows x 256 B), rotary-key rows 8 w .. 8 w + 7 (one DMA of 8 rows x
@@ -117,30 +119,33 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
   // chunks per half-wave, and row & 15 would put all four rows on the same 4
   // chunk positions (a 4-way bank conflict), while 4 (row & 3) gives each
   // row its own group of 4.
-  const int KSTR = (int)(HS * 512);  // bytes between consecutive keys in kv
+  // source rows: key j of this (sequence, head) at byte j * *_kb of its base
+  const int nkeys = p.P0 + p.T;
   int kc_vo[2], v_vo[2], kr_vo;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 4 * (2 * w + i) + (lane >> 4);
-    kc_vo[i] = row * KSTR + 16 * ((lane & 15) ^ (row & 15));
-    v_vo[i] = row * KSTR + 256 + 16 * ((lane & 15) ^ pp_vswz(row));
+    kc_vo[i] = row * p.kc_kb + 16 * ((lane & 15) ^ (row & 15));
+    v_vo[i] = row * p.v_kb + 16 * ((lane & 15) ^ pp_vswz(row));
   }
   {
     const int row = 8 * w + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
-    kr_vo = row * 128 + 16 * c;
+    kr_vo = row * p.kr_kb + 16 * c;
   }
-  const u32x4 rkv = pp_rsrc(p.kv + (rowbase * HS + h) * 256, (long)p.T * KSTR);
-  const u32x4 rkr = pp_rsrc(p.kr + rowbase * 64, (long)p.T * 128);
+  // keys past the last one read as zero (buffer range); causality masks them
+  const u32x4 rkc = pp_rsrc(p.kc + b * p.kc_b + h * p.kc_h, (long)nkeys * p.kc_kb);
+  const u32x4 rkr = pp_rsrc(p.kr2 + b * p.kr_b + h * p.kr_h, (long)nkeys * p.kr_kb);
+  const u32x4 rvv = pp_rsrc(p.vv + b * p.v_b + h * p.v_h, (long)nkeys * p.v_kb);
 #define PP_ISSUE(tt)                                                                         \
   do {                                                                                       \
     const unsigned sb_ = lds_base + ((tt) % PP_NST) * PP_STG;                                \
     const int kk_ = 64 * (tt);                                                               \
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                            \
-      pp_dma16(sb_ + 1024 * (2 * w + i), kc_vo[i] + kk_ * KSTR, rkv);                        \
-    pp_dma16(sb_ + PP_KC + 1024 * w, kr_vo + kk_ * 128, rkr);                                \
+      pp_dma16(sb_ + 1024 * (2 * w + i), kc_vo[i] + kk_ * p.kc_kb, rkc);                     \
+    pp_dma16(sb_ + PP_KC + 1024 * w, kr_vo + kk_ * p.kr_kb, rkr);                            \
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                            \
-      pp_dma16(sb_ + PP_KC + PP_KR + 1024 * (2 * w + i), v_vo[i] + kk_ * KSTR, rkv);         \
+      pp_dma16(sb_ + PP_KC + PP_KR + 1024 * (2 * w + i), v_vo[i] + kk_ * p.v_kb, rvv);       \
   } while (0)
 
   // ---- fragment offsets inside a stage (tile-invariant).
@@ -316,9 +321,9 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
 #undef PP_VREAD
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (qi < p.T) {
+  if (qrow_l < p.T) {
     const float inv = 1.f / l_tot;
-    bf16_t* op = p.out + (rowbase + qi) * (HS * 128) + (long)h * 128 + 4 * lg;
+    bf16_t* op = p.out + (rowbase + qrow_l) * (HS * 128) + (long)h * 128 + 4 * lg;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -331,7 +336,20 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
   }
 }
 
-bool flash_pp_ok(const FlashParams& p) { return (long)(p.T + 64) * p.H * 512 < 0x7fffffffL; }
+void flash_set_prefill_layout(FlashParams& p) {
+  const long kvrow = (long)p.H * 256;  // elements per token row of kv
+  p.kc = p.kv;       p.kc_b = (long)p.T * kvrow; p.kc_h = 256; p.kc_kb = (int)(kvrow * 2);
+  p.vv = p.kv + 128; p.v_b = p.kc_b;             p.v_h = 256;  p.v_kb = p.kc_kb;
+  p.kr2 = p.kr;      p.kr_b = (long)p.T * 64;    p.kr_h = 0;   p.kr_kb = 128;
+  p.P0 = 0;
+}
+
+bool flash_pp_ok(const FlashParams& p) {
+  // per-key byte offsets (64 keys past the last tile included) stay below 2^31
+  const long nk = (long)p.P0 + p.T + 64;
+  return p.P0 >= 0 && nk * p.kc_kb < 0x7fffffffL && nk * p.kr_kb < 0x7fffffffL &&
+         nk * p.v_kb < 0x7fffffffL && p.kc_kb % 16 == 0 && p.kr_kb % 16 == 0 && p.v_kb % 16 == 0;
+}
 
 hipError_t flash_prefill_pp_bf16(const FlashParams& p, hipStream_t s) {
   if (!flash_pp_ok(p)) return hipErrorInvalidValue;

@@ -167,9 +167,21 @@ struct FlashParams {
   const float* rcos; const float* rsin;  // RoPE table [>= T][32]
   int B, T, H;
   float scale_log2;  // softmax scale * log2(e)
+  // Key/value sources of the ping-pong kernel (flash_pp.hip), per sequence b
+  // and head h: key j's content part (128) at kc + b kc_b + h kc_h (elements)
+  // + j kc_kb (bytes), its rotary part (64) likewise from kr2, its value (128)
+  // from vv.  Keys 0 .. P0 + T - 1 exist; query t sits at position P0 + t
+  // and sees keys j <= P0 + t.  flash_set_prefill_layout() fills these for a
+  // plain prefill (kv / kr above, P0 = 0).
+  const bf16_t* kc;  long kc_b, kc_h; int kc_kb;
+  const bf16_t* kr2; long kr_b, kr_h; int kr_kb;
+  const bf16_t* vv;  long v_b, v_h;   int v_kb;
+  int P0;
 };
 hipError_t flash_prefill_bf16(const FlashParams& p, hipStream_t s);
-// ping-pong form (flash_pp.hip); needs (T + 64) * H * 512 < 2^31
+// the key/value source fields for the prefill layout (kv [B*T][H][256], kr [B*T][64])
+void flash_set_prefill_layout(FlashParams& p);
+// ping-pong form (flash_pp.hip); needs its byte offsets below 2^31
 bool flash_pp_ok(const FlashParams& p);
 hipError_t flash_prefill_pp_bf16(const FlashParams& p, hipStream_t s);
 

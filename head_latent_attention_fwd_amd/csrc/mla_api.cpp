@@ -210,8 +210,9 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
   b->o = c.take((size_t)M * H * d->v_head_dim * es);
   b->upart = b->ukvpart = nullptr;
   b->upart_floats = b->ukvpart_floats = 0;
-  if (splitk && d->dtype == MLA_BF16) {
-    // partials of the q and kv up-projections when M is small (decode)
+  if (d->dtype == MLA_BF16 && (splitk || M <= 64)) {
+    // partials of the q and kv up-projections when M is small (decode, or a
+    // prefill / chunk of at most 64 rows: the small-M products split K)
     const int shapes[2][2] = {{H * dqk, d->q_lora_rank},
                               {H * (d->qk_nope_dim + d->v_head_dim), d->kv_lora_rank}};
     for (int i = 0; i < 2; ++i) {
@@ -466,6 +467,7 @@ int prefill_core(const mla_dims* d, const mla_weights* w, const void* x, int B, 
     f.q = (const bf16_t*)b.q; f.kv = (const bf16_t*)b.kv; f.kr = (const bf16_t*)b.kr;
     f.out = (bf16_t*)b.o; f.B = B; f.T = T; f.H = H; f.rcos = rc; f.rsin = rs;
     f.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    flash_set_prefill_layout(f);
     if (flash_pp_ok(f)) LAUNCH("flash_prefill", flash_prefill_pp_bf16(f, st));
     else LAUNCH("flash_prefill", flash_prefill_bf16(f, st));
   } else {
@@ -683,6 +685,174 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int B, i
   prefill_layout(d, B, T, ws, &pl);
   return prefill_core(d, w, x, B, T, rc, rs, out, nullptr, k_cache, v_cache, latent_cache, L_cap,
                       pl, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------ chunked prefill
+// T new tokens per sequence at positions P0 .. P0+T-1 against a cache whose
+// slots 0 .. P0-1 hold the history.  Workspace: the projections of the
+// B*T new rows, plus (latent form) the per-head keys/values expanded from
+// the cache rows 0 .. L_cap-1 (bf16) or the absorbed query and latent output
+// (float32).
+struct ChunkPlan {
+  ProjBufs pb;
+  void* kv_exp;  // bf16 latent form: [B][L_cap][H*(dn+dv)]
+  void* q_abs;   // float32 latent form: [B*T][H][kv_lora]
+  void* o_lat;   // float32 latent form: [B*T][H][kv_lora]
+};
+
+static size_t chunk_layout(const mla_dims* d, int B, int T, int L_cap, int form, void* ws, ChunkPlan* pl) {
+  Carver c(ws);
+  const size_t es = esize(d);
+  const int H = d->n_heads;
+  carve_proj(c, d, B * T, form == 0, false, &pl->pb);
+  pl->kv_exp = pl->q_abs = pl->o_lat = nullptr;
+  if (form == 1 && d->dtype == MLA_BF16)
+    pl->kv_exp = c.take((size_t)B * L_cap * H * (d->qk_nope_dim + d->v_head_dim) * es);
+  if (form == 1 && d->dtype == MLA_F32) {
+    pl->q_abs = c.take((size_t)B * T * H * d->kv_lora_rank * es);
+    pl->o_lat = c.take((size_t)B * T * H * d->kv_lora_rank * es);
+  }
+  return c.off + 256;
+}
+
+static int chunk_impl(const mla_dims* d, const mla_weights* w, const void* x, int B, int T, int P0,
+                      int L_cap, int form, void* k_cache, void* v_cache, void* latent_cache,
+               const float* rc, const float* rs, int rope_rows, void* out, void* ws,
+               size_t ws_bytes, void* stream) {
+  int r = check_dims(d, false);
+  if (r) return r;
+  if ((r = check_weights(w))) return r;
+  if (!x || !out) return fail(MLA_ERR_NULL, "x or out is NULL");
+  if (!ws) return fail(MLA_ERR_NULL, "workspace is NULL");
+  if (form == 0 && (!k_cache || !v_cache)) return fail(MLA_ERR_NULL, "k_cache/v_cache is NULL");
+  if (form == 1 && !latent_cache) return fail(MLA_ERR_NULL, "latent_cache is NULL");
+  if (B <= 0 || T <= 0 || L_cap <= 0) return fail(MLA_ERR_SHAPE, "B, T and L_cap must be positive");
+  if (P0 < 0 || (long)P0 + T > L_cap)
+    return fail(MLA_ERR_SHAPE, "chunk positions %d..%ld outside the cache [0, %d)", P0, (long)P0 + T - 1, L_cap);
+  if ((r = check_rope(rc, rs, rope_rows, P0 + T))) return r;
+  const long M = (long)B * T;
+  const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
+  const int kl = d->kv_lora_rank, dqk = dn + dr;
+  if ((r = check_i32(M * d->d_model, "x")) || (r = check_i32(M * H * 256, "kv")) ||
+      (r = check_i32((long)L_cap * H * (dn + dv), "expanded cache rows")))
+    return r;
+  ChunkPlan pl;
+  size_t need = chunk_layout(d, B, T, L_cap, form, nullptr, &pl);
+  if (ws_bytes < need) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  chunk_layout(d, B, T, L_cap, form, ws, &pl);
+  hipStream_t st = (hipStream_t)stream;
+  const ProjBufs& b = pl.pb;
+  // projections of the new rows at positions P0 + t; the latent form's cache
+  // entries are written by the latent-norm kernel
+  if ((r = run_projections(d, w, x, (int)M, T, P0, rc, rs, b, form == 1 ? latent_cache : nullptr,
+                           L_cap, st)))
+    return r;
+  const int Lk = P0 + T;  // keys per sequence
+  if (d->dtype == MLA_BF16) {
+    FlashParams f;
+    memset(&f, 0, sizeof f);
+    f.q = (const bf16_t*)b.q; f.out = (bf16_t*)b.o; f.B = B; f.T = T; f.H = H;
+    f.rcos = rc; f.rsin = rs; f.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    f.P0 = P0;
+    if (form == 0) {
+      LAUNCH("scatter_cache", scatter_full_cache<bf16_t>((const bf16_t*)b.kv, (const bf16_t*)b.kr,
+                                                         (bf16_t*)k_cache, (bf16_t*)v_cache, B, T, P0,
+                                                         L_cap, H, dn, dr, dv, st));
+      // keys and values straight from the cache rows [K^C | k^R] and V
+      f.kc = (const bf16_t*)k_cache;      f.kc_b = (long)H * L_cap * dqk; f.kc_h = (long)L_cap * dqk; f.kc_kb = dqk * 2;
+      f.kr2 = (const bf16_t*)k_cache + dn; f.kr_b = f.kc_b; f.kr_h = f.kc_h; f.kr_kb = dqk * 2;
+      f.vv = (const bf16_t*)v_cache;      f.v_b = (long)H * L_cap * dv; f.v_h = (long)L_cap * dv; f.v_kb = dv * 2;
+    } else {
+      // per-head keys/values of cache rows 0 .. Lk-1: [K^C | V] = c^KV-hat W_UKV^T
+      // (the prefill's kv product, applied to the cached latents)
+      GemmParams g = gp_base();
+      g.A = (const bf16_t*)latent_cache; g.lda = kl + dr; g.sA = (long)L_cap * (kl + dr);
+      g.B = (const bf16_t*)w->w_ukv; g.ldb = kl; g.sB = 0;
+      g.C = pl.kv_exp; g.ldc = (long)H * (dn + dv); g.sC = (long)L_cap * H * (dn + dv);
+      g.M = Lk; g.N = H * (dn + dv); g.K = kl; g.batch = B;
+      LAUNCH("gemm_kv_expand", gemm_bf16(g, EPI_BF16, -1, st));
+      const bf16_t* kv = (const bf16_t*)pl.kv_exp;
+      const long row = (long)H * (dn + dv);
+      f.kc = kv;       f.kc_b = (long)L_cap * row; f.kc_h = dn + dv; f.kc_kb = (int)(row * 2);
+      f.vv = kv + dn;  f.v_b = f.kc_b;             f.v_h = dn + dv; f.v_kb = (int)(row * 2);
+      f.kr2 = (const bf16_t*)latent_cache + kl; f.kr_b = (long)L_cap * (kl + dr); f.kr_h = 0;
+      f.kr_kb = (kl + dr) * 2;
+    }
+    if (!flash_pp_ok(f))
+      return fail(MLA_ERR_UNSUPPORTED, "chunked prefill: cache rows too long for 32-bit offsets");
+    LAUNCH("flash_prefill", flash_prefill_pp_bf16(f, st));
+  } else if (form == 0) {
+    LAUNCH("scatter_cache", scatter_full_cache<float>((const float*)b.kv, (const float*)b.kr, (float*)k_cache,
+                                                      (float*)v_cache, B, T, P0, L_cap, H, dn, dr, dv, st));
+    AttnGenericParams a;
+    memset(&a, 0, sizeof a);
+    a.q_nope = (const float*)b.q; a.q_row = (long)H * dqk; a.q_head = dqk;
+    a.q_rope = (const float*)b.q + dn; a.qr_row = (long)H * dqk; a.qr_head = dqk;
+    a.k_nope = (const float*)k_cache; a.kn_b = (long)H * L_cap * dqk; a.kn_j = dqk; a.kn_h = (long)L_cap * dqk;
+    a.k_rope = (const float*)k_cache + dn; a.kr_b = a.kn_b; a.kr_j = dqk; a.kr_h = a.kn_h;
+    a.v = (const float*)v_cache; a.v_b = (long)H * L_cap * dv; a.v_j = dv; a.v_h = (long)L_cap * dv;
+    a.out = (float*)b.o; a.o_row = (long)H * dv; a.o_head = dv;
+    a.B = B; a.Tq = T; a.Tk = Lk; a.H = H; a.d_nope = dn; a.d_rope = dr; a.d_v = dv;
+    a.causal_offset = P0; a.scale = d->softmax_scale;
+    LAUNCH("attn_generic", attn_generic_f32(a, st));
+  } else {
+    // absorbed form over the latent cache, T queries per sequence
+    GemmF32Params g;
+    memset(&g, 0, sizeof g);
+    g.A = (const float*)b.q; g.lda = (long)H * dqk;
+    g.B = (const float*)w->w_ukv; g.ldb = kl; g.b_is_nk = 0;
+    g.C = (float*)pl.q_abs; g.ldc = (long)H * kl;
+    g.M = (int)M; g.N = kl; g.K = dn; g.batch = H;
+    g.sA = dqk; g.sB = (long)(dn + dv) * kl; g.sC = kl;
+    LAUNCH("absorb_q", gemm_f32(g, st));
+    AttnGenericParams a;
+    memset(&a, 0, sizeof a);
+    const long cw = kl + dr;
+    a.q_nope = (const float*)pl.q_abs; a.q_row = (long)H * kl; a.q_head = kl;
+    a.q_rope = (const float*)b.q + dn; a.qr_row = (long)H * dqk; a.qr_head = dqk;
+    a.k_nope = (const float*)latent_cache; a.kn_b = (long)L_cap * cw; a.kn_j = cw; a.kn_h = 0;
+    a.k_rope = (const float*)latent_cache + kl; a.kr_b = a.kn_b; a.kr_j = cw; a.kr_h = 0;
+    a.v = (const float*)latent_cache; a.v_b = a.kn_b; a.v_j = cw; a.v_h = 0;
+    a.out = (float*)pl.o_lat; a.o_row = (long)H * kl; a.o_head = kl;
+    a.B = B; a.Tq = T; a.Tk = Lk; a.H = H; a.d_nope = kl; a.d_rope = dr; a.d_v = kl;
+    a.causal_offset = P0; a.scale = d->softmax_scale;
+    LAUNCH("attn_generic", attn_generic_f32(a, st));
+    GemmF32Params u;
+    memset(&u, 0, sizeof u);
+    u.A = (const float*)pl.o_lat; u.lda = (long)H * kl;
+    u.B = (const float*)w->w_ukv + (long)dn * kl; u.ldb = kl; u.b_is_nk = 1;
+    u.C = (float*)b.o; u.ldc = (long)H * dv;
+    u.M = (int)M; u.N = dv; u.K = kl; u.batch = H;
+    u.sA = kl; u.sB = (long)(dn + dv) * kl; u.sC = dv;
+    LAUNCH("gemm_uv", gemm_f32(u, st));
+  }
+  return run_oproj(d, w->w_o, w->b_o, b.o, (int)M, nullptr, out, nullptr, 0, 1, st);
+}
+
+size_t mla_prefill_chunk_workspace_size(const mla_dims* d, int B, int T, int L_cap) {
+  if (check_dims(d, false) || B <= 0 || T <= 0 || L_cap <= 0) return 0;
+  ChunkPlan a, b;
+  const size_t s0 = chunk_layout(d, B, T, L_cap, 0, nullptr, &a);
+  const size_t s1 = chunk_layout(d, B, T, L_cap, 1, nullptr, &b);
+  return s0 > s1 ? s0 : s1;
+}
+
+int mla_prefill_chunk_fullcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int T,
+                                int P0, int L_cap, void* k_cache, void* v_cache, const float* rc,
+                                const float* rs, int rope_rows, void* out, void* ws, size_t ws_bytes,
+                                void* stream) {
+  g_err[0] = 0;
+  return chunk_impl(d, w, x, B, T, P0, L_cap, 0, k_cache, v_cache, nullptr, rc, rs, rope_rows, out, ws,
+                    ws_bytes, stream);
+}
+
+int mla_prefill_chunk_latentcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int T,
+                                  int P0, int L_cap, void* latent_cache, const float* rc,
+                                  const float* rs, int rope_rows, void* out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  g_err[0] = 0;
+  return chunk_impl(d, w, x, B, T, P0, L_cap, 1, nullptr, nullptr, latent_cache, rc, rs, rope_rows, out,
+                    ws, ws_bytes, stream);
 }
 
 size_t mla_decode_workspace_size(const mla_dims* d, int B, int L_cap) {

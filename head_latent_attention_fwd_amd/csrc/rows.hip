@@ -338,10 +338,45 @@ __global__ void scatter_full_cache_kernel(const T* __restrict__ kv, const T* __r
   else vc[base * dv + (c - dn - dr)] = src[dn + (c - dn - dr)];
 }
 
+// bf16 form: one 16-byte chunk (8 features) per thread; chunk c of (row m,
+// head h) is K^C (c < dn/8), k^R (next dr/8) or V (last dv/8).
+__global__ void scatter_full_cache_bf16x8_kernel(const bf16_t* __restrict__ kv,
+                                                 const bf16_t* __restrict__ kr, bf16_t* __restrict__ kc,
+                                                 bf16_t* __restrict__ vc, int T_, int pos0, int L_cap,
+                                                 int H, int dn, int dr, int dv, long total,
+                                                 const int* __restrict__ seq_pos, int pos_max) {
+  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int W8 = (dn + dr + dv) / 8;
+  const int c = (int)(e % W8);
+  const int h = (int)((e / W8) % H);
+  const long m = e / ((long)W8 * H);
+  const long b = m / T_;
+  const int slot = seq_pos ? seq_position(seq_pos, (int)b, 0, pos_max) : (int)(m % T_) + pos0;
+  const long base = (b * H + h) * L_cap + slot;
+  const bf16_t* src = kv + (m * H + h) * (dn + dv);
+  const int f = 8 * c;
+  if (f < dn) *(u32x4*)(kc + base * (dn + dr) + f) = *(const u32x4*)(src + f);
+  else if (f < dn + dr) *(u32x4*)(kc + base * (dn + dr) + f) = *(const u32x4*)(kr + m * dr + (f - dn));
+  else *(u32x4*)(vc + base * dv + (f - dn - dr)) = *(const u32x4*)(src + dn + (f - dn - dr));
+}
+
 template <typename T>
 hipError_t scatter_full_cache(const T* kv, const T* kr, T* k_cache, T* v_cache, int Bn, int T_,
                               int pos0, int L_cap, int H, int d_nope, int d_rope, int d_v,
                               hipStream_t s, const int* seq_pos, int pos_max) {
+  if constexpr (sizeof(T) == 2) {
+    const bool vec = d_nope % 8 == 0 && d_rope % 8 == 0 && d_v % 8 == 0 &&
+                     ((uintptr_t)kv | (uintptr_t)kr | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16 == 0;
+    if (vec) {
+      const long total8 = (long)Bn * T_ * H * ((d_nope + d_rope + d_v) / 8);
+      if (total8 == 0) return hipSuccess;
+      hipLaunchKernelGGL(scatter_full_cache_bf16x8_kernel, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0,
+                         s, (const bf16_t*)kv, (const bf16_t*)kr, (bf16_t*)k_cache, (bf16_t*)v_cache, T_, pos0,
+                         L_cap, H, d_nope, d_rope, d_v, total8, seq_pos, pos_max);
+      return hipGetLastError();
+    }
+  }
   long total = (long)Bn * T_ * H * (d_nope + d_rope + d_v);
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(scatter_full_cache_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256),

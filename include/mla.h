@@ -184,6 +184,30 @@ int mla_decode_latentcache_ragged(const mla_dims *dims, const mla_weights *w, co
                                   int rope_rows, void *out, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* ---- Chunked prefill (both cache forms) ----
+ * T new tokens per sequence at positions P0 .. P0+T-1 (x [B, T, d] ->
+ * out [B, T, d]) against a cache whose slots 0 .. P0-1 hold the history:
+ * the tokens' entries are written to slots P0 .. P0+T-1, and the token at
+ * position P0 + t attends to keys 0 .. P0 + t (the causal mask of [MP]'s
+ * code excerpt, shifted by the cached length; its size checks allow a query
+ * length above 1 against a longer key length).  P0 = 0 is a prefill with
+ * cache outputs; T = 1 is a decode step at P = P0.
+ *   k_cache/v_cache or latent_cache: as for the decode forms, [B, ...,
+ *   L_cap, ...]; requires P0 >= 0, P0 + T <= L_cap, rope_rows >= P0 + T.
+ * The latent form (bf16) expands the per-head keys and values of cache rows
+ * 0 .. P0+T-1 from the cached latents into the workspace (the unabsorbed
+ * form suits many queries per sequence); the float32 latent form attends in
+ * absorbed form.  The workspace size depends on L_cap. */
+size_t mla_prefill_chunk_workspace_size(const mla_dims *dims, int B, int T, int L_cap);
+int mla_prefill_chunk_fullcache(const mla_dims *dims, const mla_weights *w, const void *x, int B,
+                                int T, int P0, int L_cap, void *k_cache, void *v_cache,
+                                const float *rope_cos, const float *rope_sin, int rope_rows,
+                                void *out, void *workspace, size_t workspace_bytes, void *stream);
+int mla_prefill_chunk_latentcache(const mla_dims *dims, const mla_weights *w, const void *x, int B,
+                                  int T, int P0, int L_cap, void *latent_cache,
+                                  const float *rope_cos, const float *rope_sin, int rope_rows,
+                                  void *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---- Dense transformer block ([DB]) ----
  * out = x' + SwiGLU(RMSNorm(x'; g_ffn)), x' = x + MLA(RMSNorm(x; g_attn)),
  * SwiGLU(z) = (silu(z W1^T) * (z W3^T)) W2^T.  x, out [B, T, d]; causal

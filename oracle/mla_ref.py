@@ -467,6 +467,63 @@ def mla_decode_latentcache(dims: MLADims, w: MLAWeights, x_new: np.ndarray, P: i
     return out, cc
 
 
+def mla_prefill_chunk_fullcache(dims: MLADims, w: MLAWeights, x: np.ndarray, P0: int,
+                                k_cache: np.ndarray, v_cache: np.ndarray, dtype=np.float64):
+    """Chunked prefill with the full cache: the T tokens x [B, T, d] sit at
+    positions P0 .. P0+T-1 and slots 0 .. P0-1 of k_cache [B,H,L_cap,dqk] /
+    v_cache [B,H,L_cap,dv] hold the history.  The tokens' keys and values go
+    to slots P0 .. P0+T-1 (the cache update of [MP]'s code excerpt); token t
+    attends over keys 0 .. P0+t (its causal mask, [T, P0+T]), each head reading
+    its own key rows as stored.  Returns (out [B, T, d], k_cache', v_cache')."""
+    B, T, _ = x.shape
+    H, dv = dims.n_heads, dims.v_head_dim
+    pos = P0 + np.arange(T)
+    p = mla_project(dims, w, x, pos, dtype)
+    K_new, V_new = full_cache_entries(dims, p)                        # [B,H,T,*]
+    kc = _f(k_cache, dtype).copy()
+    vc = _f(v_cache, dtype).copy()
+    kc[:, :, P0:P0 + T] = K_new
+    vc[:, :, P0:P0 + T] = V_new
+    L = P0 + T
+    masked = np.arange(L)[None, :] > pos[:, None]                    # [T, L]
+    o = np.empty((B, T, H, dv), dtype=dtype)
+    for b in range(B):
+        for h in range(H):
+            Q = np.concatenate([p["q_nope"][b, :, h], p["q_rope"][b, :, h]], axis=-1)   # [T, dqk]
+            S = np.where(masked, -np.inf, (Q @ kc[b, h, :L].T) * dims.softmax_scale)
+            E = np.exp(S - np.max(S, axis=-1, keepdims=True))
+            o[b, :, h] = (E / np.sum(E, axis=-1, keepdims=True)) @ vc[b, h, :L]
+    out = _merge_heads(o) @ _f(w.w_o, dtype).T + _bias(w.b_o, dtype)
+    return out, kc, vc
+
+
+def mla_prefill_chunk_latentcache(dims: MLADims, w: MLAWeights, x: np.ndarray, P0: int,
+                                  latent_cache: np.ndarray, dtype=np.float64):
+    """Chunked prefill with the latent cache [B, L_cap, kv_lora + dr], in
+    absorbed form (as mla_decode_latentcache, with T queries at positions
+    P0 .. P0+T-1 and the causal mask of the full-cache form).
+    Returns (out [B, T, d], latent_cache')."""
+    B, T, _ = x.shape
+    r = dims.kv_lora_rank
+    pos = P0 + np.arange(T)
+    p = mla_project(dims, w, x, pos, dtype)
+    cc = _f(latent_cache, dtype).copy()
+    cc[:, P0:P0 + T] = latent_cache_entries(dims, p)
+    L = P0 + T
+    masked = (np.arange(L)[None, :] > pos[:, None])[:, None, :]     # [T, 1, L]
+    q_t = absorbed_query(dims, w, p["q_nope"], dtype)               # [B,T,H,r]
+    o_lat = np.empty((B, T, dims.n_heads, r), dtype=dtype)
+    for b in range(B):
+        C, KR = cc[b, :L, :r], cc[b, :L, r:]
+        S = (q_t[b] @ C.T + p["q_rope"][b] @ KR.T) * dims.softmax_scale    # [T,H,L]
+        S = np.where(masked, -np.inf, S)
+        E = np.exp(S - np.max(S, axis=-1, keepdims=True))
+        o_lat[b] = (E / np.sum(E, axis=-1, keepdims=True)) @ C
+    o = absorbed_output(dims, w, o_lat, dtype)                       # [B,T,H,dv]
+    out = _merge_heads(o) @ _f(w.w_o, dtype).T + _bias(w.b_o, dtype)
+    return out, cc
+
+
 def mla_decode_fullcache_ragged(dims: MLADims, w: MLAWeights, x_new: np.ndarray, positions,
                                 k_cache: np.ndarray, v_cache: np.ndarray, dtype=np.float64):
     """Decode over a ragged batch with the full cache: sequence b's new token

@@ -44,6 +44,7 @@ def _rope(od, n):
     ("tiny_ragged", ref.TINY, 2, 37, "f32", 7),
     ("kimi_narrow_bf16", KIMI_NARROW, 2, 200, "bf16", 11),
     ("kimi_bf16_T130", ref.KIMI_K2, 1, 130, "bf16", 12),
+    ("kimi_bf16_T20_small_rows", ref.KIMI_K2, 2, 20, "bf16", 13),
 ])
 def test_prefill(case):
     name, od, B, T, dt, seed = case
@@ -313,6 +314,48 @@ def test_ragged_decode_uniform_and_clamped(form):
     c2 = from_dev(run_r([P, 0, 3], P))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(c1, c2)
+
+
+# ---------------------------------------------------------- chunked prefill
+@pytest.mark.parametrize("case", [
+    ("tiny_f32", ref.TINY, 2, 5, 9, 16, "f32", 111),
+    ("kimi_narrow_bf16", KIMI_NARROW, 2, 100, 150, 300, "bf16", 112),
+    ("kimi_bf16", ref.KIMI_K2, 1, 300, 700, 1024, "bf16", 113),
+    ("kimi_bf16_P0_0", ref.KIMI_K2, 1, 130, 0, 200, "bf16", 114),
+    ("kimi_bf16_one_token", ref.KIMI_K2, 2, 1, 777, 800, "bf16", 115),
+])
+@pytest.mark.parametrize("form", ["full", "latent"])
+def test_prefill_chunk(case, form):
+    """T new tokens at positions P0 .. P0+T-1 against a cache holding
+    positions 0 .. P0-1: outputs and written cache slots against the oracle."""
+    name, od, B, T, P0, L_cap, dt, seed = case
+    log(f"[chunk {form} {name}] B={B} T={T} P0={P0} L_cap={L_cap} dtype={dt}")
+    bf = dt == "bf16"
+    x, w = synth.prefill_inputs(od, B, T, seed, bf16=bf)
+    d = dims_of(mla, od, dt)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    if form == "full":
+        _, _, kc, vc = synth.decode_full_inputs(od, B, max(P0, 1), L_cap, seed + 1, bf16=bf)
+        kd, vd = bits_to_dev(kc, dt, DEV), bits_to_dev(vc, dt, DEV)
+        got = mla.mla_prefill_chunk_fullcache(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), P0, kd, vd,
+                                              _rope(od, P0 + T))
+        torch.cuda.synchronize()
+        want, kc2, vc2 = ref.mla_prefill_chunk_fullcache(od, oracle_weights(w), x.astype(np.float64), P0,
+                                                         synth.as_f32(kc, bf).astype(np.float64),
+                                                         synth.as_f32(vc, bf).astype(np.float64))
+        assert_close(from_dev(got), want, tol, name)
+        assert_close(from_dev(kd)[:, :, P0:P0 + T], kc2[:, :, P0:P0 + T], tol, f"{name} key slots")
+        assert_close(from_dev(vd)[:, :, P0:P0 + T], vc2[:, :, P0:P0 + T], tol, f"{name} value slots")
+    else:
+        _, _, cc = synth.decode_latent_inputs(od, B, max(P0, 1), L_cap, seed + 1, bf16=bf)
+        cd = bits_to_dev(cc, dt, DEV)
+        got = mla.mla_prefill_chunk_latentcache(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), P0, cd,
+                                                _rope(od, P0 + T))
+        torch.cuda.synchronize()
+        want, cc2 = ref.mla_prefill_chunk_latentcache(od, oracle_weights(w), x.astype(np.float64), P0,
+                                                      synth.as_f32(cc, bf).astype(np.float64))
+        assert_close(from_dev(got), want, tol, name)
+        assert_close(from_dev(cd)[:, P0:P0 + T], cc2[:, P0:P0 + T], tol, f"{name} latent slots")
 
 
 # --------------------------------------------------- attention_bias variant

@@ -459,6 +459,46 @@ def test_ragged_decode():
     pin_ragged_decode(MICRO_EQ, 22)
 
 
+def pin_chunked_prefill(dims=MICRO, seed=41):
+    """Chunked prefill, both cache forms: a prefill of 7 tokens done as
+    chunks of 3 and 4 gives the prefill's output rows and cache entries; a
+    chunk at P0 = 0 is the prefill itself; a chunk of one token is the decode
+    step at P = P0."""
+    w = _mw(_bias_weights(dims, seed))
+    B, T1, T2, L_cap = 2, 3, 4, 9
+    x = _x((B, T1 + T2, dims.d_model), seed + 1)
+    want, p = ref.mla_prefill(dims, w, x, return_intermediates=True)
+    K, V = ref.full_cache_entries(dims, p)
+    C = ref.latent_cache_entries(dims, p)
+    kc = np.full((B, dims.n_heads, L_cap, dims.q_head_dim), 1e3)
+    vc = np.full((B, dims.n_heads, L_cap, dims.v_head_dim), -1e3)
+    cc = np.full((B, L_cap, dims.kv_lora_rank + dims.qk_rope_dim), 7.0)
+    o1, kc, vc = ref.mla_prefill_chunk_fullcache(dims, w, x[:, :T1], 0, kc, vc)
+    o2, kc, vc = ref.mla_prefill_chunk_fullcache(dims, w, x[:, T1:], T1, kc, vc)
+    l1, cc = ref.mla_prefill_chunk_latentcache(dims, w, x[:, :T1], 0, cc)
+    l2, cc = ref.mla_prefill_chunk_latentcache(dims, w, x[:, T1:], T1, cc)
+    for got in (np.concatenate([o1, o2], 1), np.concatenate([l1, l2], 1)):
+        _close(got, want, 1e-11)
+    _close(kc[:, :, :T1 + T2], K, 1e-12)
+    _close(vc[:, :, :T1 + T2], V, 1e-12)
+    _close(cc[:, :T1 + T2], C, 1e-12)
+    assert np.all(kc[:, :, T1 + T2:] == 1e3) and np.all(cc[:, T1 + T2:] == 7.0)
+    # one-token chunk = decode step, both forms
+    P0 = T1 + T2
+    xd = _x((B, 1, dims.d_model), seed + 2)
+    of, _, _ = ref.mla_prefill_chunk_fullcache(dims, w, xd, P0, kc, vc)
+    od, _, _ = ref.mla_decode_fullcache(dims, w, xd[:, 0], P0, kc, vc)
+    _close(of[:, 0], od, 1e-12)
+    ol, _ = ref.mla_prefill_chunk_latentcache(dims, w, xd, P0, cc)
+    odl, _ = ref.mla_decode_latentcache(dims, w, xd[:, 0], P0, cc)
+    _close(ol[:, 0], odl, 1e-12)
+
+
+def test_chunked_prefill():
+    pin_chunked_prefill()
+    pin_chunked_prefill(MICRO_EQ, 42)
+
+
 def pin_block_residual():
     """With o_proj and W2 zero the block is the identity on x (exactly)."""
     d = MICRO
@@ -491,7 +531,7 @@ ALL_PINS = [pin_parameter_counts, pin_cache_sizes, pin_rmsnorm, pin_rope, pin_si
             pin_softmax_and_mix, pin_causality, pin_brute_prefill, pin_brute_decode_full,
             pin_brute_decode_latent, pin_brute_block, pin_absorbed_equals_unabsorbed,
             pin_prefill_last_row_equals_decode, pin_block_residual, pin_ragged_decode,
-            pin_brute_bias, pin_bias_special_cases,
+            pin_brute_bias, pin_bias_special_cases, pin_chunked_prefill,
             lambda: pin_brute_prefill(MICRO_EQ), lambda: pin_brute_decode_latent(MICRO_EQ),
             lambda: pin_absorbed_equals_unabsorbed(MICRO, 15)]
 
