@@ -488,13 +488,125 @@ __global__ __launch_bounds__(256) void latent_combine_kernel(const float* part, 
   o_lat[(long)bh * 512 + 256 + threadIdx.x] = f2bf(a1 / L);
 }
 
+// Merge of the split partials fused with the value up-projection: one
+// workgroup per (head h, group of LO_BG = 8 sequences).  The merged latent
+// outputs o~ [8][512] go to LDS as bf16 (the precision of the W_UV product's
+// operand), and O[b, h*128 + c] = o~[b] . W_UV,h[c] is one
+// v_mfma_f32_32x32x16_bf16 chain per wave: rows = the 8 sequences (rows 8..31
+// of the A operand are zero), columns = 32 of the head's 128 values (wave w:
+// 32 w .. 32 w + 31), k = the 512 latent features.  Each lane's B operand,
+// row c of W_UV,h (kv_b_proj row h*256 + 128 + c), is loaded into registers
+// first, in flight while the splits are merged.  The workgroups of one head
+// run on one XCD (grid x = head), so its 128 KB of W_UV rows come from HBM
+// once.
+namespace {
+constexpr int LO_BG = 8;        // sequences per workgroup
+constexpr int LO_NSMAX = 256;   // split count bound (plan_latent_splits: <= 256)
+}
+
+__global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict__ part, int nsplit,
+                                                         int B, int H, const bf16_t* __restrict__ w_ukv,
+                                                         bf16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) char otb[LO_BG * 1024];  // o~ bf16, 16-byte chunk c of row r at c ^ r
+  __shared__ float wsc[LO_BG][LO_NSMAX];  // f_s / L per (sequence, split)
+  __shared__ float lsum[LO_BG][LO_NSMAX];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int h = blockIdx.x, b0 = blockIdx.y * LO_BG;
+  const int nb = min(LO_BG, B - b0);
+  // B operand of k-step s: W_UV,h[c][16 s + 8 lg .. + 7], c = 32 w + lr
+  const bf16_t* wr = w_ukv + ((long)h * 256 + 128 + 32 * w + lr) * 512 + 8 * lg;
+  bf16x8 wv[32];
+#pragma unroll
+  for (int s2 = 0; s2 < 32; ++s2) wv[s2] = *(const bf16x8*)(wr + 16 * s2);
+  // split statistics (m, l) of every (sequence, split), loaded in parallel
+  for (int idx = tid; idx < LO_BG * nsplit; idx += 256) {
+    const int j = idx / nsplit, sp = idx - j * nsplit;
+    const float* pp = part + (((long)(b0 + j) * nsplit + sp) * H + h) * 516;
+    const bool ok = j < nb;
+    wsc[j][sp] = ok ? pp[0] : -INFINITY;
+    lsum[j][sp] = ok ? pp[1] : 0.f;
+  }
+  __syncthreads();
+  // split weights f_s / L of sequence j: f_s = 2^(m_s - max m), L = sum f_s l_s
+  if (tid < nb) {
+    const int j = tid;
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, wsc[j][sp]);
+    float L = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float f = exp2f(wsc[j][sp] - M);
+      wsc[j][sp] = f;
+      L += f * lsum[j][sp];
+    }
+    const float inv = 1.f / L;
+    for (int sp = 0; sp < nsplit; ++sp) wsc[j][sp] *= inv;
+  }
+  __syncthreads();
+  // merged o~: thread (k4, jq) merges features 4 k4 .. +3 of sequences
+  // jq + 2 i (i < 4), loading 8 splits of all four at once
+  {
+    constexpr int NI = LO_BG / 2;
+    const int k4 = tid & 127, jq = tid >> 7;
+    floatx4 m[NI];
+    const float* pp[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      m[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      pp[i] = part + ((long)(b0 + jq + 2 * i) * nsplit * H + h) * 516 + 4 + 4 * k4;
+    }
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      floatx4 v[NI][8];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          v[i][q] = (jq + 2 * i < nb && s0 + q < nsplit) ? *(const floatx4*)(pp[i] + (long)(s0 + q) * H * 516)
+                                                       : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (s0 + q < nsplit && jq + 2 * i < nb) m[i] += wsc[jq + 2 * i][s0 + q] * v[i][q];
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = jq + 2 * i, ch = k4 >> 1;
+      *(u32x2*)(otb + r * 1024 + 16 * (ch ^ r) + 8 * (k4 & 1)) =
+          u32x2{pack2bf(m[i][0], m[i][1]), pack2bf(m[i][2], m[i][3])};
+    }
+  }
+  __syncthreads();
+  floatx16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < 32; ++s2) {
+    const int ch = 2 * s2 + lg;
+    const bf16x8 a = lr < LO_BG ? *(const bf16x8*)(otb + lr * 1024 + 16 * (ch ^ lr)) : bf16x8{};
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wv[s2], acc, 0, 0, 0);
+  }
+  // rows 4 lg + e (e < 4) of the first 8-row block are the sequences
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 4 * lg + e;
+    if (j < nb) out[(long)(b0 + j) * H * 128 + (long)h * 128 + 32 * w + lr] = f2bf(acc[e]);
+  }
+}
+
 hipError_t decode_latent_bf16(const DecodeLatentParams& p, hipStream_t s) {
   if (p.H != 64) return hipErrorInvalidValue;
+  if (p.w_ukv && p.nsplit > LO_NSMAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(decode_latent_kernel, dim3(p.nsplit, p.B), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(latent_combine_kernel, dim3(p.B * p.H), dim3(256), 0, s, p.part, p.nsplit,
-                     p.H, p.o_lat);
+  if (p.w_ukv) {
+    hipLaunchKernelGGL(latent_out_kernel, dim3(p.H, (p.B + LO_BG - 1) / LO_BG), dim3(256), 0, s, p.part,
+                       p.nsplit, p.B, p.H, p.w_ukv, p.out);
+  } else {
+    hipLaunchKernelGGL(latent_combine_kernel, dim3(p.B * p.H), dim3(256), 0, s, p.part, p.nsplit,
+                       p.H, p.o_lat);
+  }
   return hipGetLastError();
 }
 

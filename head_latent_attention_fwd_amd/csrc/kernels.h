@@ -218,6 +218,10 @@ struct DecodeLatentParams {
   int B, H, L, L_cap, nsplit, chunk;
   float scale_log2;
   const int* seq_pos;  // optional per-sequence positions, as for DecodeFullParams
+  // optional: with w_ukv (kv_b_proj [H*256][512]) the merge of the splits is
+  // fused with the value up-projection, writing out [B][H*128] (head dims
+  // 128 + 128) instead of o_lat
+  const bf16_t* w_ukv; bf16_t* out;
 };
 hipError_t decode_latent_bf16(const DecodeLatentParams& p, hipStream_t s);
 

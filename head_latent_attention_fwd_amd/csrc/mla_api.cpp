@@ -986,19 +986,9 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
     a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
     a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
     a.seq_pos = seq_pos;
+    // merge of the splits fused with O_h = o~_h W_UV,h^T
+    a.w_ukv = (const bf16_t*)w->w_ukv; a.out = (bf16_t*)b.o;
     LAUNCH("decode_latent", decode_latent_bf16(a, st));
-    // O_h = o~_h W_UV,h^T, batched over heads
-    GemmParams g = gp_base();
-    g.A = (const bf16_t*)pl.o_lat; g.lda = (long)H * kl;
-    g.B = (const bf16_t*)w->w_ukv + (long)dn * kl; g.ldb = kl;
-    g.C = b.o; g.ldc = (long)H * dv;
-    g.M = B; g.N = dv; g.K = kl;
-    g.batch = H; g.sA = kl; g.sB = (long)(dn + dv) * kl; g.sC = dv;
-    if (B <= 64 && kl <= 512) {
-      LAUNCH("gemm_uv", gemm_skinny_bf16(g, true, st));
-    } else {
-      LAUNCH("gemm_uv", gemm_bf16(g, EPI_BF16, -1, st));
-    }
   } else {
     GemmF32Params g;
     memset(&g, 0, sizeof g);
