@@ -19,17 +19,15 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 MLA_DEV float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Round-to-nearest-even float -> bf16 (NaN stays NaN).
-MLA_DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// Round-to-nearest-even float -> bf16 (NaN stays NaN): gfx950's
+// v_cvt_pk_bf16_f32, which the compiler emits for these conversions.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+MLA_DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 // Two floats -> packed bf16 pair (lo in bits 0..15).
 MLA_DEV uint32_t pack2bf(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 MLA_DEV float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }

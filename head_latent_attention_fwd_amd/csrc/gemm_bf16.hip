@@ -462,6 +462,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmGroup gg) {
   const int out_cols = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
   const int on0 = (EPI == EPI_SWIGLU) ? n0 / 2 : n0;
   bf16_t* C = (bf16_t*)p.C + (long)bidx * p.sC;
+  // kernel arguments the store loop needs, read once
+  const int rows_M = p.M;
+  const long ldc = p.ldc, ldr = p.ldr;
+  const bf16_t* __restrict__ Rres = p.R;
+  const bf16_t* __restrict__ bias = (EPI != EPI_SWIGLU) ? p.bias : nullptr;
+  constexpr int CH8 = OUTN / 8;            // 8-output chunks per row
+  constexpr int NIT = RP * CH8 / NT;       // chunks per thread and pass
+  static_assert((RP * CH8) % NT == 0, "epilogue store loop");
 #pragma unroll
   for (int pass = 0; pass < BM / RP; ++pass) {
     __syncthreads();  // LDS free: last K tile read (pass 0) or previous pass stored
@@ -486,36 +494,48 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmGroup gg) {
         }
     }
     __syncthreads();
-    constexpr int CH8 = OUTN / 8;            // 8-output chunks per row
-    for (int idx = tid; idx < RP * CH8; idx += NT) {
-      const int rl = idx / CH8, c8 = idx % CH8;
-      const int row = m0 + rlo + rl, col = on0 + 8 * c8;
-      if (row >= p.M || col >= out_cols) continue;
-      const floatx4 v0 = *(const floatx4*)&cst[cidx(rl, 8 * c8)];
-      const floatx4 v1 = *(const floatx4*)&cst[cidx(rl, 8 * c8 + 4)];
-      float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      if (EPI == EPI_RESID) {
-        const u32x4 r = *(const u32x4*)(p.R + (long)row * p.ldr + col);
+    // every chunk of this thread is read from LDS before the first
+    // conversion, so the waits overlap
+    floatx4 sv[NIT][2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[2 * q] += lo_bf(r[q]);
-          v[2 * q + 1] += hi_bf(r[q]);
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + it * NT, rl = idx / CH8, c8 = idx % CH8;
+      sv[it][0] = *(const floatx4*)&cst[cidx(rl, 8 * c8)];
+      sv[it][1] = *(const floatx4*)&cst[cidx(rl, 8 * c8 + 4)];
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + it * NT, rl = idx / CH8, c8 = idx % CH8;
+      const int row = m0 + rlo + rl, col = on0 + 8 * c8;
+      if (row >= rows_M || col >= out_cols) continue;
+      float v[8] = {sv[it][0][0], sv[it][0][1], sv[it][0][2], sv[it][0][3],
+                    sv[it][1][0], sv[it][1][1], sv[it][1][2], sv[it][1][3]};
+      if constexpr (EPI == EPI_RESID) {
+        if (col + 8 <= out_cols) {
+          const u32x4 r = *(const u32x4*)(Rres + (long)row * ldr + col);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] += lo_bf(r[q]);
+            v[2 * q + 1] += hi_bf(r[q]);
+          }
+        } else {
+          for (int q = 0; q < out_cols - col; ++q) v[q] += bf2f(Rres[(long)row * ldr + col + q]);
         }
       }
-      if (EPI != EPI_SWIGLU && p.bias) {
+      if (bias) {
         // o_proj of the attention_bias variant: y = x W^T + b
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          if (col + q < out_cols) v[q] += bf2f(p.bias[col + q]);
+          if (col + q < out_cols) v[q] += bf2f(bias[col + q]);
       }
       u32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = pack2bf(v[2 * q], v[2 * q + 1]);
       if (col + 8 <= out_cols) {
-        *(u32x4*)(C + (long)row * p.ldc + col) = o;
+        *(u32x4*)(C + (long)row * ldc + col) = o;
       } else {
         for (int q = 0; q < out_cols - col; ++q)
-          C[(long)row * p.ldc + col + q] = (bf16_t)((q & 1) ? (o[q >> 1] >> 16) : (o[q >> 1] & 0xffffu));
+          C[(long)row * ldc + col + q] = (bf16_t)((q & 1) ? (o[q >> 1] >> 16) : (o[q >> 1] & 0xffffu));
       }
     }
   }
