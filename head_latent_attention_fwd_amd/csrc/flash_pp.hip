@@ -89,19 +89,6 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
   const long rowbase = (long)b * p.T;
   const long HS = p.H;
 
-  // this wave's 32 queries as MFMA B fragments: features 16 s + 8 lg .. +8;
-  // the rotary features (s >= 8) are rotated by the RoPE row of the position
-  bf16x8 qf[12];
-  {
-    const int qrow = min(q0 + 32 * w + lr, p.T - 1);
-    const bf16_t* qp = p.q + ((rowbase + qrow) * HS + h) * 192 + 8 * lg;
-#pragma unroll
-    for (int s = 0; s < 12; ++s) {
-      u32x4 v = *(const u32x4*)(qp + 16 * s);
-      if (s >= 8) v = rope8_bf16(v, p.rcos, p.rsin, p.P0 + qrow, 32, (16 * s + 8 * lg - 128) / 2);
-      qf[s] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
   // positions: this lane's query and the wave's first / last query
   const int qlast = p.P0 + min(q0 + PP_BQ - 1, p.T - 1);
   const int n_kv = qlast / 64 + 1;
@@ -147,6 +134,23 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                            \
       pp_dma16(sb_ + PP_KC + PP_KR + 1024 * (2 * w + i), v_vo[i] + kk_ * p.v_kb, rvv);       \
   } while (0)
+
+  // Prologue loads: the first key tile is issued before the queries, so the
+  // two (and the RoPE rows) are in flight together.
+  for (int tt = 0; tt < PP_NST - 2 && tt < n_kv; ++tt) PP_ISSUE(tt);
+  // This wave's 32 queries as MFMA B fragments: features 16 s + 8 lg .. +8;
+  // the rotary features (s >= 8) are rotated by the RoPE row of the position
+  bf16x8 qf[12];
+  {
+    const int qrow = min(q0 + 32 * w + lr, p.T - 1);
+    const bf16_t* qp = p.q + ((rowbase + qrow) * HS + h) * 192 + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 12; ++s) {
+      u32x4 v = *(const u32x4*)(qp + 16 * s);
+      if (s >= 8) v = rope8_bf16(v, p.rcos, p.rsin, p.P0 + qrow, 32, (16 * s + 8 * lg - 128) / 2);
+      qf[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
 
   // ---- fragment offsets inside a stage (tile-invariant).
   // K fragment (s, mb): key row 32 mb + lr.  s < 8: content chunk 2 s + lg;
@@ -284,7 +288,6 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
   // boundary a wave first makes its own loads of the next tile land, then
   // (after the barrier) issues its loads of the tile NST - 2 ahead into the
   // buffer whose last reader (PV of the second half) finished before it.
-  for (int tt = 0; tt < PP_NST - 2 && tt < n_kv; ++tt) PP_ISSUE(tt);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (PP_NST - 2 < n_kv) PP_ISSUE(PP_NST - 2);
