@@ -10,6 +10,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -21,13 +22,11 @@ MLA_DEV float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Round-to-nearest-even float -> bf16 (NaN stays NaN): gfx950's
 // v_cvt_pk_bf16_f32, which the compiler emits for these conversions.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 MLA_DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 // Two floats -> packed bf16 pair (lo in bits 0..15).
 MLA_DEV uint32_t pack2bf(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){lo, hi}, bf16x2));
 }
 
 MLA_DEV float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }

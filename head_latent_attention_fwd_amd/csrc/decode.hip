@@ -18,8 +18,9 @@
 //                   stream, so the heads become the MFMA N dimension:
 //                   S^T = C . Q~^T (v_mfma_f32_16x16x32_bf16, 16 heads per
 //                   wave), then o~^T = C^T . P^T with C^T staged transposed in
-//                   LDS.  Split-L partials (m, l, o~) per head are merged by
-//                   latent_combine.
+//                   LDS.  Split-L partials (m, l in fp32, o~ in bf16) per
+//                   head are merged by latent_out together with the W_UV
+//                   product.
 //  absorb_q       : q~_h = Q^C_h . W_UK,h (W_UK folded into the query), an
 //                   MFMA product whose weight operand is transposed into LDS.
 #include "common.h"
@@ -297,11 +298,6 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
   const int head = 16 * w + l16;
   const int ntiles = j1 > j0 ? (j1 - j0 + LT - 1) / LT : 0;
 
-  // [q~ | roped q^R] of this head, laid out like a cache row
-  bf16x8 qf[18];
-#pragma unroll
-  for (int s = 0; s < 18; ++s)
-    qf[s] = *(const bf16x8*)(p.q_abs + ((long)b * p.H + head) * 576 + 32 * s + 8 * g4);
   const char* cb = (const char*)(p.cache + ((long)b * p.L_cap + j0) * 576);
 
   // DMA k of this wave fills LDS bytes [1024 (w * DMA_PER_WAVE + k), +1024) of
@@ -336,10 +332,19 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
     pv_off[n3] = row * ROWB + 16 * ((c ^ lat_fr(row)) & 7) + 8 * (l16 & 1);
   }
 
+  // The first tiles are issued before the query is loaded, so the two are in
+  // flight together.
+  for (int tt = 0; tt < NST - 1 && tt < ntiles; ++tt) LAT_ISSUE(tt);
+  // [q~ | roped q^R] of this head, laid out like a cache row
+  bf16x8 qf[18];
+#pragma unroll
+  for (int s = 0; s < 18; ++s)
+    qf[s] = *(const bf16x8*)(p.q_abs + ((long)b * p.H + head) * 576 + 32 * s + 8 * g4);
+
   const float sl2 = p.scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
   floatx4 O[32];
-  bool restart = ntiles > 0;
+  bool restart = ntiles > 0, first_pass = true;
   while (restart) {
     restart = false;
 #pragma unroll
@@ -348,7 +353,9 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
       asm volatile("" : "+a"(O[i]));  // keep the accumulators in AGPRs across both loops
     }
     l_run = 0.f;
-    for (int tt = 0; tt < NST - 1 && tt < ntiles; ++tt) LAT_ISSUE(tt);
+    if (!first_pass)
+      for (int tt = 0; tt < NST - 1 && tt < ntiles; ++tt) LAT_ISSUE(tt);
+    first_pass = false;
     for (int t = 0;; ++t) {
       wait_tiles(min(NST - 2, ntiles - 1 - t));
       __syncthreads();
@@ -459,33 +466,16 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
 #undef LAT_ISSUE
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  // partial record: m, l, 2 pad, o~[512] (16-byte aligned)
-  float* pp = p.part + (((long)b * p.nsplit + split) * p.H + head) * 516;
-  if (g4 == 0) {
-    pp[0] = m_run;
-    pp[1] = l_tot;
-  }
+  // split record: (m, l) in fp32 and o~[512] rounded to bf16 (the merge
+  // weights it by 2^(m - max m) / L and rounds the merged o~ to bf16 again for
+  // the W_UV product)
+  const long rec = ((long)b * p.nsplit + split) * p.H + head;
+  if (g4 == 0) *(floatx2*)(p.stats + 2 * rec) = floatx2{m_run, l_tot};
+  bf16_t* op = p.opart + rec * 512 + 4 * g4;
 #pragma unroll
   for (int i = 0; i < 32; ++i)
-    *(floatx4*)(pp + 4 + 16 * i + 4 * g4) = ntiles > 0 ? O[i] : floatx4{0.f, 0.f, 0.f, 0.f};
-}
-
-__global__ __launch_bounds__(256) void latent_combine_kernel(const float* part, int nsplit, int H,
-                                                             bf16_t* o_lat) {
-  const int bh = blockIdx.x;  // b * H + h
-  const int b = bh / H, h = bh % H;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[(((long)b * nsplit + s) * H + h) * 516]);
-  float L = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* pp = part + (((long)b * nsplit + s) * H + h) * 516;
-    const float f = exp2f(pp[0] - M);
-    L += f * pp[1];
-    a0 += f * pp[4 + threadIdx.x];
-    a1 += f * pp[4 + 256 + threadIdx.x];
-  }
-  o_lat[(long)bh * 512 + threadIdx.x] = f2bf(a0 / L);
-  o_lat[(long)bh * 512 + 256 + threadIdx.x] = f2bf(a1 / L);
+    *(u32x2*)(op + 16 * i) = ntiles > 0 ? u32x2{pack2bf(O[i][0], O[i][1]), pack2bf(O[i][2], O[i][3])}
+                                        : u32x2{0u, 0u};
 }
 
 // Merge of the split partials fused with the value up-projection: one
@@ -504,7 +494,8 @@ constexpr int LO_BG = 8;        // sequences per workgroup
 constexpr int LO_NSMAX = 256;   // split count bound (plan_latent_splits: <= 256)
 }
 
-__global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict__ part, int nsplit,
+__global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict__ stats,
+                                                         const bf16_t* __restrict__ opart, int nsplit,
                                                          int B, int H, const bf16_t* __restrict__ w_ukv,
                                                          bf16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) char otb[LO_BG * 1024];  // o~ bf16, 16-byte chunk c of row r at c ^ r
@@ -522,10 +513,11 @@ __global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict
   // split statistics (m, l) of every (sequence, split), loaded in parallel
   for (int idx = tid; idx < LO_BG * nsplit; idx += 256) {
     const int j = idx / nsplit, sp = idx - j * nsplit;
-    const float* pp = part + (((long)(b0 + j) * nsplit + sp) * H + h) * 516;
     const bool ok = j < nb;
-    wsc[j][sp] = ok ? pp[0] : -INFINITY;
-    lsum[j][sp] = ok ? pp[1] : 0.f;
+    const floatx2 ml = ok ? *(const floatx2*)(stats + 2 * (((long)(b0 + j) * nsplit + sp) * H + h))
+                          : floatx2{-INFINITY, 0.f};
+    wsc[j][sp] = ml[0];
+    lsum[j][sp] = ml[1];
   }
   __syncthreads();
   // split weights f_s / L of sequence j: f_s = 2^(m_s - max m), L = sum f_s l_s
@@ -549,25 +541,28 @@ __global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict
     constexpr int NI = LO_BG / 2;
     const int k4 = tid & 127, jq = tid >> 7;
     floatx4 m[NI];
-    const float* pp[NI];
+    const bf16_t* pp[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       m[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-      pp[i] = part + ((long)(b0 + jq + 2 * i) * nsplit * H + h) * 516 + 4 + 4 * k4;
+      pp[i] = opart + ((long)(b0 + jq + 2 * i) * nsplit * H + h) * 512 + 4 * k4;
     }
     for (int s0 = 0; s0 < nsplit; s0 += 8) {
-      floatx4 v[NI][8];
+      u32x2 v[NI][8];
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          v[i][q] = (jq + 2 * i < nb && s0 + q < nsplit) ? *(const floatx4*)(pp[i] + (long)(s0 + q) * H * 516)
-                                                       : floatx4{0.f, 0.f, 0.f, 0.f};
+          v[i][q] = (jq + 2 * i < nb && s0 + q < nsplit) ? *(const u32x2*)(pp[i] + (long)(s0 + q) * H * 512)
+                                                       : u32x2{0u, 0u};
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          if (s0 + q < nsplit && jq + 2 * i < nb) m[i] += wsc[jq + 2 * i][s0 + q] * v[i][q];
+          if (s0 + q < nsplit && jq + 2 * i < nb) {
+            const float f = wsc[jq + 2 * i][s0 + q];
+            m[i] += f * floatx4{lo_bf(v[i][q][0]), hi_bf(v[i][q][0]), lo_bf(v[i][q][1]), hi_bf(v[i][q][1])};
+          }
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -595,18 +590,12 @@ __global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict
 }
 
 hipError_t decode_latent_bf16(const DecodeLatentParams& p, hipStream_t s) {
-  if (p.H != 64) return hipErrorInvalidValue;
-  if (p.w_ukv && p.nsplit > LO_NSMAX) return hipErrorInvalidValue;
+  if (p.H != 64 || !p.w_ukv || p.nsplit > LO_NSMAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(decode_latent_kernel, dim3(p.nsplit, p.B), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.w_ukv) {
-    hipLaunchKernelGGL(latent_out_kernel, dim3(p.H, (p.B + LO_BG - 1) / LO_BG), dim3(256), 0, s, p.part,
-                       p.nsplit, p.B, p.H, p.w_ukv, p.out);
-  } else {
-    hipLaunchKernelGGL(latent_combine_kernel, dim3(p.B * p.H), dim3(256), 0, s, p.part, p.nsplit,
-                       p.H, p.o_lat);
-  }
+  hipLaunchKernelGGL(latent_out_kernel, dim3(p.H, (p.B + LO_BG - 1) / LO_BG), dim3(256), 0, s, p.stats,
+                     p.opart, p.nsplit, p.B, p.H, p.w_ukv, p.out);
   return hipGetLastError();
 }
 

@@ -212,15 +212,14 @@ hipError_t decode_full_bf16(const DecodeFullParams& p, hipStream_t s);
 struct DecodeLatentParams {
   const bf16_t* q_abs;   // [B][H][576]  [absorbed query q~ (W_UK folded in) | roped q^R]
   const bf16_t* cache;   // [B][L_cap][576]
-  float* part;           // [B][nsplit][H][516]: m, l, pad, pad, o~[512]
-  bf16_t* o_lat;         // [B][H][512]  merged latent output
+  float* stats;          // [B][nsplit][H][2]: running max m (log2 units) and sum l of each split
+  bf16_t* opart;         // [B][nsplit][H][512]: unnormalised o~ of each split
   const float* rcos; const float* rsin;  // RoPE table, row L-1 used
   int B, H, L, L_cap, nsplit, chunk;
   float scale_log2;
   const int* seq_pos;  // optional per-sequence positions, as for DecodeFullParams
-  // optional: with w_ukv (kv_b_proj [H*256][512]) the merge of the splits is
-  // fused with the value up-projection, writing out [B][H*128] (head dims
-  // 128 + 128) instead of o_lat
+  // the merge of the splits is fused with the value up-projection (W_UV rows
+  // of kv_b_proj [H*256][512]), writing out [B][H*128] (head dims 128 + 128)
   const bf16_t* w_ukv; bf16_t* out;
 };
 hipError_t decode_latent_bf16(const DecodeLatentParams& p, hipStream_t s);

@@ -549,7 +549,8 @@ size_t decode_layout(const mla_dims* d, int B, int L_cap, int form, void* ws, De
   if (cap_l > (L_cap + 31) / 32) cap_l = (L_cap + 31) / 32;
   if (cap_l < 1) cap_l = 1;
   size_t fpart = (size_t)B * H * cap_f * 130 * 4;
-  size_t lpart = (size_t)B * cap_l * H * 516 * 4;
+  // latent form: fp32 (m, l) then bf16 o~[kv_lora] per (sequence, split, head)
+  size_t lpart = (size_t)B * cap_l * H * (2 * 4 + (size_t)kl * 2);
   pl->apart = c.take(fpart > lpart ? fpart : lpart);
   pl->ns_cap = form == 0 ? cap_f : cap_l;
   pl->nsplit = 1;
@@ -980,8 +981,9 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
     LAUNCH("absorb_q", absorb_q_bf16(ab, st));
     DecodeLatentParams a;
     a.q_abs = (const bf16_t*)pl.q_abs;
-    a.cache = (const bf16_t*)latent_cache; a.part = (float*)pl.apart;
-    a.o_lat = (bf16_t*)pl.o_lat;
+    a.cache = (const bf16_t*)latent_cache;
+    a.stats = (float*)pl.apart;
+    a.opart = (bf16_t*)((char*)pl.apart + (size_t)B * pl.ns_cap * H * 2 * sizeof(float));
     a.rcos = rc; a.rsin = rs;
     a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
     a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
