@@ -116,6 +116,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmGroup gg) {
   static_assert(FM >= 1 && FN >= 1, "wave tile");
   static_assert(A_CH >= 1 && B_CH >= 1, "tile too small for the block");
   static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU pairs 32-column blocks inside a wave");
+  // Accumulator orientation.  The fp32 epilogue takes D = A.B^T per 32x32
+  // block (a lane holds one output column, rows 8 g + 4 (lane >> 5) + 0..3);
+  // the staged epilogues take D = B.A^T, so that a lane holds one output row
+  // and four consecutive output columns (8 g + 4 (lane >> 5) + 0..3), which
+  // it writes to LDS as one 8-byte (bf16) or 16-byte (fp32) chunk.
+  constexpr bool SWAP = EPI != EPI_F32;
 
   // LDS: the two-stage register-staged layout, or the direct-to-LDS ring
   constexpr int LDS_U4_REG = 2 * (BM + BN) * 8;
@@ -246,7 +252,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmGroup gg) {
 #define GD_MFMAS(slot)                                                                       \
   _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                          \
     const int i = q / FN, j = q % FN;                                                        \
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0); \
+    acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0)   \
+                     : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);  \
   }
 #define GD_SCHED()                                                                           \
   _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                          \
@@ -364,7 +371,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmGroup gg) {
     do {                                                                                    \
       _Pragma("unroll") for (int q = (lo); q < (hi); ++q) {                                 \
         const int i = q / FN, j = q % FN;                                                   \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0); \
+        acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0)   \
+                     : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);  \
       }                                                                                     \
     } while (0)
   
@@ -446,71 +454,123 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmGroup gg) {
     }
     return;
   }
-  // bf16 outputs: the fp32 tile is staged in the (now free) LDS in passes of
-  // RP rows, then every thread writes 8 consecutive outputs with one 16-byte
-  // store (residual add / SwiGLU in fp32, one rounding).
   constexpr int OUTN = (EPI == EPI_SWIGLU) ? BN / 2 : BN;   // output columns of the tile
-  constexpr int LDS_F = 2 * (BM + BN) * 8 * 4;              // floats available
-  constexpr int RP0 = LDS_F / OUTN;
-  constexpr int RP = RP0 >= BM ? BM : (RP0 >= WTM ? (RP0 / WTM) * WTM : WTM);
-  static_assert(RP * OUTN <= LDS_F, "epilogue staging does not fit the LDS");
   static_assert(OUTN % 64 == 0, "output tile width");
-  float* cst = (float*)&lds[0][0];
-  // 16-byte chunk swizzle: rows r and r+4 (the two half-waves) use opposite
-  // halves of each 256-byte bank window
-  auto cidx = [](int r, int c) { return r * OUTN + ((((c >> 2) ^ (((r >> 2) & 1) << 3))) << 2) + (c & 3); };
   const int out_cols = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
   const int on0 = (EPI == EPI_SWIGLU) ? n0 / 2 : n0;
   bf16_t* C = (bf16_t*)p.C + (long)bidx * p.sC;
-  // kernel arguments the store loop needs, read once
+  // kernel arguments the store loops need, read once
   const int rows_M = p.M;
   const long ldc = p.ldc, ldr = p.ldr;
   const bf16_t* __restrict__ Rres = p.R;
   const bf16_t* __restrict__ bias = (EPI != EPI_SWIGLU) ? p.bias : nullptr;
-  constexpr int CH8 = OUTN / 8;            // 8-output chunks per row
-  constexpr int NIT = RP * CH8 / NT;       // chunks per thread and pass
-  static_assert((RP * CH8) % NT == 0, "epilogue store loop");
+  constexpr int CH8 = OUTN / 8;  // 8-output (16-byte bf16) chunks per output row
+  // output column (in the tile) of acc[i][j][4 g + q], q = 0..3
+  auto tcol = [&](int j, int g) {
+    if (EPI == EPI_SWIGLU) return ((wn * WTN) / 32 + j) / 2 * 32 + 8 * g + 4 * lg;
+    return wn * WTN + j * 32 + 8 * g + 4 * lg;
+  };
+  if constexpr (EPI != EPI_RESID) {
+    // bf16 outputs (plain, bias, SwiGLU): the rounded tile is staged whole
+    // in the (now free) LDS, 16-byte chunk s of row r at s ^ (r % NSL), then
+    // every thread writes 8 consecutive outputs with one 16-byte store.
+    constexpr int ROWB = OUTN * 2;
+    constexpr int NSL = CH8 < 16 ? CH8 : 16;
+    static_assert(BM * ROWB <= (int)sizeof(lds_raw), "epilogue staging does not fit the LDS");
+    char* cst = (char*)&lds[0][0];
+    __syncthreads();  // last K tile read
 #pragma unroll
-  for (int pass = 0; pass < BM / RP; ++pass) {
-    __syncthreads();  // LDS free: last K tile read (pass 0) or previous pass stored
-    const int rlo = pass * RP;
-    if (wm * WTM + WTM > rlo && wm * WTM < rlo + RP) {
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 32 + lr_;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < FN; j += (EPI == EPI_SWIGLU ? 2 : 1))
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int rl = wm * WTM + i * 32 + (e >> 2) * 8 + lg * 4 + (e & 3) - rlo;
-          if (EPI == EPI_SWIGLU) {
+        for (int g = 0; g < 4; ++g) {
+          const int c = tcol(j, g);
+          float v[4];
 #pragma unroll
-            for (int j = 0; j < FN; j += 2) {
-              const int cl = ((wn * WTN) / 32 + j) / 2 * 32 + lr_;   // output column in tile
-              const float g = acc[i][j][e], u = acc[i][j + 1][e];
-              cst[cidx(rl, cl)] = g / (1.f + __expf(-g)) * u;
+          for (int q = 0; q < 4; ++q) {
+            if (EPI == EPI_SWIGLU) {
+              const float gg = acc[i][j][4 * g + q], uu = acc[i][j + 1][4 * g + q];
+              v[q] = gg / (1.f + __expf(-gg)) * uu;
+            } else {
+              v[q] = acc[i][j][4 * g + q];
             }
-          } else {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) cst[cidx(rl, wn * WTN + j * 32 + lr_)] = acc[i][j][e];
           }
+          if (bias) {
+            // o_proj of the attention_bias variant: y = x W^T + b
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (on0 + c + q < out_cols) v[q] += bf2f(bias[on0 + c + q]);
+          }
+          *(u32x2*)(cst + r * ROWB + 16 * ((c >> 3) ^ (r % NSL)) + 8 * ((c >> 2) & 1)) =
+              u32x2{pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
         }
     }
     __syncthreads();
-    // every chunk of this thread is read from LDS before the first
-    // conversion, so the waits overlap
-    floatx4 sv[NIT][2];
+    constexpr int NIT = BM * CH8 / NT;
+    static_assert((BM * CH8) % NT == 0, "epilogue store loop");
+    u32x4 sv[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int idx = tid + it * NT, rl = idx / CH8, c8 = idx % CH8;
-      sv[it][0] = *(const floatx4*)&cst[cidx(rl, 8 * c8)];
-      sv[it][1] = *(const floatx4*)&cst[cidx(rl, 8 * c8 + 4)];
+      sv[it] = *(const u32x4*)(cst + rl * ROWB + 16 * (c8 ^ (rl % NSL)));
     }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int idx = tid + it * NT, rl = idx / CH8, c8 = idx % CH8;
-      const int row = m0 + rlo + rl, col = on0 + 8 * c8;
+      const int row = m0 + rl, col = on0 + 8 * c8;
       if (row >= rows_M || col >= out_cols) continue;
-      float v[8] = {sv[it][0][0], sv[it][0][1], sv[it][0][2], sv[it][0][3],
-                    sv[it][1][0], sv[it][1][1], sv[it][1][2], sv[it][1][3]};
-      if constexpr (EPI == EPI_RESID) {
+      if (col + 8 <= out_cols) {
+        *(u32x4*)(C + (long)row * ldc + col) = sv[it];
+      } else {
+        for (int q = 0; q < out_cols - col; ++q)
+          C[(long)row * ldc + col + q] = (bf16_t)((q & 1) ? (sv[it][q >> 1] >> 16) : (sv[it][q >> 1] & 0xffffu));
+      }
+    }
+  } else {
+    // residual add: the fp32 tile is staged in passes of RP rows, 16-byte
+    // chunk s of row r at s ^ 2 (r % 8) (pairs of chunks stay together), and
+    // the store loop adds R in fp32 before the one rounding.
+    constexpr int LDS_F = (int)sizeof(lds_raw) / 4;           // floats available
+    constexpr int RP0 = LDS_F / OUTN;
+    constexpr int RP = RP0 >= BM ? BM : (RP0 >= WTM ? (RP0 / WTM) * WTM : WTM);
+    static_assert(RP * OUTN <= LDS_F, "epilogue staging does not fit the LDS");
+    float* cst = (float*)&lds[0][0];
+    auto cidx = [](int r, int c) { return r * OUTN + ((c >> 2) ^ (2 * (r & 7))) * 4 + (c & 3); };
+    constexpr int NIT = RP * CH8 / NT;
+    static_assert((RP * CH8) % NT == 0, "epilogue store loop");
+#pragma unroll
+    for (int pass = 0; pass < BM / RP; ++pass) {
+      __syncthreads();  // LDS free: last K tile read (pass 0) or previous pass stored
+      const int rlo = pass * RP;
+      if (wm * WTM + WTM > rlo && wm * WTM < rlo + RP) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int rl = wm * WTM + i * 32 + lr_ - rlo;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *(floatx4*)&cst[cidx(rl, tcol(j, g))] =
+                  floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        }
+      }
+      __syncthreads();
+      floatx4 sv[NIT][2];
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int idx = tid + it * NT, rl = idx / CH8, c8 = idx % CH8;
+        sv[it][0] = *(const floatx4*)&cst[cidx(rl, 8 * c8)];
+        sv[it][1] = *(const floatx4*)&cst[cidx(rl, 8 * c8 + 4)];
+      }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int idx = tid + it * NT, rl = idx / CH8, c8 = idx % CH8;
+        const int row = m0 + rlo + rl, col = on0 + 8 * c8;
+        if (row >= rows_M || col >= out_cols) continue;
+        float v[8] = {sv[it][0][0], sv[it][0][1], sv[it][0][2], sv[it][0][3],
+                      sv[it][1][0], sv[it][1][1], sv[it][1][2], sv[it][1][3]};
         if (col + 8 <= out_cols) {
           const u32x4 r = *(const u32x4*)(Rres + (long)row * ldr + col);
 #pragma unroll
@@ -521,21 +581,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmGroup gg) {
         } else {
           for (int q = 0; q < out_cols - col; ++q) v[q] += bf2f(Rres[(long)row * ldr + col + q]);
         }
-      }
-      if (bias) {
-        // o_proj of the attention_bias variant: y = x W^T + b
+        if (bias) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (col + q < out_cols) v[q] += bf2f(bias[col + q]);
-      }
-      u32x4 o;
+          for (int q = 0; q < 8; ++q)
+            if (col + q < out_cols) v[q] += bf2f(bias[col + q]);
+        }
+        u32x4 o;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack2bf(v[2 * q], v[2 * q + 1]);
-      if (col + 8 <= out_cols) {
-        *(u32x4*)(C + (long)row * ldc + col) = o;
-      } else {
-        for (int q = 0; q < out_cols - col; ++q)
-          C[(long)row * ldc + col + q] = (bf16_t)((q & 1) ? (o[q >> 1] >> 16) : (o[q >> 1] & 0xffffu));
+        for (int q = 0; q < 4; ++q) o[q] = pack2bf(v[2 * q], v[2 * q + 1]);
+        if (col + 8 <= out_cols) {
+          *(u32x4*)(C + (long)row * ldc + col) = o;
+        } else {
+          for (int q = 0; q < out_cols - col; ++q)
+            C[(long)row * ldc + col + q] = (bf16_t)((q & 1) ? (o[q >> 1] >> 16) : (o[q >> 1] & 0xffffu));
+        }
       }
     }
   }
