@@ -293,8 +293,12 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   const int split = blockIdx.x, b = blockIdx.y;
-  const int j0 = split * p.chunk;
-  const int j1 = min(seq_position(p.seq_pos, b, p.L - 1, p.L - 1) + 1, j0 + p.chunk);
+  // the sequence's key tiles are dealt out evenly: split s takes tiles
+  // [s n / nsplit, (s + 1) n / nsplit) of its n
+  const int Lb = seq_position(p.seq_pos, b, p.L - 1, p.L - 1) + 1;
+  const int nt_seq = (Lb + LT - 1) / LT;
+  const int j0 = LT * (int)((long)split * nt_seq / p.nsplit);
+  const int j1 = min(Lb, LT * (int)((long)(split + 1) * nt_seq / p.nsplit));
   const int head = 16 * w + l16;
   const int ntiles = j1 > j0 ? (j1 - j0 + LT - 1) / LT : 0;
 

@@ -215,7 +215,7 @@ struct DecodeLatentParams {
   float* stats;          // [B][nsplit][H][2]: running max m (log2 units) and sum l of each split
   bf16_t* opart;         // [B][nsplit][H][512]: unnormalised o~ of each split
   const float* rcos; const float* rsin;  // RoPE table, row L-1 used
-  int B, H, L, L_cap, nsplit, chunk;
+  int B, H, L, L_cap, nsplit;  // each sequence's key tiles are split evenly over nsplit
   float scale_log2;
   const int* seq_pos;  // optional per-sequence positions, as for DecodeFullParams
   // the merge of the splits is fused with the value up-projection (W_UV rows

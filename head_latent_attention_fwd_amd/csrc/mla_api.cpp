@@ -521,15 +521,13 @@ void plan_full_splits(int B, int H, int L, int* nsplit, int* chunk) {
   *nsplit = (L + ch - 1) / ch;
 }
 
-void plan_latent_splits(int B, int L, int* nsplit, int* chunk) {
+// latent form: about 256 workgroups in all, at least one 32-key tile each
+// (the kernel deals each sequence's tiles out evenly over the splits)
+int plan_latent_splits(int B, int L) {
   int s = (256 + B - 1) / B;
-  int maxs = (L + 31) / 32;
+  const int maxs = (L + 31) / 32;
   if (s > maxs) s = maxs;
-  if (s < 1) s = 1;
-  int ch = (L + s - 1) / s;
-  ch = (ch + 31) / 32 * 32;
-  *chunk = ch;
-  *nsplit = (L + ch - 1) / ch;
+  return s < 1 ? 1 : s;
 }
 
 size_t decode_layout(const mla_dims* d, int B, int L_cap, int form, void* ws, DecodePlan* pl) {
@@ -961,7 +959,7 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
   if (ws_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   decode_layout(d, B, L_cap, 1, ws, &pl);
-  plan_latent_splits(B, P + 1, &pl.nsplit, &pl.chunk);
+  pl.nsplit = plan_latent_splits(B, P + 1);
   if (pl.nsplit > pl.ns_cap) return fail(MLA_ERR_HIP, "internal: split plan exceeds workspace");
   hipStream_t st = (hipStream_t)stream;
   const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
@@ -985,7 +983,7 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
     a.stats = (float*)pl.apart;
     a.opart = (bf16_t*)((char*)pl.apart + (size_t)B * pl.ns_cap * H * 2 * sizeof(float));
     a.rcos = rc; a.rsin = rs;
-    a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
+    a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit;
     a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
     a.seq_pos = seq_pos;
     // merge of the splits fused with O_h = o~_h W_UV,h^T
