@@ -266,7 +266,95 @@ MLA_DEV void wait_tiles(int n) {
 }
 }  // namespace
 
-// One workgroup = one (batch row, key split); 4 waves x 16 heads.  Per tile of
+// block-wide sum / max of one int per thread (256 threads)
+MLA_DEV int block_sum_int(int x, int* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+MLA_DEV int block_max_int(int x, int* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// Split plan of the absorbed-cache attention, computed by one workgroup of
+// 256 threads.  The keys of sequence b (0 .. its position) form n_b 32-key
+// tiles.  With c the smallest tile count such that sum_b ceil(n_b / c) <= G,
+// sequence b gets s_b = ceil(n_b / c) workgroups, which split its tiles
+// evenly (at most c tiles each, at least one), so the longest run is as short
+// as whole-sequence runs allow.  Output (ints): plan[v] = sequence of
+// workgroup v (-1: idle), plan[G + v] and plan[2 G + v] = its key range
+// [j0, j1); plan[3 G + b] and plan[3 G + B + b] = first workgroup and count of
+// sequence b.  Needs B <= G and B <= LP_NS.
+constexpr int LP_NS = 1024;  // sequences the plan handles (tile counts kept in LDS)
+MLA_DEV void latent_plan(int B, int L, const int* seq_pos, int G, int* plan) {
+  __shared__ int red[4];
+  __shared__ int ns[LP_NS], ss[LP_NS], fs[LP_NS];  // tiles, workgroups, first workgroup
+  const int tid = threadIdx.x;
+  int t = 0, mx = 0;
+  for (int b = tid; b < B; b += 256) {
+    const int n = (seq_position(seq_pos, b, L - 1, L - 1) + LT) / LT;
+    ns[b] = n;
+    t += n;
+    mx = max(mx, n);
+  }
+  t = block_sum_int(t, red);
+  mx = block_max_int(mx, red);
+  // sum_b ceil(n_b / c) <= t / c + B, so c >= t / (G - B) always fits
+  int lo = max(1, (t + G - 1) / G);
+  int hi = G > B ? min(mx, (t + G - B - 1) / (G - B)) : mx;
+  hi = max(lo, hi);
+  while (lo < hi) {  // the same bounds in every thread
+    const int c = (lo + hi) / 2;
+    int k = 0;
+    for (int b = tid; b < B; b += 256) k += (ns[b] + c - 1) / c;
+    if (block_sum_int(k, red) <= G) hi = c;
+    else lo = c + 1;
+  }
+  for (int b = tid; b < B; b += 256) ss[b] = (ns[b] + lo - 1) / lo;
+  __syncthreads();
+  if (tid == 0) {
+    int v = 0;
+    for (int b = 0; b < B; ++b) {
+      fs[b] = v;
+      v += ss[b];
+    }
+    red[0] = v;
+  }
+  __syncthreads();
+  const int used = red[0];
+  for (int b = tid; b < B; b += 256) {
+    plan[3 * G + b] = fs[b];
+    plan[3 * G + B + b] = ss[b];
+  }
+  for (int v = tid; v < G; v += 256) {
+    if (v >= used) {
+      plan[v] = -1;
+      continue;
+    }
+    int bl = 0, bh = B - 1;  // last sequence whose first workgroup is <= v
+    while (bl < bh) {
+      const int m = (bl + bh + 1) / 2;
+      if (fs[m] <= v) bl = m;
+      else bh = m - 1;
+    }
+    const int k = v - fs[bl], s = ss[bl], n = ns[bl];
+    const int Lb = seq_position(seq_pos, bl, L - 1, L - 1) + 1;
+    plan[v] = bl;
+    plan[G + v] = LT * (k * n / s);
+    plan[2 * G + v] = min(Lb, LT * ((k + 1) * n / s));
+  }
+}
+
+// One workgroup = one run of key tiles of one sequence (latent_plan); 4 waves
+// x 16 heads.  Per tile of
 // 32 cache rows: S^T[key, head] = C[key, 0:576] . q~[head]^T (16x16x32 MFMA,
 // key rows read from LDS, the absorbed query held in registers), exp2 in
 // registers, O~^T[feature, head] += C^T[feature, key] . P^T with the C^T
@@ -292,16 +380,23 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int split = blockIdx.x, b = blockIdx.y;
-  // the sequence's key tiles are dealt out evenly: split s takes tiles
-  // [s n / nsplit, (s + 1) n / nsplit) of its n
-  const int Lb = seq_position(p.seq_pos, b, p.L - 1, p.L - 1) + 1;
-  const int nt_seq = (Lb + LT - 1) / LT;
-  const int j0 = LT * (int)((long)split * nt_seq / p.nsplit);
-  const int j1 = min(Lb, LT * (int)((long)(split + 1) * nt_seq / p.nsplit));
   const int head = 16 * w + l16;
-  const int ntiles = j1 > j0 ? (j1 - j0 + LT - 1) / LT : 0;
-
+  // this workgroup's sequence and key range: from latent_plan, or (one
+  // length for all) split k of sequence v / splits, an even share of its tiles
+  const int v = blockIdx.x;
+  int b, j0, j1;
+  if (p.plan) {
+    b = p.plan[v];
+    if (b < 0) return;  // idle: fewer runs than workgroups
+    j0 = p.plan[p.G + v];
+    j1 = p.plan[2 * p.G + v];
+  } else {
+    b = v / p.splits;
+    const int k = v - b * p.splits, n = (p.L + LT - 1) / LT;
+    j0 = LT * (k * n / p.splits);
+    j1 = min(p.L, LT * ((k + 1) * n / p.splits));
+  }
+  const int ntiles = (j1 - j0 + LT - 1) / LT;  // >= 1
   const char* cb = (const char*)(p.cache + ((long)b * p.L_cap + j0) * 576);
 
   // DMA k of this wave fills LDS bytes [1024 (w * DMA_PER_WAVE + k), +1024) of
@@ -348,7 +443,7 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
   const float sl2 = p.scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
   floatx4 O[32];
-  bool restart = ntiles > 0, first_pass = true;
+  bool restart = true, first_pass = true;
   while (restart) {
     restart = false;
 #pragma unroll
@@ -473,13 +568,12 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
   // split record: (m, l) in fp32 and o~[512] rounded to bf16 (the merge
   // weights it by 2^(m - max m) / L and rounds the merged o~ to bf16 again for
   // the W_UV product)
-  const long rec = ((long)b * p.nsplit + split) * p.H + head;
+  const long rec = (long)v * p.H + head;
   if (g4 == 0) *(floatx2*)(p.stats + 2 * rec) = floatx2{m_run, l_tot};
   bf16_t* op = p.opart + rec * 512 + 4 * g4;
 #pragma unroll
   for (int i = 0; i < 32; ++i)
-    *(u32x2*)(op + 16 * i) = ntiles > 0 ? u32x2{pack2bf(O[i][0], O[i][1]), pack2bf(O[i][2], O[i][3])}
-                                        : u32x2{0u, 0u};
+    *(u32x2*)(op + 16 * i) = u32x2{pack2bf(O[i][0], O[i][1]), pack2bf(O[i][2], O[i][3])};
 }
 
 // Merge of the split partials fused with the value up-projection: one
@@ -495,30 +589,40 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
 // once.
 namespace {
 constexpr int LO_BG = 8;        // sequences per workgroup
-constexpr int LO_NSMAX = 256;   // split count bound (plan_latent_splits: <= 256)
+constexpr int LO_NSMAX = 256;   // workgroups per sequence (latent_plan: at most 256)
 }
 
-__global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict__ stats,
-                                                         const bf16_t* __restrict__ opart, int nsplit,
-                                                         int B, int H, const bf16_t* __restrict__ w_ukv,
-                                                         bf16_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void latent_out_kernel(DecodeLatentParams p) {
   __shared__ __attribute__((aligned(16))) char otb[LO_BG * 1024];  // o~ bf16, 16-byte chunk c of row r at c ^ r
-  __shared__ float wsc[LO_BG][LO_NSMAX];  // f_s / L per (sequence, split)
+  __shared__ float wsc[LO_BG][LO_NSMAX];  // f_s / L per (sequence, split record)
   __shared__ float lsum[LO_BG][LO_NSMAX];
+  __shared__ int wfirst[LO_BG], wcount[LO_BG];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
+  const int H = p.H, G = p.G;
   const int h = blockIdx.x, b0 = blockIdx.y * LO_BG;
-  const int nb = min(LO_BG, B - b0);
+  const int nb = min(LO_BG, p.B - b0);
   // B operand of k-step s: W_UV,h[c][16 s + 8 lg .. + 7], c = 32 w + lr
-  const bf16_t* wr = w_ukv + ((long)h * 256 + 128 + 32 * w + lr) * 512 + 8 * lg;
+  const bf16_t* wr = p.w_ukv + ((long)h * 256 + 128 + 32 * w + lr) * 512 + 8 * lg;
   bf16x8 wv[32];
 #pragma unroll
   for (int s2 = 0; s2 < 32; ++s2) wv[s2] = *(const bf16x8*)(wr + 16 * s2);
-  // split statistics (m, l) of every (sequence, split), loaded in parallel
+  // the attention kernel's records of sequence b0 + j: wcount[j] of them,
+  // from slot wfirst[j] on
+  if (tid < LO_BG) {
+    const int bb = b0 + tid;
+    wfirst[tid] = tid >= nb ? 0 : p.plan ? p.plan[3 * G + bb] : bb * p.splits;
+    wcount[tid] = tid >= nb ? 0 : p.plan ? p.plan[3 * G + p.B + bb] : p.splits;
+  }
+  __syncthreads();
+  int nsplit = 0;
+#pragma unroll
+  for (int j = 0; j < LO_BG; ++j) nsplit = max(nsplit, wcount[j]);
+  // split statistics (m, l) of every (sequence, record), loaded in parallel
   for (int idx = tid; idx < LO_BG * nsplit; idx += 256) {
     const int j = idx / nsplit, sp = idx - j * nsplit;
-    const bool ok = j < nb;
-    const floatx2 ml = ok ? *(const floatx2*)(stats + 2 * (((long)(b0 + j) * nsplit + sp) * H + h))
+    const bool ok = sp < wcount[j];
+    const floatx2 ml = ok ? *(const floatx2*)(p.stats + 2 * (((long)wfirst[j] + sp) * H + h))
                           : floatx2{-INFINITY, 0.f};
     wsc[j][sp] = ml[0];
     lsum[j][sp] = ml[1];
@@ -528,15 +632,15 @@ __global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict
   if (tid < nb) {
     const int j = tid;
     float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, wsc[j][sp]);
+    for (int sp = 0; sp < wcount[j]; ++sp) M = fmaxf(M, wsc[j][sp]);
     float L = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
+    for (int sp = 0; sp < wcount[j]; ++sp) {
       const float f = exp2f(wsc[j][sp] - M);
       wsc[j][sp] = f;
       L += f * lsum[j][sp];
     }
     const float inv = 1.f / L;
-    for (int sp = 0; sp < nsplit; ++sp) wsc[j][sp] *= inv;
+    for (int sp = 0; sp < wcount[j]; ++sp) wsc[j][sp] *= inv;
   }
   __syncthreads();
   // merged o~: thread (k4, jq) merges features 4 k4 .. +3 of sequences
@@ -546,10 +650,13 @@ __global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict
     const int k4 = tid & 127, jq = tid >> 7;
     floatx4 m[NI];
     const bf16_t* pp[NI];
+    int cnt[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
+      const int j = jq + 2 * i;
       m[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-      pp[i] = opart + ((long)(b0 + jq + 2 * i) * nsplit * H + h) * 512 + 4 * k4;
+      cnt[i] = j < nb ? wcount[j] : 0;
+      pp[i] = p.opart + ((long)wfirst[j] * H + h) * 512 + 4 * k4;
     }
     for (int s0 = 0; s0 < nsplit; s0 += 8) {
       u32x2 v[NI][8];
@@ -557,13 +664,12 @@ __global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          v[i][q] = (jq + 2 * i < nb && s0 + q < nsplit) ? *(const u32x2*)(pp[i] + (long)(s0 + q) * H * 512)
-                                                       : u32x2{0u, 0u};
+          v[i][q] = s0 + q < cnt[i] ? *(const u32x2*)(pp[i] + (long)(s0 + q) * H * 512) : u32x2{0u, 0u};
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          if (s0 + q < nsplit && jq + 2 * i < nb) {
+          if (s0 + q < cnt[i]) {
             const float f = wsc[jq + 2 * i][s0 + q];
             m[i] += f * floatx4{lo_bf(v[i][q][0]), hi_bf(v[i][q][0]), lo_bf(v[i][q][1]), hi_bf(v[i][q][1])};
           }
@@ -589,17 +695,20 @@ __global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int j = 4 * lg + e;
-    if (j < nb) out[(long)(b0 + j) * H * 128 + (long)h * 128 + 32 * w + lr] = f2bf(acc[e]);
+    if (j < nb) p.out[(long)(b0 + j) * H * 128 + (long)h * 128 + 32 * w + lr] = f2bf(acc[e]);
   }
 }
 
 hipError_t decode_latent_bf16(const DecodeLatentParams& p, hipStream_t s) {
-  if (p.H != 64 || !p.w_ukv || p.nsplit > LO_NSMAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_latent_kernel, dim3(p.nsplit, p.B), dim3(256), 0, s, p);
+  if (p.H != 64 || !p.w_ukv) return hipErrorInvalidValue;
+  if (p.plan && (p.G < p.B || p.G > max(p.B, LO_NSMAX) || p.B > LP_NS)) return hipErrorInvalidValue;
+  if (!p.plan && (p.splits < 1 || p.splits > LO_NSMAX || p.G != p.B * p.splits ||
+                  p.splits > (p.L + LT - 1) / LT))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_latent_kernel, dim3(p.G), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(latent_out_kernel, dim3(p.H, (p.B + LO_BG - 1) / LO_BG), dim3(256), 0, s, p.stats,
-                     p.opart, p.nsplit, p.B, p.H, p.w_ukv, p.out);
+  hipLaunchKernelGGL(latent_out_kernel, dim3(p.H, (p.B + LO_BG - 1) / LO_BG), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -641,6 +750,9 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
   __shared__ u32x4 Qs[64 * 16];    // [b 64][c 128]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
+  // the attention kernel's split plan, made by the first workgroup
+  if (p.plan && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    latent_plan(p.B, p.L, p.seq_pos, p.G, p.plan);
   const int h = blockIdx.x, n0 = blockIdx.y * AB_N, b0 = blockIdx.z * 64;
   // W tile: 128 c x AB_N k; item = (c pair, k chunk of 8): 64 x AB_N / 8,
   // all of a thread's loads in flight together
@@ -741,6 +853,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
 
 hipError_t absorb_q_bf16(const AbsorbParams& p, hipStream_t s) {
   if (p.H <= 0 || p.B <= 0) return hipErrorInvalidValue;
+  if (p.plan && (p.B > LP_NS || p.G < p.B)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(absorb_q_kernel, dim3(p.H, 512 / AB_N, (p.B + 63) / 64), dim3(256), 0, s, p);
   return hipGetLastError();
 }

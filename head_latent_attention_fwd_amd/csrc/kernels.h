@@ -212,10 +212,15 @@ hipError_t decode_full_bf16(const DecodeFullParams& p, hipStream_t s);
 struct DecodeLatentParams {
   const bf16_t* q_abs;   // [B][H][576]  [absorbed query q~ (W_UK folded in) | roped q^R]
   const bf16_t* cache;   // [B][L_cap][576]
-  float* stats;          // [B][nsplit][H][2]: running max m (log2 units) and sum l of each split
-  bf16_t* opart;         // [B][nsplit][H][512]: unnormalised o~ of each split
+  float* stats;          // [G][H][2]: running max m (log2 units) and sum l per workgroup
+  bf16_t* opart;         // [G][H][512]: unnormalised o~ per workgroup
   const float* rcos; const float* rsin;  // RoPE table, row L-1 used
-  int B, H, L, L_cap, nsplit;  // each sequence's key tiles are split evenly over nsplit
+  // G workgroups.  With seq_pos, plan (3 G + 2 B ints, written by absorb_q;
+  // G >= B) gives each a key range of one sequence and each sequence its
+  // workgroups; without (one length L for all), plan is NULL and sequence b
+  // has workgroups b * splits .. + splits - 1 (G = B * splits)
+  int B, H, L, L_cap, G, splits;
+  const int* plan;
   float scale_log2;
   const int* seq_pos;  // optional per-sequence positions, as for DecodeFullParams
   // the merge of the splits is fused with the value up-projection (W_UV rows
@@ -235,6 +240,9 @@ struct AbsorbParams {
   const float* rcos; const float* rsin;
   int B, H, L;
   const int* seq_pos;                 // optional: row b roped at seq_pos[b] (clamped to [0, L-1])
+  // optional: the latent attention's split plan for G workgroups, written
+  // here (3 G + 2 B ints; G >= B)
+  int* plan; int G;
 };
 hipError_t absorb_q_bf16(const AbsorbParams& p, hipStream_t s);
 

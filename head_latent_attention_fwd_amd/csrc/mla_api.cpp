@@ -14,6 +14,7 @@
 //            (W1/W3 interleaved, silu(g)*u epilogue) -> W2 GEMM + residual.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -503,7 +504,7 @@ struct DecodePlan {
   void* o_lat;      // [B][H][kv_lora]
   void* apart;      // attention split partials
   int nsplit, chunk;
-  int ns_cap;       // split count the partial buffer was sized for
+  int ns_cap;       // split count (latent form: workgroups) the partial buffer was sized for
   void* opart;      // o_proj split partials ([S2][B][d], or the stream GEMM's blocks)
   size_t opart_floats;
   int S2, kchunk2;
@@ -521,8 +522,15 @@ void plan_full_splits(int B, int H, int L, int* nsplit, int* chunk) {
   *nsplit = (L + ch - 1) / ch;
 }
 
-// latent form: about 256 workgroups in all, at least one 32-key tile each
-// (the kernel deals each sequence's tiles out evenly over the splits)
+// latent form: 256 workgroups (one per CU), fewer when the batch has fewer
+// 32-key tiles at its longest length L, and at least one per sequence; the
+// device-side plan (latent_plan) gives each a run of one sequence's tiles
+int plan_latent_groups(int B, int L) {
+  const long tiles = (long)B * ((L + 31) / 32);
+  const int g = tiles < 256 ? (int)tiles : 256;
+  return g > B ? g : B;
+}
+// one length for all sequences: splits per sequence (about 256 workgroups)
 int plan_latent_splits(int B, int L) {
   int s = (256 + B - 1) / B;
   const int maxs = (L + 31) / 32;
@@ -543,12 +551,12 @@ size_t decode_layout(const mla_dims* d, int B, int L_cap, int form, void* ws, De
   if (cap_f > want_f) cap_f = want_f;
   if (cap_f < (L_cap + 4095) / 4096) cap_f = (L_cap + 4095) / 4096;
   if (cap_f < 1) cap_f = 1;
-  int cap_l = (256 + B - 1) / B;
-  if (cap_l > (L_cap + 31) / 32) cap_l = (L_cap + 31) / 32;
-  if (cap_l < 1) cap_l = 1;
+  // workgroups for any live length <= L_cap, ragged or not
+  const int cap_l = std::max(plan_latent_groups(B, L_cap), B * plan_latent_splits(B, L_cap));
   size_t fpart = (size_t)B * H * cap_f * 130 * 4;
-  // latent form: fp32 (m, l) then bf16 o~[kv_lora] per (sequence, split, head)
-  size_t lpart = (size_t)B * cap_l * H * (2 * 4 + (size_t)kl * 2);
+  // latent form: the split plan (3 G + 2 B ints), then one record per workgroup
+  size_t lpart = ((size_t)(3 * cap_l + 2 * B) * sizeof(int) + 255) / 256 * 256 +
+                 (size_t)cap_l * H * (2 * 4 + (size_t)kl * 2);
   pl->apart = c.take(fpart > lpart ? fpart : lpart);
   pl->ns_cap = form == 0 ? cap_f : cap_l;
   pl->nsplit = 1;
@@ -954,12 +962,15 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
   if (!latent_cache) return fail(MLA_ERR_NULL, "latent_cache is NULL");
   if (d->dtype == MLA_BF16 && (d->kv_lora_rank != 512 || d->n_heads != 64))
     return fail(MLA_ERR_UNSUPPORTED, "bf16 latent decode serves kv_lora 512 and 64 heads");
+  if (d->dtype == MLA_BF16 && B > 1024)
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 latent decode serves batches of up to 1024 sequences");
   DecodePlan pl;
   size_t need = decode_layout(d, B, L_cap, 1, nullptr, &pl);
   if (ws_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   decode_layout(d, B, L_cap, 1, ws, &pl);
-  pl.nsplit = plan_latent_splits(B, P + 1);
+  const int splits = seq_pos ? 0 : plan_latent_splits(B, P + 1);
+  pl.nsplit = seq_pos ? plan_latent_groups(B, P + 1) : B * splits;
   if (pl.nsplit > pl.ns_cap) return fail(MLA_ERR_HIP, "internal: split plan exceeds workspace");
   hipStream_t st = (hipStream_t)stream;
   const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
@@ -976,14 +987,19 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
     ab.qpart = nullptr; ab.qsi = StreamInfo{};
     ab.w_ukv = (const bf16_t*)w->w_ukv; ab.qa = (bf16_t*)pl.q_abs;
     ab.rcos = rc; ab.rsin = rs; ab.B = B; ab.H = H; ab.L = P + 1; ab.seq_pos = seq_pos;
+    // the attention's split plan, then its records: fp32 (m, l) and bf16 o~
+    int* plan = (int*)pl.apart;
+    char* recs = (char*)pl.apart + ((size_t)(3 * pl.ns_cap + 2 * B) * sizeof(int) + 255) / 256 * 256;
+    ab.plan = seq_pos ? plan : nullptr; ab.G = pl.nsplit;
     LAUNCH("absorb_q", absorb_q_bf16(ab, st));
     DecodeLatentParams a;
     a.q_abs = (const bf16_t*)pl.q_abs;
     a.cache = (const bf16_t*)latent_cache;
-    a.stats = (float*)pl.apart;
-    a.opart = (bf16_t*)((char*)pl.apart + (size_t)B * pl.ns_cap * H * 2 * sizeof(float));
+    a.stats = (float*)recs;
+    a.opart = (bf16_t*)(recs + (size_t)pl.ns_cap * H * 2 * sizeof(float));
+    a.plan = ab.plan; a.splits = splits;
     a.rcos = rc; a.rsin = rs;
-    a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit;
+    a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.G = pl.nsplit;
     a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
     a.seq_pos = seq_pos;
     // merge of the splits fused with O_h = o~_h W_UV,h^T

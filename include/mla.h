@@ -56,7 +56,7 @@
  *    query/key head widths up to 1024).  MLA_BF16 requires the Kimi K2 head
  *    widths d_nope = 128, d_rope = 64, d_v = 128 and d_model, q_lora,
  *    kv_lora, H*d_v and d_ff multiples of 64; the latent-cache decode in
- *    bf16 also requires kv_lora = 512 and H = 64.
+ *    bf16 also requires kv_lora = 512, H = 64 and B <= 1024.
  */
 #ifndef MLA_H_
 #define MLA_H_

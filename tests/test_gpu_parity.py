@@ -265,6 +265,10 @@ def test_decode_fullcache_ragged(case):
     ("tiny_f32", ref.TINY, [5, 0, 20], 24, "f32", 81),
     ("kimi_narrow_bf16", KIMI_NARROW, [0, 700, 31, 32], 701, "bf16", 82),
     ("kimi_bf16_splits", ref.KIMI_K2, [8192, 5, 4000], 8193, "bf16", 83),
+    # 40 sequences, most of them a few tiles long and one of 94 tiles: the
+    # split plan gives the long one many workgroups and leaves some idle;
+    # 40 is not a multiple of the merge kernel's 8-sequence groups
+    ("kimi_narrow_bf16_plan", KIMI_NARROW, [(37 * i) % 300 for i in range(39)] + [2999], 3000, "bf16", 84),
 ])
 def test_decode_latentcache_ragged(case):
     name, od, pos, L_cap, dt, seed = case
