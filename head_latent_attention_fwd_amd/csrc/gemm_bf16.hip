@@ -687,6 +687,44 @@ GemmPlan gemm_plan(int M, int N, int K, int batch, int max_split) {
 
 int gemm_pick_cfg(int M, int N, int K, int batch) { return gemm_plan(M, N, K, batch, 1).cfg; }
 
+// Plan for a product of a few hundred rows (64 < M <= 1024), where the tile
+// grid alone leaves most CUs idle and splitting K pays even with the fp32
+// partial traffic.  A time model in seconds, from rates measured on the
+// prefill and chunked-prefill shapes: a CU running one 256x256 tile
+// sustains 5.6 TFLOP/s; a 128x128 tile alone on its CU 2.46 TFLOP/s, two
+// sharing a CU 4.2 TFLOP/s together; 5 us / 3 us of prologue and epilogue
+// per tile; partials move at 5 TB/s.  With fp32_out the product's consumer
+// reads fp32 partials anyway (only the extra splits cost); otherwise the
+// partials are summed into bf16 by reduce_splits (one more launch).
+GemmPlan gemm_plan_small(int M, int N, int K, bool fp32_out, int max_split) {
+  GemmPlan best{GEMM_CFG_128x128, 1, K};
+  double best_t = 1e30;
+  const int kb = (K + 63) / 64;
+  for (int cfg : {GEMM_CFG_256x256, GEMM_CFG_128x128}) {
+    const int b = cfg == GEMM_CFG_256x256 ? 256 : 128;
+    const long tiles = (long)((M + b - 1) / b) * ((N + b - 1) / b);
+    for (int S = 1; S <= max_split; ++S) {
+      const int per = (kb + S - 1) / S;
+      if (S > 1 && per < 8) break;  // keep >= 512 of K per split
+      const int Sr = (kb + per - 1) / per;
+      const long W = tiles * Sr;
+      const double fl = 2.0 * b * b * 64.0 * per;  // FLOPs of one tile
+      double t;
+      if (b == 256) t = (double)((W + 255) / 256) * (fl / 5.6e12 + 5e-6);
+      else if (W <= 256) t = fl / 2.46e12 + 3e-6;
+      else t = (double)((W + 511) / 512) * (2.0 * fl / 4.2e12 + 3e-6);
+      const double mn = (double)M * N;
+      if (fp32_out) t += (Sr - 1) * mn * 8.0 / 5e12;
+      else if (Sr > 1) t += (Sr * mn * 8.0 + mn * 2.0) / 5e12 + 3e-6;
+      if (t < best_t * 0.999) {
+        best_t = t;
+        best = GemmPlan{cfg, Sr, per * 64};
+      }
+    }
+  }
+  return best;
+}
+
 hipError_t gemm_bf16_pair(GemmParams a, GemmParams b, int epi, int cfg, hipStream_t s) {
   GemmParams ps[2] = {a, b};
   for (auto& p : ps) {

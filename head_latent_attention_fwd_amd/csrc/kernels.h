@@ -35,6 +35,8 @@ struct GemmPlan { int cfg, ksplit, kchunk; };
 // tile config and K split (<= max_split; splits need fp32 partial outputs)
 GemmPlan gemm_plan(int M, int N, int K, int batch, int max_split);
 int gemm_pick_cfg(int M, int N, int K, int batch);
+// plan for 64 < M <= 1024 rows (K split with fp32 partials when it pays)
+GemmPlan gemm_plan_small(int M, int N, int K, bool fp32_out, int max_split);
 hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s);
 // Two independent products in one launch (same epilogue and tile config,
 // no batch or K split, at least 8 tiles each); product a's tiles are

@@ -177,6 +177,8 @@ struct ProjBufs {
   size_t upart_floats;
   void* ukvpart;  // ... and of the kv up-projection (its own buffer, so that both
   size_t ukvpart_floats;  // can stay unsummed until the attention kernel reads them)
+  void* opart;    // fp32 K-split partials of o_proj for 64 < M <= 1024 rows (or NULL)
+  size_t opart_floats;
 };
 
 void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, ProjBufs* b) {
@@ -192,7 +194,8 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
   } else if (d->dtype == MLA_BF16) {
     // the down-projection writes fp32 partials that the latent norm sums, so
     // it may split K to balance its few tiles over the CUs
-    const GemmPlan gp = gemm_plan(M, N1, d->d_model, 1, 4);
+    const GemmPlan gp = M <= 1024 ? gemm_plan_small(M, N1, d->d_model, true, 8)
+                                  : gemm_plan(M, N1, d->d_model, 1, 4);
     b->S = gp.ksplit;
     b->kchunk = gp.kchunk;
     b->cfg = gp.cfg;
@@ -228,6 +231,16 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
       void* buf = c.take(need * 4);
       if (i == 0) { b->upart = buf; b->upart_floats = need; }
       else { b->ukvpart = buf; b->ukvpart_floats = need; }
+    }
+  }
+  b->opart = nullptr;
+  b->opart_floats = 0;
+  if (d->dtype == MLA_BF16 && M > 64 && M <= 1024) {
+    const int D = d->d_model, K = d->n_heads * d->v_head_dim;
+    const GemmPlan op = gemm_plan_small(M, D, K, false, 8);
+    if (op.ksplit > 1) {
+      b->opart_floats = (size_t)op.ksplit * M * D;
+      b->opart = c.take(b->opart_floats * 4);
     }
   }
 }
@@ -429,6 +442,20 @@ int run_oproj(const mla_dims* d, const void* w_o, const void* b_o, const void* o
       g.C = out; g.ldc = D;
       return gemm_bf16_out("gemm_o_proj", g, part, part_floats, st);
     }
+    if (M > 64 && M <= 1024 && !R && part) {
+      // a few hundred rows: K split over fp32 partials, summed into bf16
+      const GemmPlan op = gemm_plan_small(M, D, K, false, 8);
+      if (op.ksplit > 1 && (size_t)op.ksplit * M * D <= part_floats) {
+        GemmParams f = g;
+        f.C = part; f.ldc = D;
+        f.ksplit = op.ksplit; f.kchunk = op.kchunk; f.split_stride = (long)M * D;
+        f.bias = nullptr;
+        LAUNCH("gemm_o_proj", gemm_bf16(f, EPI_F32, op.cfg, st));
+        LAUNCH("reduce_splits", reduce_splits<bf16_t>((const float*)part, op.ksplit, (long)M * D, M, D,
+                                                      (bf16_t*)out, D, st, (const bf16_t*)b_o));
+        return MLA_OK;
+      }
+    }
     g.C = out; g.ldc = D;
     if (R) { g.R = (const bf16_t*)R; g.ldr = D; }
     LAUNCH("gemm_o_proj", gemm_bf16(g, R ? EPI_RESID : EPI_BF16, -1, st));
@@ -494,7 +521,7 @@ int prefill_core(const mla_dims* d, const mla_weights* w, const void* x, int B, 
       LAUNCH("scatter_cache", scatter_full_cache<float>((const float*)b.kv, (const float*)b.kr, (float*)k_cache,
                                        (float*)v_cache, B, T, 0, L_cap, H, dn, dr, dv, st));
   }
-  return run_oproj(d, w->w_o, w->b_o, b.o, M, resid, out, nullptr, 0, 1, st);
+  return run_oproj(d, w->w_o, w->b_o, b.o, M, resid, out, b.opart, b.opart_floats, 1, st);
 }
 
 // --------------------------------------------------------------- decode
@@ -833,7 +860,7 @@ static int chunk_impl(const mla_dims* d, const mla_weights* w, const void* x, in
     u.sA = kl; u.sB = (long)(dn + dv) * kl; u.sC = dv;
     LAUNCH("gemm_uv", gemm_f32(u, st));
   }
-  return run_oproj(d, w->w_o, w->b_o, b.o, (int)M, nullptr, out, nullptr, 0, 1, st);
+  return run_oproj(d, w->w_o, w->b_o, b.o, (int)M, nullptr, out, b.opart, b.opart_floats, 1, st);
 }
 
 size_t mla_prefill_chunk_workspace_size(const mla_dims* d, int B, int T, int L_cap) {
