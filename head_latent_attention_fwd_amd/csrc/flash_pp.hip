@@ -82,8 +82,10 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
   const bool second = w >= 4;  // rotated phase
   const int nqt = (p.T + PP_BQ - 1) / PP_BQ;
   const int HB = p.H * p.B;
-  const int qt = nqt - 1 - (int)(blockIdx.x / HB);  // longest query tiles first
-  const int rem = blockIdx.x % HB;
+  const int sp = (int)(blockIdx.x % p.nsplit);           // key split
+  const int wg = (int)(blockIdx.x / p.nsplit);
+  const int qt = nqt - 1 - wg / HB;  // longest query tiles first
+  const int rem = wg % HB;
   const int h = rem % p.H, b = rem / p.H;
   const int q0 = qt * PP_BQ;  // first query row of the tile (query positions are P0 + row)
   const long rowbase = (long)b * p.T;
@@ -91,7 +93,9 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
 
   // positions: this lane's query and the wave's first / last query
   const int qlast = p.P0 + min(q0 + PP_BQ - 1, p.T - 1);
-  const int n_kv = qlast / 64 + 1;
+  // key tiles [k_lo, k_hi) of the tile's qlast / 64 + 1: this split's share
+  const int n_all = qlast / 64 + 1;
+  const int k_lo = sp * n_all / p.nsplit, n_kv = (sp + 1) * n_all / p.nsplit;
   const int qrow_l = q0 + 32 * w + lr;  // query row in the chunk
   const int qi = p.P0 + qrow_l;
   const int wq_first = p.P0 + q0 + 32 * w, wq_last = wq_first + 31;
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
 
   // Prologue loads: the first key tile is issued before the queries, so the
   // two (and the RoPE rows) are in flight together.
-  for (int tt = 0; tt < PP_NST - 2 && tt < n_kv; ++tt) PP_ISSUE(tt);
+  for (int tt = k_lo; tt < k_lo + PP_NST - 2 && tt < n_kv; ++tt) PP_ISSUE(tt);
   // This wave's 32 queries as MFMA B fragments: features 16 s + 8 lg .. +8;
   // the rotary features (s >= 8) are rotated by the RoPE row of the position
   bf16x8 qf[12];
@@ -290,8 +294,8 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
   // buffer whose last reader (PV of the second half) finished before it.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (PP_NST - 2 < n_kv) PP_ISSUE(PP_NST - 2);
-  for (int k = 0; k < n_kv; ++k) {
+  if (k_lo + PP_NST - 2 < n_kv) PP_ISSUE(k_lo + PP_NST - 2);
+  for (int k = k_lo; k < n_kv; ++k) {
     // The fragment offsets are loop-invariant, and left alone the compiler
     // hoists every (offset + immediate) sum out of the loop (over 50 live
     // registers); marking them as redefined here keeps those sums inside the
@@ -324,6 +328,21 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
 #undef PP_VREAD
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (p.nsplit > 1) {
+    // split partial: unnormalised O^T columns and (m, l) of this query
+    if (qrow_l < p.T) {
+      const long rec = ((long)sp * p.B * p.T + rowbase + qrow_l) * HS + h;
+      float* op = p.opart + rec * 128 + 4 * lg;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *(floatx4*)(op + 32 * d + 8 * i) =
+              floatx4{O[d][4 * i + 0], O[d][4 * i + 1], O[d][4 * i + 2], O[d][4 * i + 3]};
+      if (lg == 0) *(floatx2*)(p.ostat + 2 * rec) = floatx2{m_run, l_tot};
+    }
+    return;
+  }
   if (qrow_l < p.T) {
     const float inv = 1.f / l_tot;
     bf16_t* op = p.out + (rowbase + qrow_l) * (HS * 128) + (long)h * 128 + 4 * lg;
@@ -345,6 +364,7 @@ void flash_set_prefill_layout(FlashParams& p) {
   p.vv = p.kv + 128; p.v_b = p.kc_b;             p.v_h = 256;  p.v_kb = p.kc_kb;
   p.kr2 = p.kr;      p.kr_b = (long)p.T * 64;    p.kr_h = 0;   p.kr_kb = 128;
   p.P0 = 0;
+  p.nsplit = 1; p.opart = p.ostat = nullptr;
 }
 
 bool flash_pp_ok(const FlashParams& p) {
@@ -356,8 +376,41 @@ bool flash_pp_ok(const FlashParams& p) {
 
 hipError_t flash_prefill_pp_bf16(const FlashParams& p, hipStream_t s) {
   if (!flash_pp_ok(p)) return hipErrorInvalidValue;
+  if (p.nsplit < 1 || (p.nsplit > 1 && (!p.opart || !p.ostat))) return hipErrorInvalidValue;
   const int nqt = (p.T + PP_BQ - 1) / PP_BQ;
-  hipLaunchKernelGGL(flash_pp_kernel, dim3(nqt * p.H * p.B), dim3(512), 0, s, p);
+  hipLaunchKernelGGL(flash_pp_kernel, dim3(nqt * p.H * p.B * p.nsplit), dim3(512), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  return flash_combine_bf16(p, s);
+}
+
+// Merge of the key splits: one thread per (row, head, 4 features); split s
+// weighs by 2^(m_s - max m) and the sum is divided by sum 2^(m_s - max m) l_s.
+__global__ __launch_bounds__(256) void flash_combine_kernel(const float* __restrict__ opart,
+                                                            const float* __restrict__ ostat, int nsplit,
+                                                            long rows_h, bf16_t* __restrict__ out) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;  // (row, head) * 32 + feature quad
+  if (idx >= rows_h * 32) return;
+  const long rh = idx >> 5;
+  const int f4 = (int)(idx & 31);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ostat[2 * (s * rows_h + rh)]);
+  float L = 0.f;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const floatx2 ml = *(const floatx2*)(ostat + 2 * (s * rows_h + rh));
+    const float f = exp2f(ml[0] - M);
+    L += f * ml[1];
+    acc += f * *(const floatx4*)(opart + (s * rows_h + rh) * 128 + 4 * f4);
+  }
+  const float inv = 1.f / L;
+  *(u32x2*)(out + rh * 128 + 4 * f4) = u32x2{pack2bf(acc[0] * inv, acc[1] * inv), pack2bf(acc[2] * inv, acc[3] * inv)};
+}
+
+hipError_t flash_combine_bf16(const FlashParams& p, hipStream_t s) {
+  const long rows_h = (long)p.B * p.T * p.H;
+  hipLaunchKernelGGL(flash_combine_kernel, dim3((unsigned)((rows_h * 32 + 255) / 256)), dim3(256), 0, s,
+                     p.opart, p.ostat, p.nsplit, rows_h, p.out);
   return hipGetLastError();
 }
 

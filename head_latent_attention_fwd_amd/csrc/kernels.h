@@ -179,7 +179,16 @@ struct FlashParams {
   const bf16_t* kr2; long kr_b, kr_h; int kr_kb;
   const bf16_t* vv;  long v_b, v_h;   int v_kb;
   int P0;
+  // Key split (ping-pong kernel): with nsplit > 1, each (query tile, head)
+  // is spread over nsplit workgroups, each over an even share of its key
+  // tiles; they write unnormalised outputs opart [nsplit][B*T][H][128] and
+  // (m, l) ostat [nsplit][B*T][H][2] (fp32), which flash_combine_bf16 merges
+  // into out.  nsplit = 1: out written directly.
+  int nsplit;
+  float* opart; float* ostat;
 };
+// merge of the key-split partials of flash_prefill_pp_bf16 into p.out
+hipError_t flash_combine_bf16(const FlashParams& p, hipStream_t s);
 hipError_t flash_prefill_bf16(const FlashParams& p, hipStream_t s);
 // the key/value source fields for the prefill layout (kv [B*T][H][256], kr [B*T][64])
 void flash_set_prefill_layout(FlashParams& p);

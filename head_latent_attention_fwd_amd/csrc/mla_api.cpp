@@ -471,13 +471,31 @@ int run_oproj(const mla_dims* d, const void* w_o, const void* b_o, const void* o
   return MLA_OK;
 }
 
+// Key splits of the flash attention: when the (query tile, head, sequence)
+// workgroups are fewer than the CUs, each one's key tiles are shared out
+// over up to 256 / workgroups splits of at least 8 tiles (64 keys each).
+static int flash_splits(int B, int T, int H, int P0) {
+  const long wgs = (long)((T + 255) / 256) * H * B;
+  if (wgs >= 256) return 1;
+  const int n_min = (P0 + std::min(255, T - 1)) / 64 + 1;  // tiles of the first query tile
+  const int s = std::min((int)(256 / wgs), n_min / 8);
+  return s < 1 ? 1 : s;
+}
+static size_t flash_split_floats(int B, int T, int H, int P0) {
+  const int s = flash_splits(B, T, H, P0);
+  return s > 1 ? (size_t)s * B * T * H * (128 + 2) : 0;
+}
+
 struct PrefillPlan {
   ProjBufs pb;
+  float* fpart;  // flash key-split partials (NULL: no split): outputs, then (m, l)
 };
 
 size_t prefill_layout(const mla_dims* d, int B, int T, void* ws, PrefillPlan* pl) {
   Carver c(ws);
   carve_proj(c, d, B * T, true, false, &pl->pb);
+  const size_t ff = d->dtype == MLA_BF16 ? flash_split_floats(B, T, d->n_heads, 0) : 0;
+  pl->fpart = ff ? (float*)c.take(ff * 4) : nullptr;
   return c.off + 256;
 }
 
@@ -492,10 +510,14 @@ int prefill_core(const mla_dims* d, const mla_weights* w, const void* x, int B, 
   if (rc_) return rc_;
   if (d->dtype == MLA_BF16) {
     FlashParams f;
+    memset(&f, 0, sizeof f);
     f.q = (const bf16_t*)b.q; f.kv = (const bf16_t*)b.kv; f.kr = (const bf16_t*)b.kr;
     f.out = (bf16_t*)b.o; f.B = B; f.T = T; f.H = H; f.rcos = rc; f.rsin = rs;
     f.scale_log2 = d->softmax_scale * 1.4426950408889634f;
     flash_set_prefill_layout(f);
+    f.nsplit = pl.fpart ? flash_splits(B, T, H, 0) : 1;
+    f.opart = pl.fpart;
+    f.ostat = pl.fpart ? pl.fpart + (size_t)f.nsplit * M * H * 128 : nullptr;
     if (flash_pp_ok(f)) LAUNCH("flash_prefill", flash_prefill_pp_bf16(f, st));
     else LAUNCH("flash_prefill", flash_prefill_bf16(f, st));
   } else {
@@ -729,6 +751,7 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int B, i
 // (float32).
 struct ChunkPlan {
   ProjBufs pb;
+  float* fpart;  // flash key-split partials, sized for the largest P0 (NULL: no split)
   void* kv_exp;  // bf16 latent form: [B][L_cap][H*(dn+dv)]
   void* q_abs;   // float32 latent form: [B*T][H][kv_lora]
   void* o_lat;   // float32 latent form: [B*T][H][kv_lora]
@@ -739,6 +762,9 @@ static size_t chunk_layout(const mla_dims* d, int B, int T, int L_cap, int form,
   const size_t es = esize(d);
   const int H = d->n_heads;
   carve_proj(c, d, B * T, form == 0, false, &pl->pb);
+  // key splits only grow with P0: size them for the largest, L_cap - T
+  const size_t ff = d->dtype == MLA_BF16 ? flash_split_floats(B, T, H, std::max(0, L_cap - T)) : 0;
+  pl->fpart = ff ? (float*)c.take(ff * 4) : nullptr;
   pl->kv_exp = pl->q_abs = pl->o_lat = nullptr;
   if (form == 1 && d->dtype == MLA_BF16)
     pl->kv_exp = c.take((size_t)B * L_cap * H * (d->qk_nope_dim + d->v_head_dim) * es);
@@ -814,6 +840,9 @@ static int chunk_impl(const mla_dims* d, const mla_weights* w, const void* x, in
     }
     if (!flash_pp_ok(f))
       return fail(MLA_ERR_UNSUPPORTED, "chunked prefill: cache rows too long for 32-bit offsets");
+    f.nsplit = pl.fpart ? flash_splits(B, T, H, P0) : 1;
+    f.opart = pl.fpart;
+    f.ostat = pl.fpart ? pl.fpart + (size_t)f.nsplit * M * H * 128 : nullptr;
     LAUNCH("flash_prefill", flash_prefill_pp_bf16(f, st));
   } else if (form == 0) {
     LAUNCH("scatter_cache", scatter_full_cache<float>((const float*)b.kv, (const float*)b.kr, (float*)k_cache,

@@ -327,6 +327,11 @@ def test_ragged_decode_uniform_and_clamped(form):
     ("kimi_bf16", ref.KIMI_K2, 1, 300, 700, 1024, "bf16", 113),
     ("kimi_bf16_P0_0", ref.KIMI_K2, 1, 130, 0, 200, "bf16", 114),
     ("kimi_bf16_one_token", ref.KIMI_K2, 2, 1, 777, 800, "bf16", 115),
+    # few query tiles against a long history: the attention splits each
+    # (query tile, head)'s keys over 4, 2 and 2 workgroups
+    ("kimi_bf16_keysplit4", ref.KIMI_K2, 1, 200, 2000, 2200, "bf16", 116),
+    ("kimi_bf16_keysplit2", ref.KIMI_K2, 1, 300, 1700, 2000, "bf16", 117),
+    ("kimi_bf16_keysplit_one_token", ref.KIMI_K2, 2, 1, 4000, 4001, "bf16", 118),
 ])
 @pytest.mark.parametrize("form", ["full", "latent"])
 def test_prefill_chunk(case, form):
