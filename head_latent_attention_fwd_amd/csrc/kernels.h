@@ -50,20 +50,30 @@ int skinny_splits(int K);
 hipError_t gemm_skinny_bf16(GemmParams p, bool bf16_out, hipStream_t s);
 
 // Balanced weight-streaming GEMM (M <= 64): units of 128 weight rows x 128 k
-// dealt out to G workgroups in equal runs; each writes <= 2 fp32 partial
-// blocks [Mp][128] (slots 2 w and 2 w + 1), summed per n-block in workgroup
-// order by stream_reduce / stream_sum4.
+// dealt out to G workgroups in equal runs; each writes its fp32 partial
+// blocks [Mp][128] (at most NS per workgroup and product) to slots
+// (w - w0) NS + j, summed per n-block in workgroup order by stream_reduce /
+// stream_sum4.  One launch may stream two products (same rows M): the
+// second's units follow the first's.
 struct StreamInfo {
-  int G;    // workgroups
-  int U;    // units = NB * KS
-  int KS;   // units per 128-column block (K / 128)
-  int NB;   // 128-column blocks
+  int G;    // workgroups of the launch
+  int U;    // units of the launch (both products)
+  int KS;   // units per 128-column block of this product (K / 128)
+  int NB;   // 128-column blocks of this product
   int Mp;   // padded rows per partial block (32 or 64)
+  int u0;   // this product's first unit in the launch
+  int w0;   // first workgroup holding this product's units
+  int NS;   // partial slots per workgroup
 };
 bool stream_ok(const GemmParams& p);  // M <= 64, K % 128 == 0, N % 4 == 0, b_split % 128 == 0
 StreamInfo stream_info(int M, int N, int K);
 size_t stream_part_floats(const StreamInfo& s);
 hipError_t gemm_stream_bf16(const GemmParams& p, float* part, const StreamInfo& s, hipStream_t st);
+// Two products in one launch (same M; no b_split on the second): false when
+// some workgroup would hold more than three 128-column blocks.
+bool stream_pair_info(const GemmParams& a, const GemmParams& b, StreamInfo* sa, StreamInfo* sb);
+hipError_t gemm_stream_bf16_pair(const GemmParams& a, const GemmParams& b, float* part_a, float* part_b,
+                                 const StreamInfo& sa, const StreamInfo& sb, hipStream_t st);
 // out[m, n] = sum of the partials (+ R[m, n] when R is not NULL) (+ bias[n]
 // when bias is not NULL)
 template <typename T>
@@ -100,8 +110,6 @@ template <typename T> struct LatentNormParams {
   // optional latent cache [B][L_cap][kv_lora + d_rope]: row m = b*rope_T + t
   // goes to slot t + rope_pos0 of sequence b
   T* latent_cache; int L_cap;
-  // optional full key cache [B][H][L_cap][dqk]: k^R copied to every head
-  T* k_cache; int n_heads; int dqk; int d_nope;
   // stream != 0: `part` holds the weight-streaming GEMM's partial blocks
   // (StreamInfo si), summed here instead of the nsplit fp32 slices
   int stream; StreamInfo si;

@@ -219,12 +219,23 @@ void carve_proj(Carver& c, const mla_dims* d, int M, bool need_kv, bool splitk, 
     // prefill / chunk of at most 64 rows: the small-M products split K)
     const int shapes[2][2] = {{H * dqk, d->q_lora_rank},
                               {H * (d->qk_nope_dim + d->v_head_dim), d->kv_lora_rank}};
+    // (decode with kv: both up-projections may stream in one launch)
+    StreamInfo pair[2];
+    bool paired = false;
+    if (M <= 64 && need_kv) {
+      GemmParams a = gp_base(), bb = gp_base();
+      a.M = bb.M = M;
+      a.N = shapes[0][0]; a.K = a.lda = a.ldb = shapes[0][1];
+      bb.N = shapes[1][0]; bb.K = bb.lda = bb.ldb = shapes[1][1];
+      paired = stream_pair_info(a, bb, &pair[0], &pair[1]);
+    }
     for (int i = 0; i < 2; ++i) {
       if (i == 1 && !need_kv) break;
       const int S = skinny_splits(shapes[i][1]);
       size_t need = S > 1 ? (size_t)S * M * shapes[i][0] : 0;
       if (M <= 64) {
-        const size_t sf = stream_part_floats(stream_info(M, shapes[i][0], shapes[i][1]));
+        size_t sf = stream_part_floats(stream_info(M, shapes[i][0], shapes[i][1]));
+        if (paired) sf = std::max(sf, stream_part_floats(pair[i]));
         if (sf > need) need = sf;
       }
       if (!need) continue;
@@ -379,6 +390,14 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
         (void)hipGetLastError();
       }
     }
+    if (defer && b.kv && b.upart && b.ukvpart && stream_pair_info(q, k, &defer[0], &defer[1]) &&
+        stream_part_floats(defer[0]) <= b.upart_floats && stream_part_floats(defer[1]) <= b.ukvpart_floats) {
+      // decode: both up-projections stream in one launch and stay as partials
+      LAUNCH("gemm_qkv_up", gemm_stream_bf16_pair(q, k, (float*)b.upart, (float*)b.ukvpart, defer[0],
+                                                  defer[1], st));
+      return MLA_OK;
+    }
+    if (defer) defer[0].G = defer[1].G = 0;
     if (!(defer && gemm_stream_deferred("gemm_q_up", q, b.upart, b.upart_floats, st, &defer[0], &r_)))
       r_ = gemm_bf16_out("gemm_q_up", q, b.upart, b.upart_floats, st);
     if (r_) return r_;

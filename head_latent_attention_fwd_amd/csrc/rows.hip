@@ -148,13 +148,6 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
       lat[p.kv_lora + 2 * i] = y0;
       lat[p.kv_lora + 2 * i + 1] = y1;
     }
-    if (p.k_cache) {
-      for (int h = 0; h < p.n_heads; ++h) {
-        T* kc = p.k_cache + (((long)bseq * p.n_heads + h) * p.L_cap + pos) * p.dqk + p.d_nope;
-        kc[2 * i] = y0;
-        kc[2 * i + 1] = y1;
-      }
-    }
   }
 }
 

@@ -10,13 +10,24 @@ constexpr int SU_N = 128;  // weight rows (output columns) per unit
 constexpr int SU_K = 128;  // k per unit
 
 // first unit of workgroup w: units are dealt out as equal contiguous runs
-MLA_DEV inline int su_start(const StreamInfo& s, int w) { return (int)(((long)w * s.U) / s.G); }
+// (w U < 2^31: U is at most a few hundred thousand units)
+MLA_DEV inline int su_start(const StreamInfo& s, int w) { return w * s.U / s.G; }
 
-// Workgroups [wa, wb] hold the units of 128-column block nb.
+// Workgroups [wa, wb] hold the units of this product's 128-column block nb.
 MLA_DEV inline void su_span(const StreamInfo& s, int nb, int& wa, int& wb) {
-  const int ua = nb * s.KS, ub = ua + s.KS - 1;
-  wa = (int)(((long)(ua + 1) * s.G - 1) / s.U);  // workgroup holding unit ua
-  wb = (int)(((long)(ub + 1) * s.G - 1) / s.U);  // ... and unit ub
+  const int ua = s.u0 + nb * s.KS, ub = ua + s.KS - 1;
+  wa = ((ua + 1) * s.G - 1) / s.U;  // workgroup holding unit ua
+  wb = ((ub + 1) * s.G - 1) / s.U;  // ... and unit ub
+}
+
+// Partial slot of workgroup w's part of block nb: its blocks of this
+// product are numbered from the one holding its first unit of the product
+// (w holds units of nb, so that one is nb, nb - 1 or nb - 2).
+MLA_DEV inline long su_slot(const StreamInfo& s, int w, int nb) {
+  const int f = max(su_start(s, w), s.u0);
+  const int ua = s.u0 + nb * s.KS;
+  const int j = f >= ua ? 0 : (f >= ua - s.KS ? 1 : 2);
+  return (long)(w - s.w0) * s.NS + j;
 }
 
 // Sum of C[m][n .. n+3] over the partial slots of n's 128-column block, in
@@ -33,8 +44,7 @@ MLA_DEV inline floatx4 stream_sum4(const float* __restrict__ part, const StreamI
     for (int q = 0; q < 8; ++q) {
       const int w = w0 + q;
       if (w <= wb) {
-        const int j = su_start(s, w) / s.KS == nb ? 0 : 1;
-        v[q] = *(const floatx4*)(part + ((long)(2 * w + j) * s.Mp + m) * SU_N + nl);
+        v[q] = *(const floatx4*)(part + (su_slot(s, w, nb) * s.Mp + m) * SU_N + nl);
       } else {
         v[q] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
@@ -62,8 +72,7 @@ MLA_DEV inline void stream_sum8_rows(const float* __restrict__ part, const Strea
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int w = w0 + q;
-      const int j = w <= wb && su_start(s, w) / s.KS != nb ? 1 : 0;
-      const float* base = part + (long)(2 * w + j) * s.Mp * SU_N + nl;
+      const float* base = part + (w <= wb ? su_slot(s, w, nb) : 0) * s.Mp * SU_N + nl;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const bool go = w <= wb && ok[r];
