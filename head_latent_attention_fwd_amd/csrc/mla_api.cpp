@@ -1051,15 +1051,17 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
   const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
   const int kl = d->kv_lora_rank, dqk = dn + dr;
   const ProjBufs& b = pl.pb;
-  // q is summed by its own reduction here: spread over the absorption
-  // kernel's 512 workgroups, the partial sums measured slower than that
-  if ((r = run_projections(d, w, x, B, 1, P, rc, rs, b, latent_cache, L_cap, st, nullptr, seq_pos, P)))
+  // bf16: the q up-projection stays as weight-stream partials, summed by the
+  // absorption kernel as it loads q (no reduction launch)
+  StreamInfo def[2];
+  if ((r = run_projections(d, w, x, B, 1, P, rc, rs, b, latent_cache, L_cap, st,
+                           d->dtype == MLA_BF16 ? def : nullptr, seq_pos, P)))
     return r;
   if (d->dtype == MLA_BF16) {
     // [q~ | roped q^R] per head
     AbsorbParams ab;
     ab.q = (const bf16_t*)b.q;
-    ab.qpart = nullptr; ab.qsi = StreamInfo{};
+    ab.qpart = def[0].G > 0 ? (const float*)b.upart : nullptr; ab.qsi = def[0];
     ab.w_ukv = (const bf16_t*)w->w_ukv; ab.qa = (bf16_t*)pl.q_abs;
     ab.rcos = rc; ab.rsin = rs; ab.B = B; ab.H = H; ab.L = P + 1; ab.seq_pos = seq_pos;
     // the attention's split plan, then its records: fp32 (m, l) and bf16 o~

@@ -68,10 +68,12 @@ MLA_DEV float down_bias(const LatentNormParams<T>& p, int c) {
   return p.bias_kvr ? to_f<T>(p.bias_kvr[c - p.q_lora]) : 0.f;
 }
 
-// One workgroup of NT threads per row: sum the down-projection partials of
-// the row in a fixed order (deterministic) -- either nsplit fp32 K-slices or
-// the weight-streaming GEMM's partial blocks -- then the two RMSNorms and the
-// RoPE of the shared key, with the optional cache writes.
+// Workgroups of NT threads per row: sum the down-projection partials of the
+// row in a fixed order (deterministic) -- either nsplit fp32 K-slices or the
+// weight-streaming GEMM's partial blocks -- then the RMSNorms and the RoPE of
+// the shared key, with the optional cache writes.  With gridDim.y = 2 the
+// two halves of a row go to two workgroups: y = 0 the query latent and its
+// norm, y = 1 the kv latent, its norm and the rotary key.
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T> p) {
   extern __shared__ float row[];  // [q_lora + kv_lora + d_rope]
@@ -79,11 +81,14 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
   const int N1 = p.q_lora + p.kv_lora + p.d_rope;
+  const bool do_q = gridDim.y == 1 || blockIdx.y == 0;
+  const bool do_kv = gridDim.y == 1 || blockIdx.y == 1;
+  const int c_lo = do_q ? 0 : p.q_lora, c_hi = do_kv ? N1 : p.q_lora;
   float sq = 0.f, skv = 0.f;
   // 4 columns per thread and iteration, all splits' loads in flight together
-  const bool vec = (N1 % 4 == 0) && (p.ld_part % 4 == 0) && (p.split_stride % 4 == 0);
+  const bool vec = (N1 % 4 == 0) && (p.ld_part % 4 == 0) && (p.split_stride % 4 == 0) && (c_lo % 4 == 0);
   if (p.stream) {
-    for (int c4 = tid; c4 < N1 / 4; c4 += NT) {
+    for (int c4 = c_lo / 4 + tid; c4 < c_hi / 4; c4 += NT) {
       const floatx4 v = stream_sum4(p.part, p.si, m, 4 * c4);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
       }
     }
   } else if (vec) {
-    for (int c4 = tid; c4 < N1 / 4; c4 += NT) {
+    for (int c4 = c_lo / 4 + tid; c4 < c_hi / 4; c4 += NT) {
       const floatx4 v = sum_splits4(p.part + (long)m * p.ld_part + 4 * c4, p.split_stride, p.nsplit);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
       }
     }
   } else {
-    for (int c = tid; c < N1; c += NT) {
+    for (int c = c_lo + tid; c < c_hi; c += NT) {
       float v = 0.f;
       for (int s = 0; s < p.nsplit; ++s)
         v += p.part[(long)s * p.split_stride + (long)m * p.ld_part + c];
@@ -117,10 +122,13 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
       else if (c < p.q_lora + p.kv_lora) skv += v * v;
     }
   }
-  const float tq = block_sum<NT>(sq, red);
-  const float tkv = block_sum<NT>(skv, red);
-  const float rq = 1.0f / sqrtf(tq / (float)p.q_lora + p.eps);
-  const float rkv = 1.0f / sqrtf(tkv / (float)p.kv_lora + p.eps);
+  if (do_q) {
+    const float rq = 1.0f / sqrtf(block_sum<NT>(sq, red) / (float)p.q_lora + p.eps);
+    for (int c = tid; c < p.q_lora; c += NT)
+      p.cq[(long)m * p.ld_cq + c] = from_f<T>(to_f<T>(p.g_q[c]) * (row[c] * rq));
+  }
+  if (!do_kv) return;
+  const float rkv = 1.0f / sqrtf(block_sum<NT>(skv, red) / (float)p.kv_lora + p.eps);
 
   const int t = m % p.rope_T;
   const int pos = p.seq_pos ? seq_position(p.seq_pos, m, 0, p.pos_max) : t + p.rope_pos0;
@@ -129,8 +137,6 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
                ? p.latent_cache + ((long)bseq * p.L_cap + pos) * (p.kv_lora + p.d_rope)
                : nullptr;
 
-  for (int c = tid; c < p.q_lora; c += NT)
-    p.cq[(long)m * p.ld_cq + c] = from_f<T>(to_f<T>(p.g_q[c]) * (row[c] * rq));
   for (int c = tid; c < p.kv_lora; c += NT) {
     T y = from_f<T>(to_f<T>(p.g_kv[c]) * (row[p.q_lora + c] * rkv));
     p.ckv[(long)m * p.ld_ckv + c] = y;
@@ -157,10 +163,13 @@ hipError_t latent_norm_rope(const LatentNormParams<T>& p, hipStream_t s) {
   if (p.stream && (p.q_lora + p.kv_lora + p.d_rope) % 4) return hipErrorInvalidValue;
   // few rows (decode): a wide workgroup keeps the partial loads of a row in
   // flight together
+  // the query and kv halves of a row in workgroups of their own when the
+  // split falls on a 4-column boundary
+  const dim3 g(p.M, p.q_lora % 4 == 0 ? 2 : 1);
   if (p.M <= 64)
-    hipLaunchKernelGGL((latent_norm_rope_kernel<T, 1024>), dim3(p.M), dim3(1024), shm, s, p);
+    hipLaunchKernelGGL((latent_norm_rope_kernel<T, 1024>), g, dim3(1024), shm, s, p);
   else
-    hipLaunchKernelGGL((latent_norm_rope_kernel<T, 256>), dim3(p.M), dim3(256), shm, s, p);
+    hipLaunchKernelGGL((latent_norm_rope_kernel<T, 256>), g, dim3(256), shm, s, p);
   return hipGetLastError();
 }
 template hipError_t latent_norm_rope<float>(const LatentNormParams<float>&, hipStream_t);
