@@ -73,13 +73,19 @@ struct ProfScope {
   hipStream_t st;
   hipEvent_t a = nullptr;
   ProfScope(const char* n, hipStream_t s) : name(n), st(s) {
-    if (g_prof && (a = prof_event())) hipEventRecord(a, st);
+    if (g_prof && (a = prof_event()) && hipEventRecord(a, st) != hipSuccess) {
+      g_prof_pool.push_back(a);  // not recorded: no sample for this launch
+      a = nullptr;
+    }
   }
   ~ProfScope() {
     if (!a) return;
     hipEvent_t b = prof_event();
-    if (!b) return;
-    hipEventRecord(b, st);
+    if (!b || hipEventRecord(b, st) != hipSuccess) {
+      g_prof_pool.push_back(a);
+      if (b) g_prof_pool.push_back(b);
+      return;
+    }
     g_prof_pending.push_back({name, a, b});
   }
 };
