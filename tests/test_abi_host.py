@@ -159,6 +159,13 @@ def test_unsupported_rejected():
     st = L.mla_decode_latentcache(ctypes.byref(d), ctypes.byref(_w()), FAKE, 2, 3, 16, FAKE, FAKE,
                                   FAKE, 16, FAKE, FAKE, 1 << 40, None)
     assert st == -3
+    d = kimi()                                      # bf16 latent decode: at most 1024 sequences
+    st = L.mla_decode_latentcache(ctypes.byref(d), ctypes.byref(_w()), FAKE, 1025, 3, 16, FAKE, FAKE,
+                                  FAKE, 16, FAKE, FAKE, 1 << 40, None)
+    assert st == -3 and "1024" in L.mla_last_error().decode()
+    st = L.mla_decode_latentcache(ctypes.byref(d), ctypes.byref(_w()), FAKE, 1024, 3, 16, FAKE, FAKE,
+                                  FAKE, 16, FAKE, FAKE, 1, None)
+    assert st == -4                                 # 1024 passes the batch check, then the workspace one
 
 
 def test_small_workspace_rejected():
