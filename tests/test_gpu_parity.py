@@ -289,6 +289,32 @@ def test_decode_latentcache_ragged(case):
         assert_close(cdf[b, P], cc2[b, P], tol, f"{name} latent slot {P}")
 
 
+def test_decode_latentcache_max_batch():
+    """The largest batch the bf16 latent decode serves, 1024 sequences: one
+    length for all, then ragged positions in [0, 40] (the device split plan
+    then gives every sequence one workgroup and fills its 1024-entry tables).
+    Sequences are independent, so the oracle runs on a sample of them."""
+    od = KIMI_NARROW
+    log("[decode latent max batch] B=1024 P=40 L_cap=48 bf16 uniform")
+    got, want, *_ = _decode_latent_case(od, 1024, 40, 48, "bf16", 95, sample=[0, 1, 511, 1000, 1023])
+    assert_close(got, want, TOL_BF16, "decode latent B=1024 sampled")
+    pos = [(7 * i) % 41 for i in range(1024)]
+    log("[decode latent max batch] B=1024 ragged positions in [0, 40] L_cap=48 bf16")
+    x, w, cc = synth.decode_latent_inputs(od, 1024, 40, 48, 96, bf16=True)
+    cd = bits_to_dev(cc, "bf16", DEV)
+    got = mla.mla_decode_latentcache_ragged(dims_of(mla, od, "bf16"), weights_to_dev(w, "bf16", DEV),
+                                            to_dev(x, "bf16", DEV), _pos_dev(pos), 40, cd, _rope(od, 41))
+    torch.cuda.synchronize()
+    bs = [0, 5, 40, 41, 512, 1023]
+    cf = synth.as_f32(cc[bs], True).astype(np.float64)
+    want, cc2 = ref.mla_decode_latentcache_ragged(od, oracle_weights(w), x[bs].astype(np.float64),
+                                                  [pos[b] for b in bs], cf)
+    assert_close(from_dev(got)[bs], want, TOL_BF16, "decode latent ragged B=1024 sampled")
+    cdf = from_dev(cd)
+    for i, b in enumerate(bs):
+        assert_close(cdf[b, pos[b]], cc2[i, pos[b]], TOL_BF16, f"latent slot {pos[b]} of sequence {b}")
+
+
 @pytest.mark.parametrize("form", ["full", "latent"])
 def test_ragged_decode_uniform_and_clamped(form):
     """Equal positions give the uniform entry point's result bit for bit;
