@@ -27,6 +27,7 @@ struct GemmParams {
   int batch;
   long sA, sB, sC;   // batch strides in elements
   int tiles_m, tiles_n;  // filled by the launcher
+  int group_m;           // M tiles per group of the tile order (launcher)
   const bf16_t* bias;    // optional per-output-column bias [N] (bf16-output
                          // epilogues: EPI_BF16, EPI_RESID, the skinny kernel)
 };
