@@ -189,6 +189,28 @@ def bench_prefill(torch, mla, dev, steps, warmup, k=KIMI, B=1, T=2048):
     return {"ms": ms, "ms_with_kernel_events": ms_ev, "wall_s": wall, "flops": total, "kernels": kern, "w": w, "d": d}
 
 
+def bench_prefill_bias(torch, mla, dev, d, w, steps, warmup, k=KIMI, B=1, T=2048):
+    """The headline prefill in the attention_bias variant: biases on the two
+    down-projections and on o_proj, added in the kernels' epilogues.  The
+    FLOP count is the headline's (the bias adds are not counted)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(1007)
+    wb = dict(w)
+    for n, shp in mla.bias_shapes(d).items():
+        wb[n] = (torch.randn(shp, generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    x = torch.randn(B, T, k["d_model"], generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    rope = mla.mla_rope_table(T, k["qk_rope_dim"], 10000.0, dev)
+    out = torch.empty_like(x)
+    ws = torch.empty(mla.prefill_workspace_size(d, B, T), dtype=torch.uint8, device=dev)
+    fn = lambda: mla.mla_prefill(d, wb, x, rope, out=out, workspace=ws)  # noqa: E731
+    warm(torch, fn, warmup)
+    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps)
+    flops = sum(v for n, v in prefill_kernel_flops(B, T, k).items() if n != "gemm_qkv_up")
+    return {"workload": f"Kimi K2 MLA prefill with attention_bias (q_a, kv_a and o_proj biases), bf16, B={B}, T={T}",
+            "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev,
+            "tflops": flops / (ms * 1e-3) / 1e12, "kernels": kern}
+
+
 def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000):
     k = KIMI
     L_cap = P + 1
@@ -373,7 +395,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode_full", "decode_latent", "decode_latent_ragged",
-                                       "chunk_full", "chunk_latent", "block", "copy"])
+                                       "prefill_bias", "chunk_full", "chunk_latent", "block", "copy"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -412,6 +434,7 @@ def main():
               "decode_latent": lambda: bench_decode_latent(torch, mla, dev, d, w, args.steps, args.warmup, flush),
               "decode_latent_ragged": lambda: bench_decode_latent_ragged(torch, mla, dev, d, w, args.steps,
                                                                          args.warmup, flush),
+              "prefill_bias": lambda: bench_prefill_bias(torch, mla, dev, d, w, args.steps, args.warmup),
               "chunk_full": lambda: bench_prefill_chunk(torch, mla, dev, d, w, args.steps, args.warmup, "full"),
               "chunk_latent": lambda: bench_prefill_chunk(torch, mla, dev, d, w, args.steps, args.warmup, "latent"),
               "block": lambda: bench_block(torch, mla, dev, d, w, args.steps, args.warmup)}[args.only]
@@ -448,6 +471,7 @@ def main():
         for name, fn in (("decode_fullcache", lambda: bench_decode_full(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
                          ("decode_latentcache", lambda: bench_decode_latent(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
                          ("decode_latentcache_ragged", lambda: bench_decode_latent_ragged(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
+                         ("prefill_attention_bias", lambda: bench_prefill_bias(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3)),
                          ("prefill_chunk_fullcache", lambda: bench_prefill_chunk(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, "full")),
                          ("prefill_chunk_latentcache", lambda: bench_prefill_chunk(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, "latent")),
                          ("dense_block", lambda: bench_block(torch, mla, dev, r["d"], r["w"], max(3, args.steps // 4), 2))):
