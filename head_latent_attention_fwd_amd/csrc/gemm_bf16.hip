@@ -480,6 +480,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmGroup gg) {
     constexpr int NSL = CH8 < 16 ? CH8 : 16;
     static_assert(BM * ROWB <= (int)sizeof(lds_raw), "epilogue staging does not fit the LDS");
     char* cst = (char*)&lds[0][0];
+    // bias of this lane's output columns (the same for all its rows), loaded
+    // once; columns past the output read as zero
+    float bcol[EPI == EPI_SWIGLU ? 1 : FN][4][4];
+    if (EPI != EPI_SWIGLU && bias) {
+#pragma unroll
+      for (int j = 0; j < (EPI == EPI_SWIGLU ? 1 : FN); ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int cc = on0 + tcol(j, g) + q;
+            bcol[j][g][q] = cc < out_cols ? bf2f(bias[cc]) : 0.f;
+          }
+    }
     __syncthreads();  // last K tile read
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -499,11 +513,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmGroup gg) {
               v[q] = acc[i][j][4 * g + q];
             }
           }
-          if (bias) {
+          if (EPI != EPI_SWIGLU && bias) {
             // o_proj of the attention_bias variant: y = x W^T + b
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (on0 + c + q < out_cols) v[q] += bf2f(bias[on0 + c + q]);
+            for (int q = 0; q < 4; ++q) v[q] += bcol[EPI == EPI_SWIGLU ? 0 : j][g][q];
           }
           *(u32x2*)(cst + r * ROWB + 16 * ((c >> 3) ^ (r % NSL)) + 8 * ((c >> 2) & 1)) =
               u32x2{pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
