@@ -11,7 +11,6 @@ There is no fallback: if ``libmla.so`` has not been built, every call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -119,8 +118,10 @@ def _check(status):
 
 def make_dims(d_model, n_heads, q_lora_rank, kv_lora_rank, qk_nope_dim, qk_rope_dim, v_head_dim,
               d_ff=0, rms_eps=1e-6, softmax_scale=None, dtype="bf16") -> Dims:
+    """mla_dims of one layer.  softmax_scale None passes 0, for which the
+    library uses its documented default."""
     if softmax_scale is None:
-        softmax_scale = 1.0 / math.sqrt(qk_nope_dim + qk_rope_dim)
+        softmax_scale = 0.0
     dt = MLA_BF16 if dtype in ("bf16", torch.bfloat16, MLA_BF16) else MLA_F32
     return Dims(d_model, n_heads, q_lora_rank, kv_lora_rank, qk_nope_dim, qk_rope_dim, v_head_dim,
                 d_ff, rms_eps, softmax_scale, dt)

@@ -1,14 +1,14 @@
 // Causal flash attention for the MLA prefill, bf16 with fp32 softmax, gfx950:
 // ping-pong form.
 //
-// What it computes is what flash_prefill.hip computes ("Kimi K2 · Mix and
-// project", code excerpt; query/key assembly of "Kimi K2 · Dense transformer
-// block"): s_ij = scale * [Q^C ; Q^R]_i . [K^C_h ; k^R]_j over keys j <= i,
-// a float32 softmax over j, O_i = sum_j p_ij V_h,j, written into the
+// What it computes ("Kimi K2 · Mix and project", code excerpt; query/key
+// assembly of "Kimi K2 · Dense transformer block"):
+// s_ij = scale * [Q^C ; Q^R]_i . [K^C_h ; k^R]_j over keys j <= i, a float32
+// softmax over j, O_i = sum_j p_ij V_h,j, written into the
 // head-merged layout [B*T, H*128].  RoPE of the query's rotary part is applied
 // as the query fragments are loaded.
 //
-// Why a second form: with one barrier per key tile, all eight waves run the
+// Why ping-pong: with one barrier per key tile, all eight waves run the
 // QK products, the softmax and the PV products in lockstep, so the two waves
 // sharing a SIMD reach their softmax (VALU) together and the matrix pipe
 // idles.  Here the waves of the second half (4..7) run the same work rotated
@@ -33,6 +33,8 @@
 // group, output lane i receives element i % 4 of the 8-byte rows addressed by
 // lanes i / 4 + 4 j (j = 0..3), so lanes addressing 4 consecutive key rows x 4
 // feature quads yield, per lane, one feature over 4 consecutive keys.
+#include <cstring>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -247,8 +249,10 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
     }                                                                                        \
     const bool raise_ = tmax > m_run + PP_LAZY;                                              \
     const float m_new_ = raise_ ? tmax : m_run;                                              \
+    /* a query whose keys so far are all masked keeps m = -inf; it subtracts 0 */           \
+    const float m_sub_ = m_new_ == -INFINITY ? 0.f : m_new_;                                 \
     if (__any(raise_)) {                                                                     \
-      const float alpha_ = __builtin_amdgcn_exp2f(m_run - m_new_);                           \
+      const float alpha_ = __builtin_amdgcn_exp2f(m_run - m_sub_);                           \
       l_run *= alpha_;                                                                       \
       _Pragma("unroll") for (int d = 0; d < 4; ++d)                                          \
         _Pragma("unroll") for (int e = 0; e < 16; ++e) O[d][e] *= alpha_;                    \
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
     float psum_ = 0.f;                                                                       \
     _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                         \
       _Pragma("unroll") for (int e = 0; e < 16; ++e) {                                       \
-        const float pv_ = __builtin_amdgcn_exp2f(fmaf(S[mb][e], sl2, -m_new_));              \
+        const float pv_ = __builtin_amdgcn_exp2f(fmaf(S[mb][e], sl2, -m_sub_));              \
         S[mb][e] = pv_;                                                                      \
         psum_ += pv_;                                                                        \
       }                                                                                      \
@@ -365,6 +369,15 @@ void flash_set_prefill_layout(FlashParams& p) {
   p.kr2 = p.kr;      p.kr_b = (long)p.T * 64;    p.kr_h = 0;   p.kr_kb = 128;
   p.P0 = 0;
   p.nsplit = 1; p.opart = p.ostat = nullptr;
+}
+
+bool flash_prefill_fits(int T, int H) {
+  FlashParams p;
+  memset(&p, 0, sizeof p);
+  p.T = T; p.H = H; p.B = 1;
+  p.kc_kb = p.v_kb = H * 256 * 2;  // the prefill layout's per-key strides
+  p.kr_kb = 128;
+  return flash_pp_ok(p);
 }
 
 bool flash_pp_ok(const FlashParams& p) {

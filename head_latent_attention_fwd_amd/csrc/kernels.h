@@ -198,11 +198,13 @@ struct FlashParams {
 };
 // merge of the key-split partials of flash_prefill_pp_bf16 into p.out
 hipError_t flash_combine_bf16(const FlashParams& p, hipStream_t s);
-hipError_t flash_prefill_bf16(const FlashParams& p, hipStream_t s);
 // the key/value source fields for the prefill layout (kv [B*T][H][256], kr [B*T][64])
 void flash_set_prefill_layout(FlashParams& p);
 // ping-pong form (flash_pp.hip); needs its byte offsets below 2^31
 bool flash_pp_ok(const FlashParams& p);
+// whether a plain prefill of T tokens with H heads fits flash_pp_ok (host
+// check, before any launch)
+bool flash_prefill_fits(int T, int H);
 hipError_t flash_prefill_pp_bf16(const FlashParams& p, hipStream_t s);
 
 // bf16 decode over the full per-head cache (one query per sequence).

@@ -119,8 +119,8 @@ int check_dims(const mla_dims* d, bool need_ff) {
     return fail(MLA_ERR_SHAPE, "every width of mla_dims must be positive");
   if (d->qk_rope_dim % 2) return fail(MLA_ERR_SHAPE, "qk_rope_dim must be even (RoPE pairs)");
   if (need_ff && d->d_ff <= 0) return fail(MLA_ERR_SHAPE, "d_ff must be positive for the block");
-  if (!(d->rms_eps >= 0.f) || !std::isfinite(d->softmax_scale) || d->softmax_scale <= 0.f)
-    return fail(MLA_ERR_SHAPE, "rms_eps must be >= 0 and softmax_scale positive and finite");
+  if (!(d->rms_eps >= 0.f) || !std::isfinite(d->softmax_scale) || d->softmax_scale < 0.f)
+    return fail(MLA_ERR_SHAPE, "rms_eps must be >= 0 and softmax_scale 0 (default) or positive and finite");
   if (d->dtype != MLA_F32 && d->dtype != MLA_BF16)
     return fail(MLA_ERR_UNSUPPORTED, "dtype %d is neither MLA_F32 nor MLA_BF16", d->dtype);
   if (d->dtype == MLA_F32) {
@@ -135,6 +135,25 @@ int check_dims(const mla_dims* d, bool need_ff) {
         (need_ff && d->d_ff % 64))
       return fail(MLA_ERR_UNSUPPORTED, "bf16 path: d_model, q_lora, kv_lora, d_ff multiples of 64");
   }
+  return MLA_OK;
+}
+
+// The score scale: softmax_scale when positive, else 1/sqrt(d_nope + d_rope)
+// (the head width of the scaled scores in the code excerpt of "Kimi K2 · Mix
+// and project"; the same value serves the absorbed form).
+float scale_of(const mla_dims* d) {
+  if (d->softmax_scale > 0.f) return d->softmax_scale;
+  return (float)(1.0 / std::sqrt((double)(d->qk_nope_dim + d->qk_rope_dim)));
+}
+constexpr float kLog2e = 1.4426950408889634f;
+
+// The bf16 flash kernel addresses keys by 32-bit byte offsets from each
+// (sequence, head) base; a prefill whose kv rows do not fit is refused up
+// front (no other attention kernel serves it).
+int check_flash_prefill(const mla_dims* d, int T) {
+  if (d->dtype == MLA_BF16 && !flash_prefill_fits(T, d->n_heads))
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 prefill: T=%d with %d heads exceeds the attention kernel's "
+                "32-bit key offsets", T, d->n_heads);
   return MLA_OK;
 }
 
@@ -538,13 +557,13 @@ int prefill_core(const mla_dims* d, const mla_weights* w, const void* x, int B, 
     memset(&f, 0, sizeof f);
     f.q = (const bf16_t*)b.q; f.kv = (const bf16_t*)b.kv; f.kr = (const bf16_t*)b.kr;
     f.out = (bf16_t*)b.o; f.B = B; f.T = T; f.H = H; f.rcos = rc; f.rsin = rs;
-    f.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    f.scale_log2 = scale_of(d) * kLog2e;
     flash_set_prefill_layout(f);
     f.nsplit = pl.fpart ? flash_splits(B, T, H, 0) : 1;
     f.opart = pl.fpart;
     f.ostat = pl.fpart ? pl.fpart + (size_t)f.nsplit * M * H * 128 : nullptr;
-    if (flash_pp_ok(f)) LAUNCH("flash_prefill", flash_prefill_pp_bf16(f, st));
-    else LAUNCH("flash_prefill", flash_prefill_bf16(f, st));
+    if (!flash_pp_ok(f)) return fail(MLA_ERR_HIP, "internal: prefill outside the flash kernel's range");
+    LAUNCH("flash_prefill", flash_prefill_pp_bf16(f, st));
   } else {
     AttnGenericParams a;
     memset(&a, 0, sizeof a);
@@ -556,7 +575,7 @@ int prefill_core(const mla_dims* d, const mla_weights* w, const void* x, int B, 
     a.v = (const float*)b.kv + dn; a.v_b = (long)T * kvw; a.v_j = kvw; a.v_h = dn + dv;
     a.out = (float*)b.o; a.o_row = (long)H * dv; a.o_head = dv;
     a.B = B; a.Tq = T; a.Tk = T; a.H = H; a.d_nope = dn; a.d_rope = dr; a.d_v = dv;
-    a.causal_offset = 0; a.scale = d->softmax_scale;
+    a.causal_offset = 0; a.scale = scale_of(d);
     LAUNCH("attn_generic", attn_generic_f32(a, st));
   }
   if (k_cache) {
@@ -757,7 +776,8 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int B, i
   if ((k_cache || latent_cache) && L_cap < T)
     return fail(MLA_ERR_SHAPE, "L_cap=%d smaller than T=%d", L_cap, T);
   const long M = (long)B * T;
-  if ((r = check_i32(M * d->d_model, "x")) || (r = check_i32(M * d->n_heads * 256, "kv")))
+  if ((r = check_i32(M * d->d_model, "x")) || (r = check_i32(M * d->n_heads * 256, "kv")) ||
+      (r = check_flash_prefill(d, T)))
     return r;
   PrefillPlan pl;
   size_t need = prefill_layout(d, B, T, nullptr, &pl);
@@ -837,7 +857,7 @@ static int chunk_impl(const mla_dims* d, const mla_weights* w, const void* x, in
     FlashParams f;
     memset(&f, 0, sizeof f);
     f.q = (const bf16_t*)b.q; f.out = (bf16_t*)b.o; f.B = B; f.T = T; f.H = H;
-    f.rcos = rc; f.rsin = rs; f.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    f.rcos = rc; f.rsin = rs; f.scale_log2 = scale_of(d) * kLog2e;
     f.P0 = P0;
     if (form == 0) {
       LAUNCH("scatter_cache", scatter_full_cache<bf16_t>((const bf16_t*)b.kv, (const bf16_t*)b.kr,
@@ -881,7 +901,7 @@ static int chunk_impl(const mla_dims* d, const mla_weights* w, const void* x, in
     a.v = (const float*)v_cache; a.v_b = (long)H * L_cap * dv; a.v_j = dv; a.v_h = (long)L_cap * dv;
     a.out = (float*)b.o; a.o_row = (long)H * dv; a.o_head = dv;
     a.B = B; a.Tq = T; a.Tk = Lk; a.H = H; a.d_nope = dn; a.d_rope = dr; a.d_v = dv;
-    a.causal_offset = P0; a.scale = d->softmax_scale;
+    a.causal_offset = P0; a.scale = scale_of(d);
     LAUNCH("attn_generic", attn_generic_f32(a, st));
   } else {
     // absorbed form over the latent cache, T queries per sequence
@@ -903,7 +923,7 @@ static int chunk_impl(const mla_dims* d, const mla_weights* w, const void* x, in
     a.v = (const float*)latent_cache; a.v_b = a.kn_b; a.v_j = cw; a.v_h = 0;
     a.out = (float*)pl.o_lat; a.o_row = (long)H * kl; a.o_head = kl;
     a.B = B; a.Tq = T; a.Tk = Lk; a.H = H; a.d_nope = kl; a.d_rope = dr; a.d_v = kl;
-    a.causal_offset = P0; a.scale = d->softmax_scale;
+    a.causal_offset = P0; a.scale = scale_of(d);
     LAUNCH("attn_generic", attn_generic_f32(a, st));
     GemmF32Params u;
     memset(&u, 0, sizeof u);
@@ -991,7 +1011,7 @@ static int decode_full_impl(const mla_dims* d, const mla_weights* w, const void*
     a.kr = (const bf16_t*)b.kr;
     a.rcos = rc; a.rsin = rs;
     a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
-    a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    a.scale_log2 = scale_of(d) * kLog2e;
     a.seq_pos = seq_pos;
     LAUNCH("decode_full", decode_full_bf16(a, st));
   } else {
@@ -1008,7 +1028,7 @@ static int decode_full_impl(const mla_dims* d, const mla_weights* w, const void*
     a.v = (const float*)v_cache; a.v_b = (long)H * L_cap * dv; a.v_j = dv; a.v_h = (long)L_cap * dv;
     a.out = (float*)b.o; a.o_row = (long)H * dv; a.o_head = dv;
     a.B = B; a.Tq = 1; a.Tk = P + 1; a.H = H; a.d_nope = dn; a.d_rope = dr; a.d_v = dv;
-    a.causal_offset = P; a.scale = d->softmax_scale;
+    a.causal_offset = P; a.scale = scale_of(d);
     a.seq_pos = seq_pos; a.pos_max = P;
     LAUNCH("attn_generic", attn_generic_f32(a, st));
   }
@@ -1083,7 +1103,7 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
     a.plan = ab.plan; a.splits = splits;
     a.rcos = rc; a.rsin = rs;
     a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.G = pl.nsplit;
-    a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    a.scale_log2 = scale_of(d) * kLog2e;
     a.seq_pos = seq_pos;
     // merge of the splits fused with O_h = o~_h W_UV,h^T
     a.w_ukv = (const bf16_t*)w->w_ukv; a.out = (bf16_t*)b.o;
@@ -1108,7 +1128,7 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
     a.v = (const float*)latent_cache; a.v_b = a.kn_b; a.v_j = cw; a.v_h = 0;
     a.out = (float*)pl.o_lat; a.o_row = (long)H * kl; a.o_head = kl;
     a.B = B; a.Tq = 1; a.Tk = P + 1; a.H = H; a.d_nope = kl; a.d_rope = dr; a.d_v = kl;
-    a.causal_offset = P; a.scale = d->softmax_scale;
+    a.causal_offset = P; a.scale = scale_of(d);
     a.seq_pos = seq_pos; a.pos_max = P;
     LAUNCH("attn_generic", attn_generic_f32(a, st));
     // O_h = o~_h . W_UV,h^T
@@ -1169,7 +1189,7 @@ int dense_block_fwd(const mla_dims* d, const mla_block_weights* w, const void* x
   if ((r = check_rope(rc, rs, rope_rows, T))) return r;
   const long M = (long)B * T;
   if ((r = check_i32(M * d->d_ff, "ffn hidden")) || (r = check_i32(M * d->n_heads * 256, "kv")) ||
-      (r = check_i32((long)d->d_ff * d->d_model, "W1")))
+      (r = check_i32((long)d->d_ff * d->d_model, "W1")) || (r = check_flash_prefill(d, T)))
     return r;
   size_t need = dense_block_workspace_size(d, B, T);
   if (ws_bytes < need)

@@ -43,9 +43,11 @@
  *    passes the table R as rope_cos/rope_sin [rope_rows, d_rope/2] (float32;
  *    mla_rope_table fills it), row t for position t.
  *  - Ownership: the caller allocates and owns every buffer (inputs, weights,
- *    caches, outputs and the workspace).  The library never allocates or
- *    frees, keeps no pointer after a call returns and has no global state
- *    beyond a thread-local error message.
+ *    caches, outputs and the workspace).  The compute calls never allocate
+ *    or free device memory and keep no pointer after they return.  Library
+ *    state: a thread-local error message; the opt-in kernel timer
+ *    (mla_profile_enable) creates HIP events and keeps them, with its
+ *    pending records, in thread-local pools until the process ends.
  *  - Asynchrony: calls only enqueue kernels on `stream` (a hipStream_t; NULL
  *    is the default stream) and return.  Device faults surface at the
  *    caller's next synchronisation.
@@ -89,7 +91,9 @@ typedef struct {
   int v_head_dim;    /* per-head value width: 128 ([MP] in/out line)      */
   int d_ff;          /* SwiGLU inner width (block only): 18432            */
   float rms_eps;     /* RMSNorm epsilon (1e-6)                            */
-  float softmax_scale; /* score scale; 1/sqrt(qk_nope_dim + qk_rope_dim)  */
+  float softmax_scale; /* score scale; 0 selects 1/sqrt(qk_nope_dim +    */
+                       /* qk_rope_dim) (the value adopted for the pages'   */
+                       /* unstated scale), negative or NaN is rejected     */
   int dtype;         /* mla_dtype                                         */
 } mla_dims;
 
@@ -129,7 +133,12 @@ int mla_rope_table(int n_pos, int d_rope, double base, float *cos_out, float *si
  *     [K^C ; k^R] and value, as the pinned implementation caches them;
  *   latent_cache [B, L_cap, kv_lora + d_rope]: slots 0..T-1 receive the
  *     576-value entries [c^KV-hat ; k^R].
- * Requires T <= L_cap when a cache is given. */
+ * Requires T <= L_cap when a cache is given.  bf16: the attention kernel
+ * addresses each head's keys with 32-bit byte offsets, so (T + 64) * H * 512
+ * must stay below 2^31 (T <= 65471 at 64 heads); a longer prefill returns
+ * MLA_ERR_UNSUPPORTED (mla_prefill_chunk_fullcache below, whose keys are
+ * 384-byte cache rows, serves longer contexts in pieces).  The same limit
+ * holds for dense_block_fwd. */
 size_t mla_prefill_workspace_size(const mla_dims *dims, int B, int T);
 int mla_prefill(const mla_dims *dims, const mla_weights *w, const void *x, int B, int T,
                 const float *rope_cos, const float *rope_sin, int rope_rows, void *out,

@@ -168,6 +168,34 @@ def test_unsupported_rejected():
     assert st == -4                                 # 1024 passes the batch check, then the workspace one
 
 
+def test_prefill_beyond_attention_offsets_rejected():
+    """A bf16 prefill whose per-head key rows do not fit the flash kernel's
+    32-bit byte offsets is refused up front (MLA_ERR_UNSUPPORTED), for the
+    prefill and the dense block, whatever the workspace; the largest T that
+    fits passes that check and stops at the workspace check."""
+    L = _lib()
+    d = kimi()
+    T_bad = (1 << 31) // (64 * 256 * 2) - 64        # 65472: (T + 64) kv rows reach 2^31 bytes
+    assert _prefill(L, d, T=T_bad, rows=T_bad, wsb=1 << 40) == -3
+    assert "offsets" in L.mla_last_error().decode()
+    bw = mla.BlockWeights(FAKE, FAKE, _w(), FAKE, FAKE, FAKE)
+    st = L.dense_block_fwd(ctypes.byref(d), ctypes.byref(bw), FAKE, 1, T_bad, FAKE, FAKE, T_bad, FAKE,
+                           FAKE, 1 << 40, None)
+    assert st == -3
+    assert _prefill(L, d, T=T_bad - 1, rows=T_bad, wsb=1) == -4
+
+
+def test_softmax_scale_default_and_range():
+    """softmax_scale 0 selects the default scale (accepted); a negative one
+    is rejected."""
+    L = _lib()
+    d = tiny()
+    d.softmax_scale = 0.0
+    assert _prefill(L, d, wsb=1) == -4               # past the dims check
+    d.softmax_scale = -0.5
+    assert _prefill(L, d) == -2
+
+
 def test_small_workspace_rejected():
     L = _lib()
     d = kimi()

@@ -76,8 +76,7 @@ def test_prefill_kimi_full_size_sampled_rows():
 
 def test_prefill_kimi_ragged_T2000_sampled_rows():
     """Kimi K2 widths at T=2000: 256-row tiles with a ragged last row tile in
-    every GEMM, the 256 x 224 output-projection tiles among them, and a
-    ragged last query tile in the attention kernel."""
+    every GEMM and a ragged last query tile in the attention kernel."""
     od = ref.KIMI_K2
     B, T = 1, 2000
     log(f"[prefill kimi ragged] B={B} T={T} bf16")
@@ -514,6 +513,126 @@ def test_decode_latentcache_max_jump_restart():
     assert_close(from_dev(got)[bs], want, TOL_BF16, "decode latent with score jumps")
 
 
+# ------------------------------------------- online-softmax running-max raise
+# The prefill attention keeps a running score maximum per (query, head) and,
+# when a later key tile's scores clear it, rescales what it has accumulated
+# (the online form of the float32 softmax in the code excerpt of "Kimi K2 ·
+# Mix and project").  With the N(0,1) / N(0,0.02^2) inputs the first tile a
+# query sees already holds its largest scores within a few units, so these
+# cases plant keys whose scores jump far above everything before them.
+RAISE_MARGIN = 8.0 * np.log(2.0)   # natural-log units; 8 in log2 units
+
+
+def _late_raises(P, q_pos, tile=64):
+    """(head, query, tile) events in the oracle probabilities P [H, Tq, Tk]
+    where the best key of a key tile after the first outscores every earlier
+    key by more than RAISE_MARGIN (scores differ as log-probabilities do)."""
+    with np.errstate(divide="ignore"):
+        lp = np.log(P)
+    n = 0
+    for qi, pos in enumerate(q_pos):
+        run = lp[:, qi, :tile].max(-1)
+        for t0 in range(tile, pos + 1, tile):
+            tm = lp[:, qi, t0:min(t0 + tile, pos + 1)].max(-1)
+            n += int(np.sum(tm > run + RAISE_MARGIN))
+            run = np.maximum(run, tm)
+    return n
+
+
+def _scaled_bf16(a, k):
+    """bf16 values times a power of two (exact)."""
+    return synth.bf16_round(np.asarray(a, np.float32) * np.float32(k))
+
+
+def test_prefill_running_max_raise():
+    """Kimi K2 widths, B=1, T=1024: tokens 300 and 700 have their input
+    scaled by 8 and 32.  Their latent and query paths pass an RMSNorm and do
+    not change; their shared rotary key k^R = x W_KR grows with the input, so
+    the scores of keys 300 and 700 jump far above the first key tile for
+    many (query, head) pairs, in two steps for queries after 700.  Oracle on
+    sampled rows; the oracle's own probabilities confirm the raises."""
+    od = ref.KIMI_K2
+    B, T = 1, 1024
+    log(f"[prefill running-max raise] B={B} T={T} bf16")
+    x, w = synth.prefill_inputs(od, B, T, 1021, bf16=True)
+    x[0, 300] = _scaled_bf16(x[0, 300], 8.0)
+    x[0, 700] = _scaled_bf16(x[0, 700], 32.0)
+    rows = sorted(set([0, 299, 300, 301, 363, 511, 512, 699, 700, 701, 767, 768, 900, T - 1] +
+                      list(np.random.default_rng(7).choice(T, 10, replace=False))))
+    ow = oracle_weights(w)
+    want = ref.mla_prefill(od, ow, x.astype(np.float64), rows=rows)
+    p = ref.mla_project(od, ow, x.astype(np.float64), np.arange(T))
+    chk = [r for r in rows if r >= 320]
+    _, P = ref.attention(p["q_nope"][0, chk], p["q_rope"][0, chk], p["k_nope"][0], p["k_rope"][0],
+                         p["v"][0], od.softmax_scale, np.asarray(chk), np.arange(T), return_probs=True)
+    n = _late_raises(P, chk)
+    log(f"  raise events in the sample: {n}")
+    assert n >= 100
+    d = dims_of(mla, od, "bf16")
+    got = mla.mla_prefill(d, weights_to_dev(w, "bf16", DEV), to_dev(x, "bf16", DEV), _rope(od, T))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got)[:, rows], want, TOL_BF16, "prefill with score jumps, sampled rows")
+
+
+@pytest.mark.parametrize("form", ["full", "latent"])
+def test_prefill_chunk_running_max_raise(form):
+    """Chunked prefill, B=1, 200 new tokens after 2000 cached positions: the
+    attention splits each query tile's keys over several workgroups whose
+    partial maxima and sums are merged.  Cached keys 330, 771, 1320 and 1927
+    (one inside each key split) are scaled by 16 (the whole key in the full
+    cache; the rotary part of the latent entry, which leaves values alone),
+    and new token 100 (position 2100) has its input scaled by 16."""
+    od = ref.KIMI_K2
+    B, T, P0, L_cap, seed = 1, 200, 2000, 2200, 131
+    spikes = [330, 771, 1320, 1927]
+    log(f"[chunk running-max raise {form}] B={B} T={T} P0={P0}")
+    x, w = synth.prefill_inputs(od, B, T, seed, bf16=True)
+    x[0, 100] = _scaled_bf16(x[0, 100], 16.0)
+    ow = oracle_weights(w)
+    d = dims_of(mla, od, "bf16")
+    r = od.kv_lora_rank
+    pos = P0 + np.arange(T)
+    chk = list(range(100, T, 9))
+    if form == "full":
+        _, _, kc, vc = synth.decode_full_inputs(od, B, P0, L_cap, seed + 1, bf16=True)
+        kf = synth.as_f32(kc, True)
+        for j in spikes:
+            kf[:, :, j] = _scaled_bf16(kf[:, :, j], 16.0)
+        kc = synth.bf16_bits(kf)
+        vf = synth.as_f32(vc, True).astype(np.float64)
+        want, kc2, vc2 = ref.mla_prefill_chunk_fullcache(od, ow, x.astype(np.float64), P0,
+                                                         kf.astype(np.float64), vf)
+        p = ref.mla_project(od, ow, x.astype(np.float64), pos)
+        qf = np.concatenate([p["q_nope"][0], p["q_rope"][0]], -1)[chk]          # [Tq,H,192]
+        kk = kc2[0].transpose(1, 0, 2)                                          # [L,H,192]
+        _, P = ref.attention(qf, qf[..., :0], kk, kk[:, 0, :0], vc2[0].transpose(1, 0, 2),
+                             od.softmax_scale, pos[chk], np.arange(L_cap), return_probs=True)
+        kd, vd = bits_to_dev(kc, "bf16", DEV), bits_to_dev(vc, "bf16", DEV)
+        got = mla.mla_prefill_chunk_fullcache(d, weights_to_dev(w, "bf16", DEV), to_dev(x, "bf16", DEV), P0,
+                                              kd, vd, _rope(od, P0 + T))
+    else:
+        _, _, cc = synth.decode_latent_inputs(od, B, P0, L_cap, seed + 1, bf16=True)
+        cf = synth.as_f32(cc, True)
+        for j in spikes:
+            cf[:, j, r:] = _scaled_bf16(cf[:, j, r:], 16.0)
+        cc = synth.bf16_bits(cf)
+        want, cc2 = ref.mla_prefill_chunk_latentcache(od, ow, x.astype(np.float64), P0, cf.astype(np.float64))
+        p = ref.mla_project(od, ow, x.astype(np.float64), pos)
+        qt = ref.absorbed_query(od, ow, p["q_nope"][0, chk])                    # [Tq,H,r]
+        C = cc2[0]
+        Cb = np.broadcast_to(C[:, None, :r], (L_cap, od.n_heads, r))
+        _, P = ref.attention(qt, p["q_rope"][0, chk], Cb, C[:, r:], Cb, od.softmax_scale, pos[chk],
+                             np.arange(L_cap), return_probs=True)
+        cd = bits_to_dev(cc, "bf16", DEV)
+        got = mla.mla_prefill_chunk_latentcache(d, weights_to_dev(w, "bf16", DEV), to_dev(x, "bf16", DEV), P0,
+                                                cd, _rope(od, P0 + T))
+    n = _late_raises(P, list(pos[chk]))
+    log(f"  raise events in the sample: {n}")
+    assert n >= 100
+    torch.cuda.synchronize()
+    assert_close(from_dev(got), want, TOL_BF16, f"chunk {form} with score jumps")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_absorbed_equals_full_on_gpu(dt):
     """Latent decode and full-cache decode over the cache expanded from the
@@ -603,8 +722,8 @@ def test_dense_block_kimi_sampled_rows():
 
 
 def test_dense_block_kimi_T2048_sampled_rows():
-    """Kimi K2 block at T=2048: the o_proj and W2 products take the 256 x 224
-    tile kernel with its residual epilogue."""
+    """Kimi K2 block at T=2048: 224 output tiles of 256 x 256 in o_proj and
+    W2, with the residual epilogue."""
     od = ref.KIMI_K2
     B, T = 1, 2048
     log(f"[block kimi T=2048] B={B} T={T} bf16")
@@ -617,6 +736,27 @@ def test_dense_block_kimi_T2048_sampled_rows():
                               to_dev(x, "bf16", DEV), _rope(od, T))
     torch.cuda.synchronize()
     assert_close(from_dev(got)[:, rows], want, TOL_BF16, "kimi block T=2048 sampled rows")
+
+
+def test_dense_block_kimi_T4096_sampled_rows():
+    """The dense block workload itself (B=1, T=4096, Kimi K2 widths, d_ff
+    18432) in the launch configuration the benchmark times: 16 query tiles
+    per head in the attention, 448 output tiles in o_proj and W2.  The
+    oracle computes every key/value and a sample of rows (tile edges, the
+    last rows and random ones)."""
+    od = ref.KIMI_K2
+    B, T = 1, 4096
+    log(f"[block kimi T=4096] B={B} T={T} bf16")
+    x, w, blk = synth.block_inputs(od, B, T, 1025, bf16=True)
+    rows = sorted(set([0, 1, 255, 256, 1023, 2047, 2048, 3071, 3072, 3583, 3840, 4000, T - 2, T - 1] +
+                      list(np.random.default_rng(8).choice(T, 10, replace=False))))
+    bw = ref.BlockWeights(attn=oracle_weights(w), **{k: np.asarray(v, np.float64) for k, v in blk.items()})
+    want = ref.dense_block(od, bw, x.astype(np.float64), rows=rows)
+    d = dims_of(mla, od, "bf16")
+    got = mla.dense_block_fwd(d, weights_to_dev(w, "bf16", DEV), weights_to_dev(blk, "bf16", DEV),
+                              to_dev(x, "bf16", DEV), _rope(od, T))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got)[:, rows], want, TOL_BF16, "kimi block T=4096 sampled rows")
 
 
 def test_rope_table_matches_definition():
