@@ -79,6 +79,8 @@ def load():
                                        _I, _P, _P, _SZ, _P]
     L.mla_decode_latentcache.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _I, _I, _P, _P, _P,
                                          _I, _P, _P, _SZ, _P]
+    L.mla_decode_latentcache_noalloc.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _I, _I, _P, _P,
+                                                 _P, _I, _P, _P]
     L.mla_decode_fullcache_ragged.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _P, _I, _I, _P,
                                               _P, _P, _P, _I, _P, _P, _SZ, _P]
     L.mla_decode_latentcache_ragged.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _P, _I, _I,
@@ -102,7 +104,7 @@ def load():
     L.mla_last_error.argtypes = []
     L.mla_last_error.restype = ctypes.c_char_p
     for name in ("mla_rope_table", "mla_prefill", "mla_decode_fullcache",
-                 "mla_decode_latentcache", "mla_decode_fullcache_ragged",
+                 "mla_decode_latentcache", "mla_decode_latentcache_noalloc", "mla_decode_fullcache_ragged",
                  "mla_decode_latentcache_ragged", "mla_prefill_chunk_fullcache",
                  "mla_prefill_chunk_latentcache", "dense_block_fwd"):
         getattr(L, name).restype = _I
@@ -300,6 +302,28 @@ def mla_decode_latentcache(d: Dims, w: dict, x, P, latent_cache, rope, out=None,
                                     B, int(P), L_cap, lc, rc, rs, rows,
                                     ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
                                     ws.numel(), _stream(dev)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES of include/mla.h
+
+
+def mla_decode_latentcache_noalloc(d: Dims, w: dict, x, P, latent_cache, rope, out):
+    """mla_decode_latentcache with the library's own device scratch array
+    instead of a workspace (no device allocation by the library; `out` must be
+    given).  Steps whose workspace exceeds the array raise MLAError."""
+    L = load()
+    dev = x.device
+    B = x.shape[0]
+    _tensor(x, "x", (B, d.d_model), d.torch_dtype, dev)
+    L_cap = latent_cache.shape[1]
+    lc = _tensor(latent_cache, "latent_cache", (B, L_cap, d.kv_lora_rank + d.qk_rope_dim), d.torch_dtype, dev)
+    wt = _weights(d, w, dev)
+    rc, rs, rows = _rope(rope, P + 1, d, dev)
+    _tensor(out, "out", x.shape, d.torch_dtype, dev)
+    _check(L.mla_decode_latentcache_noalloc(ctypes.byref(d), ctypes.byref(wt), ctypes.c_void_p(x.data_ptr()),
+                                            B, int(P), L_cap, lc, rc, rs, rows,
+                                            ctypes.c_void_p(out.data_ptr()), _stream(dev)))
     return out
 
 

@@ -668,8 +668,8 @@ size_t decode_layout(const mla_dims* d, int B, int L_cap, int form, void* ws, De
 }
 
 int check_decode_args(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
-                      int L_cap, const float* rc, const float* rs, int rope_rows, void* out,
-                      void* ws) {
+                      int L_cap, const float* rc, const float* rs, int rope_rows, const void* out,
+                      const void* ws) {
   int r = check_dims(d, false);
   if (r) return r;
   if ((r = check_weights(w))) return r;
@@ -1054,17 +1054,28 @@ int mla_decode_fullcache_ragged(const mla_dims* d, const mla_weights* w, const v
 }
 
 // Latent-cache decode step; P and seq_pos as for decode_full_impl.
-static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
-                              const int* seq_pos, int L_cap, void* latent_cache, const float* rc,
-                              const float* rs, int rope_rows, void* out, void* ws, size_t ws_bytes,
-                              void* stream) {
-  int r = check_decode_args(d, w, x, B, P, L_cap, rc, rs, rope_rows, out, ws);
+// Every argument check of the latent-cache decode except the workspace
+// (no HIP call).
+static int decode_latent_check(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
+                               int L_cap, const void* latent_cache, const float* rc, const float* rs,
+                               int rope_rows, const void* out) {
+  int r = check_decode_args(d, w, x, B, P, L_cap, rc, rs, rope_rows, out, d);  // workspace checked later
   if (r) return r;
   if (!latent_cache) return fail(MLA_ERR_NULL, "latent_cache is NULL");
   if (d->dtype == MLA_BF16 && (d->kv_lora_rank != 512 || d->n_heads != 64))
     return fail(MLA_ERR_UNSUPPORTED, "bf16 latent decode serves kv_lora 512 and 64 heads");
   if (d->dtype == MLA_BF16 && B > 1024)
     return fail(MLA_ERR_UNSUPPORTED, "bf16 latent decode serves batches of up to 1024 sequences");
+  return MLA_OK;
+}
+
+static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
+                              const int* seq_pos, int L_cap, void* latent_cache, const float* rc,
+                              const float* rs, int rope_rows, void* out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  int r = decode_latent_check(d, w, x, B, P, L_cap, latent_cache, rc, rs, rope_rows, out);
+  if (r) return r;
+  if (!ws) return fail(MLA_ERR_NULL, "workspace is NULL");
   DecodePlan pl;
   size_t need = decode_layout(d, B, L_cap, 1, nullptr, &pl);
   if (ws_bytes < need)
@@ -1142,6 +1153,20 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
     LAUNCH("gemm_uv", gemm_f32(u, st));
   }
   return run_oproj(d, w->w_o, w->b_o, b.o, B, nullptr, out, pl.opart, pl.opart_floats, pl.S2, st);
+}
+
+// Hooks of the allocation-free entry point (noalloc.hip): the argument
+// checks of the latent decode, and an error report into this thread's
+// message.
+__attribute__((visibility("hidden"))) int mla_internal_decode_latent_check(const mla_dims* d, const mla_weights* w, const void* x, int B,
+                                     int P, int L_cap, const void* latent_cache, const float* rc,
+                                     const float* rs, int rope_rows, const void* out) {
+  g_err[0] = 0;
+  return decode_latent_check(d, w, x, B, P, L_cap, latent_cache, rc, rs, rope_rows, out);
+}
+
+__attribute__((visibility("hidden"))) int mla_internal_fail(int code, const char* msg) {
+  return fail(code, "%s", msg);
 }
 
 int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,

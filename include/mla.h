@@ -167,6 +167,31 @@ int mla_decode_latentcache(const mla_dims *dims, const mla_weights *w, const voi
                            const float *rope_sin, int rope_rows, void *out, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* ---- Latent-cache decode that allocates nothing ----
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * step as mla_decode_latentcache (same arguments, results bit for bit), with
+ * the workspace in a library-owned device array of
+ * MLA_NOALLOC_SCRATCH_BYTES (64 MiB; one per GPU that loads the library,
+ * held until the process ends) instead of a caller buffer.  No call
+ * allocates or frees memory; the first call on a device looks up the
+ * array's device address once (hipGetSymbolAddress).
+ *   - Limit: mla_decode_workspace_size(dims, B, L_cap) must be at most
+ *     MLA_NOALLOC_SCRATCH_BYTES (e.g. the Kimi K2 shapes up to B = 32 at
+ *     L_cap = 100,000); a larger step returns MLA_ERR_WORKSPACE and
+ *     enqueues nothing.
+ *   - Device: the calling thread's current device; `stream` (NULL = default)
+ *     must belong to it, else MLA_ERR_UNSUPPORTED.
+ *   - Sharing: every call on a GPU uses that GPU's one array and leaves its
+ *     contents behind; the step writes every word it reads, so nothing needs
+ *     clearing.  Calls that overlap on one GPU (other streams or threads)
+ *     race on the array: serialise them. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mla_decode_latentcache_noalloc(const mla_dims *dims, const mla_weights *w, const void *x,
+                                   int B, int P, int L_cap, void *latent_cache,
+                                   const float *rope_cos, const float *rope_sin, int rope_rows,
+                                   void *out, void *stream);
+
 /* ---- Decode over a ragged batch (both cache forms) ----
  * As mla_decode_fullcache / mla_decode_latentcache, but sequence b's new
  * token sits at its own position positions[b] ([MP]'s decode mode per
