@@ -12,8 +12,9 @@ Secondary lines (same JSON object, key "secondary") time the full-cache
 decode (B=64, P=1000), the absorbed latent-cache decode (B=32, P=8192), the
 same over a ragged batch (B=32, per-sequence positions uniform in
 [0, 8192]), a chunked prefill (512 new tokens after 3584 cached positions,
-full and latent cache forms) and the dense block (B=1, T=4096) with the same
-weights, against the HBM or MFMA roofline.  The CPU baseline times the float32 oracle on the host cores.
+full and latent cache forms), the dense block (B=1, T=4096) with the same
+weights, and a decode sweep over P in {1000, 4096, 8192, 16384} at B = 32 and
+64 for both cache forms, against the HBM or MFMA roofline.  The CPU baseline times the float32 oracle on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -88,6 +89,27 @@ def measured_traffic(kernel):
     return int(m.group(1))
 
 
+def decode_traffic(form):
+    """HBM bytes per launch of the decode attention kernel (read + write)
+    from the committed rocprofv3 counter summary of that workload, or None
+    when decode.hip changed since the counters were taken."""
+    import hashlib
+    import re
+    name = {"full": "decode_fullcache_B64_P1000_hbm_traffic.md",
+            "latent": "decode_latentcache_B32_P8192_hbm_traffic.md"}[form]
+    kern = {"full": "decode_full", "latent": "decode_latent"}[form]
+    src = os.path.join(ROOT, "head_latent_attention_fwd_amd", "csrc", "decode.hip")
+    try:
+        text = open(os.path.join(ROOT, "profiles", name)).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    m = re.search(rf"{kern} traffic_bytes_per_launch=(\d+) decode_source_sha256_16=([0-9a-f]+)", text)
+    if not m or m.group(2) != sha:
+        return None
+    return int(m.group(1))
+
+
 def make_weights(torch, dev, k, seed):
     """Synthetic N(0, 0.02^2) weights with unit gains, drawn on the device."""
     import head_latent_attention_fwd_amd as mla
@@ -103,6 +125,12 @@ def make_weights(torch, dev, k, seed):
         else:
             w[name] = (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
     return d, w, g
+
+
+def normal_bf16(torch, shape, g, dev):
+    """N(0,1) values drawn directly in bf16 on the device (no float32 copy of
+    a multi-GB cache)."""
+    return torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(0.0, 1.0, generator=g)
 
 
 def warm(torch, fn, warmup, min_s=WARM_S):
@@ -217,8 +245,8 @@ def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000)
     g = torch.Generator(device=dev)
     g.manual_seed(1003)
     H = k["n_heads"]
-    kc = torch.randn(B, H, L_cap, 192, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    vc = torch.randn(B, H, L_cap, 128, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    kc = normal_bf16(torch, (B, H, L_cap, 192), g, dev)
+    vc = normal_bf16(torch, (B, H, L_cap, 128), g, dev)
     x = torch.randn(B, k["d_model"], generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     rope = mla.mla_rope_table(L_cap, 64, 10000.0, dev)
     out = torch.empty_like(x)
@@ -231,6 +259,9 @@ def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000)
     nbytes = cache_bytes + mla_param_count() * 2 + B * H * 320 * 2 + 2 * B * k["d_model"] * 2
     if "decode_full" in kern:
         kern["decode_full"]["gbs"] = cache_bytes / (kern["decode_full"]["avg_ms"] * 1e-3) / 1e9
+        kern["decode_full"]["algorithmic_bytes"] = cache_bytes
+        if (B, P) == (64, 1000):
+            kern["decode_full"]["traffic"] = decode_traffic("full")
     del kc, vc
     return {"workload": f"MLA decode, full cache, bf16, B={B}, P={P} (L={L} keys)",
             "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev, "tokens_per_s": B / (ms * 1e-3),
@@ -243,7 +274,7 @@ def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=819
     L_cap = P + 1
     g = torch.Generator(device=dev)
     g.manual_seed(1004)
-    cc = torch.randn(B, L_cap, 576, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    cc = normal_bf16(torch, (B, L_cap, 576), g, dev)
     x = torch.randn(B, k["d_model"], generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     rope = mla.mla_rope_table(L_cap, 64, 10000.0, dev)
     out = torch.empty_like(x)
@@ -256,6 +287,9 @@ def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=819
     nbytes = cache_bytes + mla_param_count() * 2 + B * 576 * 2 + 2 * B * k["d_model"] * 2
     if "decode_latent" in kern:
         kern["decode_latent"]["gbs"] = cache_bytes / (kern["decode_latent"]["avg_ms"] * 1e-3) / 1e9
+        kern["decode_latent"]["algorithmic_bytes"] = cache_bytes
+        if (B, P) == (32, 8192):
+            kern["decode_latent"]["traffic"] = decode_traffic("latent")
     return {"workload": f"MLA decode, absorbed latent cache, bf16, B={B}, P={P} (L={L} keys)",
             "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev, "tokens_per_s": B / (ms * 1e-3),
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -291,6 +325,31 @@ def bench_decode_latent_ragged(torch, mla, dev, d, w, steps, warmup, flush, B=32
             "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev, "tokens_per_s": B / (ms * 1e-3),
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None}
+
+
+SWEEP_P = (1000, 4096, 8192, 16384)
+SWEEP_B = (32, 64)
+
+
+def bench_decode_sweep(torch, mla, dev, d, w, steps, warmup, flush):
+    """Decode steps over the number of cached positions P (the decode mode's
+    P of "Kimi K2 · Mix and project", 1,000 there) for both cache forms at
+    B = 32 and 64: time per step, tokens/s and algorithmic HBM GB/s."""
+    rows = []
+    for form, fn in (("full", bench_decode_full), ("latent", bench_decode_latent)):
+        for B in SWEEP_B:
+            for P in SWEEP_P:
+                log(f"[bench] decode sweep {form} B={B} P={P}")
+                r = fn(torch, mla, dev, d, w, steps, warmup, flush, B=B, P=P)
+                kname = "decode_full" if form == "full" else "decode_latent"
+                rows.append({"form": form, "B": B, "P": P, "ms_per_step": r["ms_per_step"],
+                             "tokens_per_s": r["tokens_per_s"], "hbm_gbs": r["hbm_gbs"],
+                             "hbm_frac": r["hbm_frac"],
+                             "attention_kernel_gbs": r["kernels"].get(kname, {}).get("gbs")})
+                torch.cuda.empty_cache()
+    return {"workload": "MLA decode step over P in " + str(list(SWEEP_P)) + ", B in " + str(list(SWEEP_B)) +
+                        ", both cache forms, bf16, Infinity Cache flushed before each step",
+            "points": rows}
 
 
 def chunk_flops(B, T, P0, k=KIMI):
@@ -395,7 +454,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode_full", "decode_latent", "decode_latent_ragged",
-                                       "prefill_bias", "chunk_full", "chunk_latent", "block", "copy"])
+                                       "prefill_bias", "chunk_full", "chunk_latent", "block", "decode_sweep",
+                                       "copy"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -437,7 +497,9 @@ def main():
               "prefill_bias": lambda: bench_prefill_bias(torch, mla, dev, d, w, args.steps, args.warmup),
               "chunk_full": lambda: bench_prefill_chunk(torch, mla, dev, d, w, args.steps, args.warmup, "full"),
               "chunk_latent": lambda: bench_prefill_chunk(torch, mla, dev, d, w, args.steps, args.warmup, "latent"),
-              "block": lambda: bench_block(torch, mla, dev, d, w, args.steps, args.warmup)}[args.only]
+              "block": lambda: bench_block(torch, mla, dev, d, w, args.steps, args.warmup),
+              "decode_sweep": lambda: bench_decode_sweep(torch, mla, dev, d, w, args.steps, args.warmup,
+                                                         flush)}[args.only]
         print(json.dumps(fn()))
         return
 
@@ -474,7 +536,8 @@ def main():
                          ("prefill_attention_bias", lambda: bench_prefill_bias(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3)),
                          ("prefill_chunk_fullcache", lambda: bench_prefill_chunk(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, "full")),
                          ("prefill_chunk_latentcache", lambda: bench_prefill_chunk(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, "latent")),
-                         ("dense_block", lambda: bench_block(torch, mla, dev, r["d"], r["w"], max(3, args.steps // 4), 2))):
+                         ("dense_block", lambda: bench_block(torch, mla, dev, r["d"], r["w"], max(3, args.steps // 4), 2)),
+                         ("decode_sweep", lambda: bench_decode_sweep(torch, mla, dev, r["d"], r["w"], 5, 2, flush))):
             log(f"[bench] {name}")
             try:
                 sec[name] = fn()
