@@ -647,6 +647,304 @@ static int pick_group_m(int tiles_m, int tiles_n, int ksplit) {
   return cost(best) * 5 <= cost(r0) * 4 ? best : 8;
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 224 tiles for products 7168 columns wide (o_proj, the dense block's
+// W2).  7168 = 28 x 256, so 256 x 256 tiles come in multiples of 28 per 256
+// rows: 224 tiles for 2048 rows leave 32 of the 256 CUs idle, 448 for 4096
+// rows run as 1.75 waves.  Cutting every 256-column tile into seven 32-column
+// strips for a "main" tile plus one strip left over gives 8 x 28 / 7 = 32
+// tiles of seven strips per 256 rows: the 28 main tiles (strips 0..6 of
+// 256-column tile t) and 4 gathered tiles (strip 7 of tiles 7 u .. 7 u + 6).
+// Every tile is a whole-K 256 x 224 product, so the launch fills whole waves
+// (256 tiles for 2048 rows, 512 for 4096) and all workgroups of an XCD still
+// move through K in step, sharing A and B stages in its L2.
+//
+// Eight waves: wave w owns rows 64 (w % 4) .. + 63 (two 32-row MFMA blocks)
+// and strips 0..3 (w < 4) or 4..6 (w >= 4).  The eight waves of a workgroup
+// land on the four SIMDs in a pattern of period four (read back from the
+// HW_ID register), so the two waves of a SIMD, w and w + 4, issue
+// 8 + 6 = 14 v_mfma_f32_32x32x16_bf16 per 16-wide k step, every SIMD the same.  Operands arrive by direct-to-LDS loads in a
+// two-stage ring of 64-k stages (A 32 KB + B 28 KB), as in the generic tile.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int V_BM = 256, V_NS = 7, V_BN = 32 * V_NS, V_SK = 64, V_ROWB = 128, V_NSTG = 2;
+constexpr int V_A_BYTES = V_BM * V_ROWB, V_B_BYTES = V_BN * V_ROWB, V_STAGE = V_A_BYTES + V_B_BYTES;
+constexpr int V_LDS = V_NSTG * V_STAGE;  // 120 KB, reused by the epilogue staging
+}  // namespace
+
+// first output column of strip j (0..6) of column tile tv; nt = N / 256
+MLA_DEV int v224_col(int tv, int j, int nt) {
+  return tv < nt ? 256 * tv + 32 * j : 256 * (7 * (tv - nt) + j) + 224;
+}
+
+// K loop of one wave: FN strips (4 or 3) starting at strip s0, rows 64 rg ...
+template <int FN>
+MLA_DEV void v224_loop(floatx16 (&acc)[2][4], const char* ldsc, unsigned lds_base, int nst, int wv,
+                       const int (&a_vo)[4], const int (&b_vo)[4], int b_dma0, u32x4 ra, u32x4 rb,
+                       int a_rd, int b_rd, int sw, int lg) {
+  constexpr int NMF = 2 * FN, NRD = 2 + FN, KSTEPS = V_SK / 16;
+#define V_ISSUE(u_)                                                                          \
+  do {                                                                                       \
+    const unsigned sb_ = lds_base + ((u_) % V_NSTG) * V_STAGE;                               \
+    const int ko_ = V_ROWB * (u_);                                                           \
+    _Pragma("unroll") for (int d = 0; d < 4; ++d)                                            \
+      gemm_dma16(sb_ + 1024 * (4 * wv + d), a_vo[d] + ko_, ra);                              \
+    _Pragma("unroll") for (int d = 0; d < FN; ++d)                                           \
+      gemm_dma16(sb_ + V_A_BYTES + 1024 * (b_dma0 + d), b_vo[d] + ko_, rb);                  \
+  } while (0)
+#define V_FREAD(u_, s_, slot)                                                                \
+  do {                                                                                       \
+    const char* sb_ = ldsc + ((u_) % V_NSTG) * V_STAGE;                                      \
+    const int co_ = 16 * ((2 * (s_) + lg) ^ sw);                                             \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                            \
+      fa[slot][i] = *(const bf16x8*)(sb_ + a_rd + i * 32 * V_ROWB + co_);                    \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
+      fb[slot][j] = *(const bf16x8*)(sb_ + b_rd + j * 32 * V_ROWB + co_);                    \
+  } while (0)
+#define V_MFMAS(slot)                                                                        \
+  _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                          \
+    const int i = q / FN, j = q % FN;                                                        \
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0); \
+  }
+#define V_SCHED()                                                                            \
+  _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                          \
+    MLA_SGB(SG_MFMA, 1);                                                                     \
+    if (q < NRD) MLA_SGB(SG_DS_RD, 1);                                                       \
+  }
+  bf16x8 fa[2][2], fb[2][FN];
+  if (nst <= 0) return;
+  V_ISSUE(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (nst > 1) V_ISSUE(1);
+  V_FREAD(0, 0, 0);
+  for (int t = 0; t < nst; ++t) {
+#pragma unroll
+    for (int s = 0; s + 1 < KSTEPS; ++s) {
+      V_FREAD(t, s + 1, (s + 1) & 1);
+      V_MFMAS(s & 1)
+      V_SCHED()
+    }
+    // stage t + 1 landed (this wave's loads; the barrier covers the others')
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + V_NSTG < nst) V_ISSUE(t + V_NSTG);  // into stage t's buffer, read by now
+    V_FREAD(min(t + 1, nst - 1), 0, 0);
+    V_MFMAS(1)
+    V_SCHED()
+  }
+#undef V_ISSUE
+#undef V_FREAD
+#undef V_MFMAS
+#undef V_SCHED
+}
+
+// bf16 epilogue of one wave: bias (when given) added in fp32, the rounded
+// tile staged in LDS (row pitch 448 B; 16-byte chunk c of row r at
+// c ^ ((r >> 2) & 3), which stays inside c's aligned group of four)
+template <int FN>
+MLA_DEV void v224_stage_bf16(const floatx16 (&acc)[2][4], char* cst, int rg, int s0, int lr, int lg,
+                             const bf16_t* __restrict__ bias, int tv, int nt) {
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int colg = v224_col(tv, s0 + j, nt);  // output column of this strip's column 0
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 32 * (s0 + j) + 8 * g + 4 * lg;  // column in the tile
+      float bq[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bq[q] = bf2f(bias[colg + 8 * g + 4 * lg + q]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 64 * rg + 32 * i + lr;
+        const floatx16& a = acc[i][j];
+        *(u32x2*)(cst + r * (V_BN * 2) + 16 * ((c >> 3) ^ ((r >> 2) & 3)) + 8 * ((c >> 2) & 1)) =
+            u32x2{pack2bf(a[4 * g] + bq[0], a[4 * g + 1] + bq[1]), pack2bf(a[4 * g + 2] + bq[2], a[4 * g + 3] + bq[3])};
+      }
+    }
+  }
+}
+
+// fp32 staging of rows [rlo, rlo + 128) for the residual epilogue: 4-float
+// chunk c4 of row r at c4 ^ (r & 7), inside c4's aligned group of eight
+MLA_DEV int v224_fidx(int r, int c) { return r * V_BN + (((c >> 2) ^ (r & 7)) << 2) + (c & 3); }
+template <int FN>
+MLA_DEV void v224_stage_f32(const floatx16 (&acc)[2][4], float* cst, int rg, int s0, int lr, int lg, int rlo) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rl = 64 * rg + 32 * i + lr - rlo;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 32 * (s0 + j) + 8 * g + 4 * lg;
+        *(floatx4*)&cst[v224_fidx(rl, c)] =
+            floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+      }
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_v224_kernel(GemmParams p) {
+  static_assert(EPI == EPI_BF16 || EPI == EPI_RESID, "bf16 and residual epilogues only");
+  __shared__ __attribute__((aligned(16))) char lds[V_LDS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wv & 3, cg = wv >> 2;
+  const int s0 = cg ? 4 : 0;  // first strip of this wave
+  const int lr = lane & 31, lg = lane >> 5;
+  const int nt = p.N / 256;
+
+  // tile coordinates: XCD-aware, grouped along M (as the generic tile)
+  const int lin = xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n);
+  const int GM = p.group_m;
+  const int group = lin / (GM * p.tiles_n);
+  const int first_m = group * GM;
+  const int gm = min(p.tiles_m - first_m, GM);
+  const int within = lin - group * GM * p.tiles_n;
+  const int tm = first_m + within % gm, tv = within / gm;
+  const int m0 = tm * V_BM;
+
+  floatx16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  {
+    // DMA d of a wave fills 8 rows of 128 B: lane l -> row 8 g + l / 8
+    // (g = the DMA's index in its tile), chunk position l % 8 holding
+    // logical chunk (l % 8) ^ swz(row), swz(r) = (r >> 1) & 7.  A: DMAs
+    // 4 w .. 4 w + 3.  B: strip wv (DMAs 4 wv ..) for w < 4, DMAs
+    // 16 + 3 (w - 4) .. for w >= 4; DMA g covers rows 8 (g % 4) .. of strip g / 4.
+    int a_vo[4], b_vo[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int r = 8 * (4 * wv + d) + lane / 8;
+      const int c = (lane % 8) ^ gemm_swz(r);
+      a_vo[d] = (min(m0 + r, p.M - 1) * (int)p.lda + 8 * c) * 2;
+    }
+    const int b_dma0 = cg ? 16 + 3 * (wv - 4) : 4 * wv;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int g = b_dma0 + d;
+      const int r = 8 * g + lane / 8;  // row of the B tile
+      const int c = (lane % 8) ^ gemm_swz(r);
+      const int src = min(v224_col(tv, min(g, 27) / 4, nt) + 8 * (g % 4) + lane / 8, p.N - 1);
+      b_vo[d] = (src * (int)p.ldb + 8 * c) * 2;
+    }
+    const u32x4 ra = gemm_rsrc(p.A), rb = gemm_rsrc(p.B);
+    const unsigned lds_base = (unsigned)(unsigned long)(__attribute__((address_space(3))) char*)lds;
+    const int sw = gemm_swz(lr);  // fragment rows are lr (mod 32)
+    const int a_rd = (64 * rg + lr) * V_ROWB, b_rd = V_A_BYTES + (32 * s0 + lr) * V_ROWB;
+    const int nst = p.K / V_SK;
+    if (cg == 0)
+      v224_loop<4>(acc, lds, lds_base, nst, wv, a_vo, b_vo, b_dma0, ra, rb, a_rd, b_rd, sw, lg);
+    else
+      v224_loop<3>(acc, lds, lds_base, nst, wv, a_vo, b_vo, b_dma0, ra, rb, a_rd, b_rd, sw, lg);
+  }
+
+  const int rows_M = p.M;
+  const long ldc = p.ldc;
+  bf16_t* C = (bf16_t*)p.C;
+  const bf16_t* __restrict__ bias = p.bias;
+  constexpr int CH8 = V_BN / 8;  // 28 16-byte output chunks per tile row
+  if constexpr (EPI == EPI_BF16) {
+    char* cst = lds;
+    __syncthreads();  // last K stage read
+    if (cg == 0) v224_stage_bf16<4>(acc, cst, rg, s0, lr, lg, bias, tv, nt);
+    else v224_stage_bf16<3>(acc, cst, rg, s0, lr, lg, bias, tv, nt);
+    __syncthreads();
+    constexpr int NIT = V_BM * CH8 / 512;  // 14
+    u32x4 sv[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + it * 512, rl = idx / CH8, c8 = idx % CH8;
+      sv[it] = *(const u32x4*)(cst + rl * (V_BN * 2) + 16 * (c8 ^ ((rl >> 2) & 3)));
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + it * 512, rl = idx / CH8, c8 = idx % CH8;
+      const int row = m0 + rl;
+      if (row >= rows_M) continue;
+      *(u32x4*)(C + (long)row * ldc + v224_col(tv, c8 >> 2, nt) + 8 * (c8 & 3)) = sv[it];
+    }
+  } else {
+    // residual add in two passes of 128 rows (waves with rg < 2, then rg >= 2)
+    float* cst = (float*)lds;
+    const bf16_t* __restrict__ Rres = p.R;
+    const long ldr = p.ldr;
+    constexpr int NIT = 128 * CH8 / 512;  // 7
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      __syncthreads();  // LDS free: last K stage read (pass 0) or previous pass stored
+      const int rlo = 128 * pass;
+      if ((rg >> 1) == pass) {
+        if (cg == 0) v224_stage_f32<4>(acc, cst, rg, s0, lr, lg, rlo);
+        else v224_stage_f32<3>(acc, cst, rg, s0, lr, lg, rlo);
+      }
+      __syncthreads();
+      floatx4 sv[NIT][2];
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int idx = tid + it * 512, rl = idx / CH8, c8 = idx % CH8;
+        sv[it][0] = *(const floatx4*)&cst[v224_fidx(rl, 8 * c8)];
+        sv[it][1] = *(const floatx4*)&cst[v224_fidx(rl, 8 * c8 + 4)];
+      }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int idx = tid + it * 512, rl = idx / CH8, c8 = idx % CH8;
+        const int row = m0 + rlo + rl;
+        if (row >= rows_M) continue;
+        const int col = v224_col(tv, c8 >> 2, nt) + 8 * (c8 & 3);
+        float v[8] = {sv[it][0][0], sv[it][0][1], sv[it][0][2], sv[it][0][3],
+                      sv[it][1][0], sv[it][1][1], sv[it][1][2], sv[it][1][3]};
+        const u32x4 r = *(const u32x4*)(Rres + (long)row * ldr + col);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] += lo_bf(r[q]);
+          v[2 * q + 1] += hi_bf(r[q]);
+        }
+        if (bias) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] += bf2f(bias[col + q]);
+        }
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack2bf(v[2 * q], v[2 * q + 1]);
+        *(u32x4*)(C + (long)row * ldc + col) = o;
+      }
+    }
+  }
+}
+
+// The 256 x 224 tiling applies to single bf16-output products whose width
+// is a multiple of 1792 (seven 256-column tiles) with no batch, K split or
+// second weight, when its whole waves beat the 256 x 256 tile's.
+static bool v224_ok(const GemmParams& p, int epi) {
+  if ((epi != EPI_BF16 && epi != EPI_RESID) || p.N % 1792 != 0 || p.batch != 1 || p.ksplit != 1 ||
+      p.b_split > 0 || p.B2 || p.K % V_SK != 0 || p.kchunk != p.K || p.M <= 0)
+    return false;
+  if ((long)p.M * p.lda * 2 >= 0x7fffffffL || (long)p.N * p.ldb * 2 >= 0x7fffffffL) return false;
+  if ((p.ldc % 8) != 0 || (epi == EPI_RESID && (p.ldr % 8) != 0)) return false;
+  const long tm = (p.M + 255) / 256;
+  const long w256 = (tm * (p.N / 256) + 255) / 256, w224 = (tm * (p.N / 224) + 255) / 256;
+  return w224 * 7 < w256 * 8;
+}
+
+template <int EPI>
+static hipError_t launch_v224(GemmParams p, hipStream_t s) {
+  p.tiles_m = (p.M + 255) / 256;
+  p.tiles_n = p.N / 224;
+  p.group_m = pick_group_m<256, 224>(p.tiles_m, p.tiles_n, 1);
+  hipLaunchKernelGGL(gemm_v224_kernel<EPI>, dim3(p.tiles_m * p.tiles_n), dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int EPI>
 static hipError_t launch_cfg(const GemmParams* ps, int n, hipStream_t s) {
   GemmGroup g;
@@ -787,6 +1085,8 @@ hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s) {
   if (p.batch <= 0) p.batch = 1;
   if (p.ksplit <= 0) p.ksplit = 1;
   if (p.kchunk <= 0) p.kchunk = p.K;
+  if (cfg < 0 && v224_ok(p, epi))
+    return epi == EPI_BF16 ? launch_v224<EPI_BF16>(p, s) : launch_v224<EPI_RESID>(p, s);
   if (cfg < 0) cfg = gemm_pick_cfg(p.M, p.N, p.kchunk, p.batch * p.ksplit);
   switch (epi) {
     case EPI_F32: return launch_epi<EPI_F32>(p, cfg, s);
