@@ -421,6 +421,25 @@ def test_prefill_attention_bias(case):
     assert_close(from_dev(lc)[:, :T], ref.latent_cache_entries(od, p), tol, f"{name} latent cache")
 
 
+def test_prefill_attention_bias_kimi_T1100_sampled_rows():
+    """Biases at Kimi K2 widths above 1024 rows: o_proj takes the 256 x 224
+    tiles (bias added in their staged epilogue, including the gathered
+    strips 224..255 of each 256-column block) with a ragged last row tile
+    (1100 = 4 x 256 + 76)."""
+    od = ref.KIMI_K2
+    B, T = 1, 1100
+    log(f"[prefill bias kimi T=1100] B={B} T={T} bf16")
+    x, w = synth.prefill_inputs(od, B, T, 1021, bf16=True)
+    w = _with_biases(w, od, 1022, True)
+    rows = sorted(set([0, 1, 255, 256, 1023, 1024, 1087, T - 1] +
+                      list(np.random.default_rng(8).choice(T, 8, replace=False))))
+    want = ref.mla_prefill(od, oracle_weights(w), x.astype(np.float64), rows=rows)
+    d = dims_of(mla, od, "bf16")
+    got = mla.mla_prefill(d, weights_to_dev(w, "bf16", DEV), to_dev(x, "bf16", DEV), _rope(od, T))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got)[:, rows], want, TOL_BF16, "kimi prefill with biases T=1100 sampled rows")
+
+
 @pytest.mark.parametrize("form", ["full", "latent"])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_decode_attention_bias(form, dt):
@@ -722,8 +741,8 @@ def test_dense_block_kimi_sampled_rows():
 
 
 def test_dense_block_kimi_T2048_sampled_rows():
-    """Kimi K2 block at T=2048: 224 output tiles of 256 x 256 in o_proj and
-    W2, with the residual epilogue."""
+    """Kimi K2 block at T=2048: o_proj and W2 on the 256 x 224 tiles (256 of
+    them, seven 32-column strips each) with the residual epilogue."""
     od = ref.KIMI_K2
     B, T = 1, 2048
     log(f"[block kimi T=2048] B={B} T={T} bf16")
