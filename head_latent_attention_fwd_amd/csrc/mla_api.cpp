@@ -19,7 +19,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -157,15 +159,27 @@ int check_flash_prefill(const mla_dims* d, int T) {
   return MLA_OK;
 }
 
+// The kernels move every tensor with 16-byte vector and direct-to-LDS
+// accesses, so device pointers must be 16-byte aligned (NULL is allowed
+// here: the NULL checks are separate).
+int check_align(std::initializer_list<const void*> ps, const char* what) {
+  for (const void* q : ps)
+    if (q && ((uintptr_t)q & 15u))
+      return fail(MLA_ERR_UNSUPPORTED, "%s: device pointer %p is not 16-byte aligned", what, q);
+  return MLA_OK;
+}
+
 int check_weights(const mla_weights* w) {
   if (!w) return fail(MLA_ERR_NULL, "weights is NULL");
   if (!w->w_dq || !w->g_q || !w->w_uqr || !w->w_dkvr || !w->g_kv || !w->w_ukv || !w->w_o)
     return fail(MLA_ERR_NULL, "a weight pointer is NULL");
-  return MLA_OK;
+  return check_align({w->w_dq, w->g_q, w->w_uqr, w->w_dkvr, w->g_kv, w->w_ukv, w->w_o, w->b_dq,
+                      w->b_dkvr, w->b_o}, "weights");
 }
 
 int check_rope(const float* c, const float* s, int rows, int need) {
   if (!c || !s) return fail(MLA_ERR_NULL, "rope table pointer is NULL");
+  if (int r = check_align({c, s}, "rope table")) return r;
   if (rows < need) return fail(MLA_ERR_SHAPE, "rope_rows %d < %d positions needed", rows, need);
   return MLA_OK;
 }
@@ -701,6 +715,7 @@ int check_decode_args(const mla_dims* d, const mla_weights* w, const void* x, in
   if ((r = check_weights(w))) return r;
   if (!x || !out) return fail(MLA_ERR_NULL, "x or out is NULL");
   if (!ws) return fail(MLA_ERR_NULL, "workspace is NULL");
+  if ((r = check_align({x, out}, "x / out"))) return r;
   if (B <= 0 || L_cap <= 0) return fail(MLA_ERR_SHAPE, "B and L_cap must be positive");
   if (P < 0 || P >= L_cap) return fail(MLA_ERR_SHAPE, "P=%d outside [0, L_cap=%d)", P, L_cap);
   if ((r = check_rope(rc, rs, rope_rows, P + 1))) return r;
@@ -772,6 +787,7 @@ int mla_rope_table(int n_pos, int d_rope, double base, float* cos_out, float* si
                    void* stream) {
   g_err[0] = 0;
   if (!cos_out || !sin_out) return fail(MLA_ERR_NULL, "rope table output is NULL");
+  if (int r = check_align({cos_out, sin_out}, "rope table output")) return r;
   if (n_pos <= 0 || d_rope <= 0 || d_rope % 2) return fail(MLA_ERR_SHAPE, "bad n_pos/d_rope");
   if (!(base > 0.0)) return fail(MLA_ERR_SHAPE, "base must be positive");
   hipStream_t st = (hipStream_t)stream;
@@ -799,6 +815,8 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int B, i
   if ((r = check_rope(rc, rs, rope_rows, T))) return r;
   if ((k_cache == nullptr) != (v_cache == nullptr))
     return fail(MLA_ERR_NULL, "k_cache and v_cache must be given together");
+  if ((r = check_align({x, out, ws, k_cache, v_cache, latent_cache}, "x / out / workspace / caches")))
+    return r;
   if ((k_cache || latent_cache) && L_cap < T)
     return fail(MLA_ERR_SHAPE, "L_cap=%d smaller than T=%d", L_cap, T);
   const long M = (long)B * T;
@@ -857,6 +875,8 @@ static int chunk_impl(const mla_dims* d, const mla_weights* w, const void* x, in
   if (!ws) return fail(MLA_ERR_NULL, "workspace is NULL");
   if (form == 0 && (!k_cache || !v_cache)) return fail(MLA_ERR_NULL, "k_cache/v_cache is NULL");
   if (form == 1 && !latent_cache) return fail(MLA_ERR_NULL, "latent_cache is NULL");
+  if ((r = check_align({x, out, ws, k_cache, v_cache, latent_cache}, "x / out / workspace / caches")))
+    return r;
   if (B <= 0 || T <= 0 || L_cap <= 0) return fail(MLA_ERR_SHAPE, "B, T and L_cap must be positive");
   if (P0 < 0 || (long)P0 + T > L_cap)
     return fail(MLA_ERR_SHAPE, "chunk positions %d..%ld outside the cache [0, %d)", P0, (long)P0 + T - 1, L_cap);
@@ -1007,6 +1027,7 @@ static int decode_full_impl(const mla_dims* d, const mla_weights* w, const void*
   int r = check_decode_args(d, w, x, B, P, L_cap, rc, rs, rope_rows, out, ws);
   if (r) return r;
   if (!k_cache || !v_cache) return fail(MLA_ERR_NULL, "k_cache/v_cache is NULL");
+  if ((r = check_align({k_cache, v_cache, ws}, "caches / workspace"))) return r;
   DecodePlan pl;
   size_t need = decode_layout(d, B, L_cap, 0, nullptr, &pl);
   if (ws_bytes < need)
@@ -1088,6 +1109,7 @@ static int decode_latent_check(const mla_dims* d, const mla_weights* w, const vo
   int r = check_decode_args(d, w, x, B, P, L_cap, rc, rs, rope_rows, out, d);  // workspace checked later
   if (r) return r;
   if (!latent_cache) return fail(MLA_ERR_NULL, "latent_cache is NULL");
+  if ((r = check_align({latent_cache}, "latent_cache"))) return r;
   if (d->dtype == MLA_BF16 && (d->kv_lora_rank != 512 || d->n_heads != 64))
     return fail(MLA_ERR_UNSUPPORTED, "bf16 latent decode serves kv_lora 512 and 64 heads");
   if (d->dtype == MLA_BF16 && B > 1024)
@@ -1102,6 +1124,7 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
   int r = decode_latent_check(d, w, x, B, P, L_cap, latent_cache, rc, rs, rope_rows, out);
   if (r) return r;
   if (!ws) return fail(MLA_ERR_NULL, "workspace is NULL");
+  if ((r = check_align({ws}, "workspace"))) return r;
   DecodePlan pl;
   size_t need = decode_layout(d, B, L_cap, 1, nullptr, &pl);
   if (ws_bytes < need)
@@ -1236,6 +1259,9 @@ int dense_block_fwd(const mla_dims* d, const mla_block_weights* w, const void* x
     return fail(MLA_ERR_NULL, "a block weight pointer is NULL");
   if (!x || !out) return fail(MLA_ERR_NULL, "x or out is NULL");
   if (!ws) return fail(MLA_ERR_NULL, "workspace is NULL");
+  if ((r = check_align({w->g_attn, w->g_ffn, w->w1, w->w3, w->w2, x, out, ws},
+                       "block weights / x / out / workspace")))
+    return r;
   if (B <= 0 || T <= 0) return fail(MLA_ERR_SHAPE, "B and T must be positive");
   if ((r = check_rope(rc, rs, rope_rows, T))) return r;
   const long M = (long)B * T;

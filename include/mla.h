@@ -23,7 +23,12 @@
  * ---------------------------------
  *  - Pointers are DEVICE pointers unless stated; all tensors are contiguous
  *    row-major.  Every tensor has the element type dims->dtype (MLA_F32 or
- *    MLA_BF16) except the RoPE tables, which are always float32.
+ *    MLA_BF16) except the RoPE tables, which are always float32.  Every
+ *    device pointer (tensors, weights, gains, biases, RoPE tables, caches,
+ *    outputs, workspace) must be 16-byte aligned: the kernels move data in
+ *    16-byte vectors.  A misaligned pointer returns MLA_ERR_UNSUPPORTED
+ *    (device allocations are 256-byte aligned; offsets into them must keep
+ *    16-byte alignment).
  *  - Weights use the nn.Linear [out, in] layout and the fused orderings of
  *    the module code excerpt on [KV]:
  *      w_dq   [q_lora, d]                     query down-projection

@@ -219,3 +219,26 @@ def test_binding_raises_without_gpu_tensors():
     d = tiny()
     with pytest.raises((ValueError, TypeError)):
         mla.mla_prefill(d, {}, torch.zeros(1, 4, 256), (torch.zeros(4, 8), torch.zeros(4, 8)))
+
+
+def test_misaligned_pointers_are_rejected():
+    """Every device pointer must be 16-byte aligned (the kernels move data in
+    16-byte vectors): a misaligned tensor, weight, table or workspace pointer
+    returns MLA_ERR_UNSUPPORTED (-3) before any HIP call."""
+    L = _lib()
+    d = kimi()
+    odd = ctypes.c_void_p(0x1008)
+    assert _prefill(L, d, x=odd) == -3
+    assert b"16-byte" in L.mla_last_error()
+    assert _prefill(L, d, out=odd) == -3
+    assert _prefill(L, d, ws=odd) == -3
+    assert _prefill(L, d, rc=odd) == -3
+    assert _prefill(L, d, w=_w(w_o=odd)) == -3
+    assert _prefill(L, d, kc=odd, vc=FAKE, L_cap=16) == -3
+    w = _w()
+    st = L.mla_decode_latentcache(ctypes.byref(d), ctypes.byref(w), FAKE, 2, 10, 16, odd, FAKE,
+                                  FAKE, 64, FAKE, FAKE, 1 << 40, None)
+    assert st == -3
+    st = L.mla_decode_fullcache(ctypes.byref(d), ctypes.byref(w), FAKE, 2, 10, 16, FAKE, FAKE,
+                                FAKE, FAKE, 64, FAKE, odd, 1 << 40, None)
+    assert st == -3
