@@ -415,10 +415,11 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
     k.M = M; k.N = H * (dn + dv); k.K = kl;
     if (b.kv && M > 64) {
       // prefill: both up-projections in one launch when they take the same
-      // tile shape, the q tiles (longer K) scheduled first on every XCD, so
-      // the kv tiles fill the CUs the q product's last partial wave leaves idle
+      // tile shape (256 x 256, or 128 x 128 for the 512-row chunks), the q
+      // tiles (longer K) scheduled first on every XCD, so the kv tiles fill
+      // the CUs the q product's last partial wave leaves idle
       const int cfg = gemm_pick_cfg(M, q.N, q.K, 1);
-      if (cfg == gemm_pick_cfg(M, k.N, k.K, 1) && cfg == GEMM_CFG_256x256) {
+      if (cfg == gemm_pick_cfg(M, k.N, k.K, 1) && (cfg == GEMM_CFG_256x256 || cfg == GEMM_CFG_128x128)) {
         hipError_t e;
         {
           ProfScope ps_("gemm_qkv_up", st);
