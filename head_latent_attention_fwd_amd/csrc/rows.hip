@@ -341,21 +341,23 @@ __global__ void scatter_full_cache_kernel(const T* __restrict__ kv, const T* __r
 }
 
 // bf16 form: one 16-byte chunk (8 features) per thread; chunk c of (row m,
-// head h) is K^C (c < dn/8), k^R (next dr/8) or V (last dv/8).
+// head h) is K^C (c < dn/8), k^R (next dr/8) or V (last dv/8).  Grid: x =
+// token row m (its sequence and slot are uniform per workgroup), y covers
+// the H * (dn + dr + dv) / 8 chunks of the row in blocks of 256, so the
+// per-thread index arithmetic is 32-bit.
 __global__ void scatter_full_cache_bf16x8_kernel(const bf16_t* __restrict__ kv,
                                                  const bf16_t* __restrict__ kr, bf16_t* __restrict__ kc,
                                                  bf16_t* __restrict__ vc, int T_, int pos0, int L_cap,
-                                                 int H, int dn, int dr, int dv, long total,
+                                                 int H, int dn, int dr, int dv,
                                                  const int* __restrict__ seq_pos, int pos_max) {
-  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= total) return;
   const int W8 = (dn + dr + dv) / 8;
-  const int c = (int)(e % W8);
-  const int h = (int)((e / W8) % H);
-  const long m = e / ((long)W8 * H);
-  const long b = m / T_;
-  const int slot = seq_pos ? seq_position(seq_pos, (int)b, 0, pos_max) : (int)(m % T_) + pos0;
-  const long base = (b * H + h) * L_cap + slot;
+  const int e = blockIdx.y * blockDim.x + threadIdx.x;  // chunk within the row: (h, c)
+  if (e >= H * W8) return;
+  const long m = blockIdx.x;
+  const int b = (int)(blockIdx.x / (unsigned)T_);
+  const int slot = seq_pos ? seq_position(seq_pos, b, 0, pos_max) : (int)(blockIdx.x - (unsigned)b * T_) + pos0;
+  const int h = e / W8, c = e - h * W8;
+  const long base = ((long)b * H + h) * L_cap + slot;
   const bf16_t* src = kv + (m * H + h) * (dn + dv);
   const int f = 8 * c;
   if (f < dn) *(u32x4*)(kc + base * (dn + dr) + f) = *(const u32x4*)(src + f);
@@ -370,12 +372,13 @@ hipError_t scatter_full_cache(const T* kv, const T* kr, T* k_cache, T* v_cache, 
   if constexpr (sizeof(T) == 2) {
     const bool vec = d_nope % 8 == 0 && d_rope % 8 == 0 && d_v % 8 == 0 &&
                      ((uintptr_t)kv | (uintptr_t)kr | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16 == 0;
-    if (vec) {
-      const long total8 = (long)Bn * T_ * H * ((d_nope + d_rope + d_v) / 8);
-      if (total8 == 0) return hipSuccess;
-      hipLaunchKernelGGL(scatter_full_cache_bf16x8_kernel, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0,
-                         s, (const bf16_t*)kv, (const bf16_t*)kr, (bf16_t*)k_cache, (bf16_t*)v_cache, T_, pos0,
-                         L_cap, H, d_nope, d_rope, d_v, total8, seq_pos, pos_max);
+    const long rows = (long)Bn * T_;
+    const long row8 = (long)H * ((d_nope + d_rope + d_v) / 8);  // chunks per token row
+    if (vec && rows <= 0x7fffffffL && row8 <= 65535L * 256) {
+      if (rows == 0 || row8 == 0) return hipSuccess;
+      hipLaunchKernelGGL(scatter_full_cache_bf16x8_kernel, dim3((unsigned)rows, (unsigned)((row8 + 255) / 256)),
+                         dim3(256), 0, s, (const bf16_t*)kv, (const bf16_t*)kr, (bf16_t*)k_cache,
+                         (bf16_t*)v_cache, T_, pos0, L_cap, H, d_nope, d_rope, d_v, seq_pos, pos_max);
       return hipGetLastError();
     }
   }
