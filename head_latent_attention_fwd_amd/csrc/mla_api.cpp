@@ -355,10 +355,16 @@ bool gemm_stream_deferred(const char* name, const GemmParams& g, void* part, siz
 // weight-stream partials (b.upart, b.ukvpart) for the attention kernels to
 // sum; defer[0] / defer[1] then hold their StreamInfo (G = 0: materialised
 // in b.q / b.kv as usual).
+// With `extra` (a bf16 product that depends only on the latent norms' outputs,
+// e.g. the chunked latent form's per-head K/V expansion), the q up-projection,
+// when it runs alone, shares one launch with it; *extra_done reports whether
+// it did (otherwise the caller launches `extra` itself).
 int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int M, int rowsT,
                     int pos0, const float* rc, const float* rs, const ProjBufs& b,
                     void* latent_cache, int L_cap, hipStream_t st, StreamInfo* defer = nullptr,
-                    const int* seq_pos = nullptr, int pos_max = 0) {
+                    const int* seq_pos = nullptr, int pos_max = 0, const GemmParams* extra = nullptr,
+                    bool* extra_done = nullptr) {
+  if (extra_done) *extra_done = false;
   if (defer) defer[0].G = defer[1].G = 0;
   const int H = d->n_heads, dn = d->qk_nope_dim, dr = d->qk_rope_dim, dv = d->v_head_dim;
   const int dqk = dn + dr, ql = d->q_lora_rank, kl = d->kv_lora_rank;
@@ -436,6 +442,22 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
       LAUNCH("gemm_qkv_up", gemm_stream_bf16_pair(q, k, (float*)b.upart, (float*)b.ukvpart, defer[0],
                                                   defer[1], st));
       return MLA_OK;
+    }
+    if (extra && extra_done && !b.kv && M > 64 && extra->batch <= 1 &&
+        gemm_pick_cfg(extra->M, extra->N, extra->K, 1) == GEMM_CFG_256x256) {
+      // q (K = q_lora, the longer) first on every XCD, the extra product's
+      // short-K tiles filling in behind it
+      hipError_t e;
+      {
+        ProfScope ps_("gemm_q_up_kv_expand", st);
+        e = gemm_bf16_pair(q, *extra, EPI_BF16, GEMM_CFG_256x256, st);
+      }
+      if (e == hipSuccess) {
+        *extra_done = true;
+        return MLA_OK;
+      }
+      if (e != hipErrorInvalidValue) return fail(MLA_ERR_HIP, "gemm_bf16_pair failed: %s", hipGetErrorString(e));
+      (void)hipGetLastError();
     }
     if (defer) defer[0].G = defer[1].G = 0;
     if (!(defer && gemm_stream_deferred("gemm_q_up", q, b.upart, b.upart_floats, st, &defer[0], &r_)))
@@ -896,10 +918,20 @@ static int chunk_impl(const mla_dims* d, const mla_weights* w, const void* x, in
   const ProjBufs& b = pl.pb;
   // projections of the new rows at positions P0 + t; the latent form's cache
   // entries are written by the latent-norm kernel
-  if ((r = run_projections(d, w, x, (int)M, T, P0, rc, rs, b, form == 1 ? latent_cache : nullptr,
-                           L_cap, st)))
-    return r;
   const int Lk = P0 + T;  // keys per sequence
+  // latent form, bf16: per-head keys/values of cache rows 0 .. Lk-1,
+  // [K^C | V] = c^KV-hat W_UKV^T (the prefill's kv product applied to the
+  // cached latents), launched together with the q up-projection when it can
+  GemmParams kx = gp_base();
+  kx.A = (const bf16_t*)latent_cache; kx.lda = kl + dr; kx.sA = (long)L_cap * (kl + dr);
+  kx.B = (const bf16_t*)w->w_ukv; kx.ldb = kl; kx.sB = 0;
+  kx.C = pl.kv_exp; kx.ldc = (long)H * (dn + dv); kx.sC = (long)L_cap * H * (dn + dv);
+  kx.M = Lk; kx.N = H * (dn + dv); kx.K = kl; kx.batch = B;
+  const bool with_exp = form == 1 && d->dtype == MLA_BF16;
+  bool exp_done = false;
+  if ((r = run_projections(d, w, x, (int)M, T, P0, rc, rs, b, form == 1 ? latent_cache : nullptr,
+                           L_cap, st, nullptr, nullptr, 0, with_exp ? &kx : nullptr, &exp_done)))
+    return r;
   if (d->dtype == MLA_BF16) {
     FlashParams f;
     memset(&f, 0, sizeof f);
@@ -915,14 +947,7 @@ static int chunk_impl(const mla_dims* d, const mla_weights* w, const void* x, in
       f.kr2 = (const bf16_t*)k_cache + dn; f.kr_b = f.kc_b; f.kr_h = f.kc_h; f.kr_kb = dqk * 2;
       f.vv = (const bf16_t*)v_cache;      f.v_b = (long)H * L_cap * dv; f.v_h = (long)L_cap * dv; f.v_kb = dv * 2;
     } else {
-      // per-head keys/values of cache rows 0 .. Lk-1: [K^C | V] = c^KV-hat W_UKV^T
-      // (the prefill's kv product, applied to the cached latents)
-      GemmParams g = gp_base();
-      g.A = (const bf16_t*)latent_cache; g.lda = kl + dr; g.sA = (long)L_cap * (kl + dr);
-      g.B = (const bf16_t*)w->w_ukv; g.ldb = kl; g.sB = 0;
-      g.C = pl.kv_exp; g.ldc = (long)H * (dn + dv); g.sC = (long)L_cap * H * (dn + dv);
-      g.M = Lk; g.N = H * (dn + dv); g.K = kl; g.batch = B;
-      LAUNCH("gemm_kv_expand", gemm_bf16(g, EPI_BF16, -1, st));
+      if (!exp_done) LAUNCH("gemm_kv_expand", gemm_bf16(kx, EPI_BF16, -1, st));
       const bf16_t* kv = (const bf16_t*)pl.kv_exp;
       const long row = (long)H * (dn + dv);
       f.kc = kv;       f.kc_b = (long)L_cap * row; f.kc_h = dn + dv; f.kc_kb = (int)(row * 2);
