@@ -22,6 +22,7 @@
 //              lane holds g and u of the same output column and writes
 //              silu(g) * u (the SwiGLU steps of the dense block)
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -945,6 +946,335 @@ static hipError_t launch_v224(GemmParams p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Persistent 256 x 256 tile loop for launches of more than one round of tiles
+// with a bf16 or SwiGLU output.  With one workgroup per tile, every tile pays
+// its own first-stage wait and an epilogue staged through the whole LDS with
+// two workgroup barriers per pass (~5.5 us per tile on the paired
+// up-projections, against 1.4 us per 64-k stage).  Here one workgroup per CU
+// runs a list of tiles, and between two tiles:
+//   - the next tile's first stage is issued into ring buffer 0 as soon as
+//     every wave has read the last stage;
+//   - each wave writes its own 128 x 64 part of the finished tile through a
+//     private 4 KB LDS slot (the 32 KB beyond the 128 KB ring), 32 rows at a
+//     time, and stores whole 128-byte row segments: no workgroup barrier,
+//     since a wave's LDS operations complete in issue order;
+//   - the second stage is issued after the stores, so that waiting until at
+//     most one stage of loads is in flight (loads complete in order) proves
+//     the first stage landed without waiting for the stores.
+// The first k-step of every tile starts its MFMA chains from a zero C
+// operand instead of zeroing 128 accumulators.
+//
+// Schedule (static, per XCD): the logical order is the one-workgroup-per-tile
+// launch's (workgroup b on XCD b % 8, XCD-contiguous tile ranges, product 0
+// first), and the W workgroups of an XCD split its slots longest first:
+// product 0's slots round robin (slot w + k W to workgroup w), then
+// product 1's slots in runs whose lengths the launcher computes by greedy
+// least-loaded assignment with per-tile costs of (K / 64 + 2) stages.  The
+// workgroups with one more product-0 slot (w < n0 % W) and the others each
+// start equally loaded, and ties go to the lower index, so in each of the two
+// groups the first e workgroups get a + 1 runs of product 1 and the rest a:
+// four numbers per XCD describe the schedule (a kernel argument block of a
+// kilobyte of per-workgroup tables launched measurably slower).
+// Products with a bias keep the per-tile kernel.
+// ---------------------------------------------------------------------------
+struct PersSched {
+  int W;                        // workgroups per XCD (grid 8 W)
+  int aH[8], eH[8], aL[8], eL[8];  // pairs: product-1 run lengths per XCD (see above)
+};
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_pers_kernel(GemmGroup gg, PersSched ps) {
+  static_assert(EPI == EPI_BF16 || EPI == EPI_SWIGLU, "bf16-output epilogues only");
+  constexpr int BM = 256, BN = 256, WN = 4;
+  constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32, NMF = FM * FN, NRD = FM + FN;
+  constexpr int KSTEPS = 4, CH = 8, ROWB = 128;
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE_B = A_BYTES + B_BYTES;  // 64 KB
+  constexpr int A_DMA = A_BYTES / 1024 / 8, B_DMA = B_BYTES / 1024 / 8;                 // 4 + 4
+  static_assert(A_DMA + B_DMA == 8, "the stage wait below counts 8 loads per wave");
+  constexpr int RPD = 1024 / ROWB;  // rows per DMA
+  constexpr int WST = 4096;         // per-wave epilogue staging
+  __shared__ u32x4 lds_raw[(2 * STAGE_B + 8 * WST) / 16];  // 160 KB
+  char* ldsc = (char*)lds_raw;
+  const unsigned lds_base = (unsigned)(unsigned long)(__attribute__((address_space(3))) char*)lds_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = tid >> 6, wv = __builtin_amdgcn_readfirstlane(wid);
+  const int wm = wid / WN, wn = wid % WN;
+  const int lr = lane & 31, lg = lane >> 5;
+
+  // ---- this workgroup's slots ----
+  const int x = blockIdx.x & 7, w = blockIdx.x >> 3, W = ps.W;
+  const int total = gg.tiles0 + (gg.n == 2 ? gg.tiles1 : 0);
+  const int slots = total / 8 + (x < total % 8 ? 1 : 0);
+  const int n0 = gg.n == 2 ? gg.tiles0 / 8 + (x < gg.tiles0 % 8 ? 1 : 0) : slots;
+  const int nl = w < n0 ? (n0 - w + W - 1) / W : 0;
+  int ns = 0, sbase = n0;
+  if (gg.n == 2) {
+    const int r0 = n0 % W, aH = ps.aH[x], eH = ps.eH[x], aL = ps.aL[x], eL = ps.eL[x];
+    if (w < r0) {
+      ns = aH + (w < eH ? 1 : 0);
+      sbase += w * aH + min(w, eH);
+    } else {
+      const int u = w - r0;
+      ns = aL + (u < eL ? 1 : 0);
+      sbase += r0 * aH + eH + u * aL + min(u, eL);
+    }
+  }
+  const int nitems = nl + ns;
+  if (nitems == 0) return;
+
+  // ---- per-tile state: source offsets of this wave's DMAs, tile origin ----
+  int a_vo[A_DMA], b_vo[B_DMA];
+  unsigned b_src2 = 0;
+  u32x4 ra, rb1, rb2;
+  int nst = 0, prob = 0, m0 = 0, n0c = 0;
+  auto setup = [&](int k) {
+    const int slot = k < nl ? w + k * W : sbase + (k - nl);
+    int lin;
+    gemm_tile_of(gg, 8 * slot + x, prob, lin);
+    const GemmParams& p = gg.p[prob];
+    const int GM = p.group_m;
+    const int group = lin / (GM * p.tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(p.tiles_m - first_m, GM);
+    const int within = lin - group * GM * p.tiles_n;
+    m0 = (first_m + within % gm) * BM;
+    n0c = (within / gm) * BN;
+    nst = p.K / 64;
+#pragma unroll
+    for (int d = 0; d < A_DMA; ++d) {
+      const int r = RPD * (wv * A_DMA + d) + lane / CH;
+      const int c = (lane % CH) ^ gemm_swz(r);
+      a_vo[d] = (min(m0 + r, p.M - 1) * (int)p.lda + 8 * c) * 2;
+    }
+    b_src2 = 0;
+#pragma unroll
+    for (int d = 0; d < B_DMA; ++d) {
+      const int r = RPD * (wv * B_DMA + d) + lane / CH;
+      const int c = (lane % CH) ^ gemm_swz(r);
+      int src;
+      if (EPI == EPI_SWIGLU) {
+        const int rb = r >> 5;
+        src = min(n0c / 2 + (rb >> 1) * 32 + (r & 31), p.N / 2 - 1);
+        if (rb & 1) b_src2 |= 1u << d;
+      } else {
+        src = min(n0c + r, p.N - 1);
+        if (p.b_split > 0 && n0c + RPD * (wv * B_DMA + d) >= p.b_split) {
+          src -= p.b_split;
+          b_src2 |= 1u << d;
+        }
+      }
+      b_vo[d] = (src * (int)p.ldb + 8 * c) * 2;
+    }
+    ra = gemm_rsrc(p.A);
+    rb1 = gemm_rsrc(p.B);
+    rb2 = gemm_rsrc(p.B2 ? p.B2 : p.B);
+  };
+
+#define PS_ISSUE(u_)                                                                         \
+  do {                                                                                       \
+    const unsigned sb_ = lds_base + ((u_) & 1) * STAGE_B;                                    \
+    const int ko_ = ROWB * (u_);                                                             \
+    _Pragma("unroll") for (int d = 0; d < A_DMA; ++d)                                        \
+      gemm_dma16(sb_ + 1024 * (wv * A_DMA + d), a_vo[d] + ko_, ra);                          \
+    _Pragma("unroll") for (int d = 0; d < B_DMA; ++d)                                        \
+      gemm_dma16(sb_ + A_BYTES + 1024 * (wv * B_DMA + d), b_vo[d] + ko_,                     \
+                 ((b_src2 >> d) & 1) ? rb2 : rb1);                                           \
+  } while (0)
+  const int sw = gemm_swz(lr);  // fragment rows are lr (mod 32)
+  const int a_rd = (wm * WTM + lr) * ROWB, b_rd = A_BYTES + (wn * WTN + lr) * ROWB;
+#define PS_FREAD(u_, s_, slot)                                                               \
+  do {                                                                                       \
+    const char* sb_ = ldsc + ((u_) & 1) * STAGE_B;                                           \
+    const int co_ = 16 * ((2 * (s_) + lg) ^ sw);                                             \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                           \
+      fa[slot][i] = *(const bf16x8*)(sb_ + a_rd + i * 32 * ROWB + co_);                      \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
+      fb[slot][j] = *(const bf16x8*)(sb_ + b_rd + j * 32 * ROWB + co_);                      \
+  } while (0)
+#define PS_MFMAS(slot, zero_)                                                                \
+  _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                          \
+    const int i = q / FN, j = q % FN;                                                        \
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i],            \
+                                                        (zero_) ? floatx16{} : acc[i][j], 0, 0, 0); \
+  }
+#define PS_SCHED()                                                                           \
+  _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                          \
+    MLA_SGB(SG_MFMA, 1);                                                                     \
+    if (q < NRD) MLA_SGB(SG_DS_RD, 1);                                                       \
+  }
+
+  bf16x8 fa[2][FM], fb[2][FN];
+  floatx16 acc[FM][FN];
+  // one 64-k stage: k-step s + 1's fragments read under k-step s's MFMAs; the
+  // barrier before the last k-step, whose MFMAs cover the next stage's first
+  // fragment reads (FIRST: the stage that starts the accumulators)
+  auto stage = [&](int t, auto first_) {
+    constexpr bool FIRST = decltype(first_)::value;
+#pragma unroll
+    for (int s = 0; s + 1 < KSTEPS; ++s) {
+      PS_FREAD(t, s + 1, (s + 1) & 1);
+      PS_MFMAS(s & 1, FIRST && s == 0)
+      PS_SCHED()
+    }
+    // stage t + 1 landed (this wave's loads; the barrier covers the others')
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 2 < nst) PS_ISSUE(t + 2);  // into stage t's buffer, read by now
+    PS_FREAD(min(t + 1, nst - 1), 0, 0);
+    PS_MFMAS(1, false)
+    PS_SCHED()
+  };
+
+  setup(0);
+  PS_ISSUE(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (nst > 1) PS_ISSUE(1);
+  PS_FREAD(0, 0, 0);
+
+  for (int k = 0; k < nitems; ++k) {
+    stage(0, std::true_type{});
+    for (int t = 1; t < nst; ++t) stage(t, std::false_type{});
+
+    // ---- epilogue of this tile; the next tile's first stage loads meanwhile ----
+    const int eprob = prob, em0 = m0, en0 = n0c;
+    __syncthreads();  // every wave's last fragment reads done: both ring buffers free
+    const bool more = k + 1 < nitems;
+    if (more) {
+      setup(k + 1);
+      PS_ISSUE(0);
+    }
+    {
+      const GemmParams& p = gg.p[eprob];
+      // this wave's output part: rows wm WTM + 32 i + (0..31), OCW columns
+      constexpr int OCW = (EPI == EPI_SWIGLU) ? WTN / 2 : WTN;
+      constexpr int RB = OCW * 2, NCH = RB / 16;  // staged row bytes, 16-byte chunks per row
+      constexpr int RPI = 64 / NCH;               // rows per 16-byte-per-lane read
+      const int out_cols = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
+      const int ocol0 = (EPI == EPI_SWIGLU) ? en0 / 2 + wn * OCW : en0 + wn * OCW;
+      bf16_t* C = (bf16_t*)p.C;
+      const int rows_M = p.M;
+      const long ldc = p.ldc;
+      char* wst = ldsc + 2 * STAGE_B + wid * WST;
+      // chunk swizzle: the 32 rows one write instruction covers spread over all
+      // 64 banks, and the rows one 16-lane read phase covers are disjoint
+      auto swz = [](int r) { return (EPI == EPI_SWIGLU) ? ((r >> 2) & 3) : ((r >> 1) & 7); };
+      const int rrow = lane / NCH, rch = lane % NCH;  // read-out: row within the group, chunk
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        asm volatile("" ::: "memory");  // the previous rows' reads stay before these writes
+#pragma unroll
+        for (int j = 0; j < FN; j += (EPI == EPI_SWIGLU ? 2 : 1))
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (EPI == EPI_SWIGLU) {
+                const float gg_ = acc[i][j][4 * g + q], uu = acc[i][j + 1][4 * g + q];
+                v[q] = gg_ / (1.f + __expf(-gg_)) * uu;
+              } else {
+                v[q] = acc[i][j][4 * g + q];
+              }
+            }
+            const int c = (EPI == EPI_SWIGLU) ? g : 4 * j + g;  // 16-byte chunk of the row
+            *(u32x2*)(wst + lr * RB + 16 * (c ^ swz(lr)) + 8 * lg) = u32x2{pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
+          }
+        asm volatile("" ::: "memory");  // a wave's LDS operations complete in order
+        u32x4 sv[32 / RPI];
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+          const int r = it * RPI + rrow;
+          sv[it] = *(const u32x4*)(wst + r * RB + 16 * (rch ^ swz(r)));
+        }
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+          const int row = em0 + wm * WTM + 32 * i + it * RPI + rrow, col = ocol0 + 8 * rch;
+          if (row >= rows_M || col >= out_cols) continue;
+          bf16_t* dst = C + (long)row * ldc + col;
+          if (col + 8 <= out_cols) {
+            *(u32x4*)dst = sv[it];
+          } else {
+            for (int q = 0; q < out_cols - col; ++q)
+              dst[q] = (bf16_t)((q & 1) ? (sv[it][q >> 1] >> 16) : (sv[it][q >> 1] & 0xffffu));
+          }
+        }
+      }
+    }
+    if (more) {
+      // stage 1 goes after the stores: at most its 8 loads still in flight
+      // means stage 0 has landed, whatever the stores are doing
+      if (nst > 1) {
+        PS_ISSUE(1);
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();
+      PS_FREAD(0, 0, 0);
+    }
+  }
+#undef PS_ISSUE
+#undef PS_FREAD
+#undef PS_MFMAS
+#undef PS_SCHED
+}
+
+// Persistent launch of a 256 x 256 bf16 / SwiGLU product (or pair) without
+// bias: one workgroup per CU when the tiles take more than one round.  Pairs
+// need product 0 to be the longer one (it is scheduled first).
+static bool pers_ok(const GemmGroup& g) {
+  const long total = g.tiles0 + (g.n == 2 ? g.tiles1 : 0);
+  if (total <= 256) return false;
+  for (int i = 0; i < g.n; ++i)
+    if (g.p[i].batch != 1 || g.p[i].ksplit != 1 || g.p[i].kchunk != g.p[i].K || g.p[i].K % 64 != 0 ||
+        g.p[i].bias)
+      return false;
+  return g.n == 1 || g.p[0].K >= g.p[1].K;
+}
+
+// Greedy least-loaded split of each XCD's product-1 slots (ties to the lower
+// workgroup index), in the compact form the kernel reads.  Within each of the
+// two groups the loads differ by at most one product-1 tile and the
+// least-loaded member is the first one holding the group's smallest count, so
+// the greedy choice only compares the two groups' candidates: O(1) per slot.
+static bool pers_plan(const GemmGroup& g, PersSched& ps) {
+  constexpr int W = 32;  // workgroups per XCD: one per CU of the 256
+  ps = PersSched{};
+  ps.W = W;
+  if (g.n != 2) return true;
+  const long c0 = g.p[0].K / 64 + 2, c1 = g.p[1].K / 64 + 2;
+  const int total = g.tiles0 + g.tiles1;
+  for (int x = 0; x < 8; ++x) {
+    const int slots = total / 8 + (x < total % 8 ? 1 : 0);
+    const int n0 = g.tiles0 / 8 + (x < g.tiles0 % 8 ? 1 : 0);
+    const int r0 = n0 % W, sz[2] = {r0, W - r0};
+    const long base[2] = {(n0 / W + 1) * c0, (n0 / W) * c0};
+    long cnt[2] = {0, 0};  // product-1 slots given to group H (w < r0) and L
+    for (int j = n0; j < slots; ++j) {
+      // the group's least-loaded member holds cnt / size slots
+      long best = -1;
+      int bg = 0;
+      for (int gi = 0; gi < 2; ++gi) {
+        if (sz[gi] == 0) continue;
+        const long ld = base[gi] + (cnt[gi] / sz[gi]) * c1;
+        if (best < 0 || ld < best) {  // equal loads: group H holds the lower index
+          best = ld;
+          bg = gi;
+        }
+      }
+      ++cnt[bg];
+    }
+    ps.aH[x] = r0 ? (int)(cnt[0] / r0) : 0;
+    ps.eH[x] = r0 ? (int)(cnt[0] % r0) : 0;
+    ps.aL[x] = (int)(cnt[1] / (W - r0));
+    ps.eL[x] = (int)(cnt[1] % (W - r0));
+  }
+  return true;
+}
+
 template <int BM, int BN, int WM, int WN, int EPI>
 static hipError_t launch_cfg(const GemmParams* ps, int n, hipStream_t s) {
   GemmGroup g;
@@ -961,6 +1291,13 @@ static hipError_t launch_cfg(const GemmParams* ps, int n, hipStream_t s) {
   g.tiles0 = g.p[0].tiles_m * g.p[0].tiles_n;
   g.tiles1 = n == 2 ? g.p[1].tiles_m * g.p[1].tiles_n : 0;
   dim3 grid(g.tiles0 + g.tiles1, ps[0].batch * ps[0].ksplit);
+  if constexpr (BM == 256 && BN == 256 && (EPI == EPI_BF16 || EPI == EPI_SWIGLU)) {
+    PersSched sch;
+    if (dma && pers_ok(g) && pers_plan(g, sch)) {
+      hipLaunchKernelGGL(gemm_pers_kernel<EPI>, dim3(8 * sch.W), dim3(512), 0, s, g, sch);
+      return hipGetLastError();
+    }
+  }
   if constexpr (BM >= 128) {
     if (dma) {
       hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI, true>), grid, dim3(WM * WN * 64), 0, s, g);
