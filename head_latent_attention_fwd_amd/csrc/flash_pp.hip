@@ -48,6 +48,9 @@ constexpr int PP_KR = 64 * 128;              // rotary key tile (64 features)
 constexpr int PP_V = 64 * 256;               // value tile (128 features)
 constexpr int PP_STG = PP_KC + PP_KR + PP_V; // 40 KB
 constexpr int PP_DPW = 5;                    // DMAs per wave per tile (2 + 1 + 2)
+constexpr int PP_QROW = 192 * 2;             // bytes of one query row (one head)
+constexpr int PP_QST = PP_BQ * PP_QROW;      // 96 KB: the tile's queries, staged in LDS
+constexpr int PP_LDS = PP_NST * PP_STG > PP_STG + PP_QST ? PP_NST * PP_STG : PP_STG + PP_QST;
 constexpr float PP_LAZY = 8.0f;              // raise the running max past this margin (log2)
 
 MLA_DEV void pp_dma16(unsigned m0, int voff, u32x4 rsrc) {
@@ -63,6 +66,10 @@ MLA_DEV void pp_dma16(unsigned m0, int voff, u32x4 rsrc) {
 }
 // chunk swizzle of a value-tile row
 MLA_DEV int pp_vswz(int row) { return (row & 3) << 2; }
+// chunk swizzle of a staged query row (384 B = 96 banks): rows r and r + 1 sit
+// 32 banks apart, and XOR (r >> 1) & 7 spreads the 16 rows of a fragment
+// read over the remaining eight 16-byte positions
+MLA_DEV int pp_qswz(int row) { return (row >> 1) & 7; }
 MLA_DEV u32x4 pp_rsrc(const void* base, long bytes) {
   const unsigned long a = (unsigned long)base;
   u32x4 r;
@@ -75,7 +82,7 @@ MLA_DEV u32x4 pp_rsrc(const void* base, long bytes) {
 }  // namespace
 
 __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[PP_NST * PP_STG];
+  __shared__ __attribute__((aligned(16))) char lds[PP_LDS];
   const unsigned lds_base = (unsigned)(unsigned long)(__attribute__((address_space(3))) char*)lds;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -132,7 +139,7 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
   const u32x4 rvv = pp_rsrc(p.vv + b * p.v_b + h * p.v_h, (long)nkeys * p.v_kb);
 #define PP_ISSUE(tt)                                                                         \
   do {                                                                                       \
-    const unsigned sb_ = lds_base + ((tt) % PP_NST) * PP_STG;                                \
+    const unsigned sb_ = lds_base + (((tt) - k_lo) % PP_NST) * PP_STG;                       \
     const int kk_ = 64 * (tt);                                                               \
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                            \
       pp_dma16(sb_ + 1024 * (2 * w + i), kc_vo[i] + kk_ * p.kc_kb, rkc);                     \
@@ -141,22 +148,32 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
       pp_dma16(sb_ + PP_KC + PP_KR + 1024 * (2 * w + i), v_vo[i] + kk_ * p.v_kb, rvv);       \
   } while (0)
 
-  // Prologue loads: the first key tile is issued before the queries, so the
-  // two (and the RoPE rows) are in flight together.
+  // Prologue loads: the first key tile (ring slot 0: slots count from the
+  // split's first tile), then the tile's 256 query rows by direct-to-LDS
+  // loads into slots 1 and 2 and the 16 KB past the ring, and the RoPE rows
+  // of this lane's query, all in flight together.  Staged rows cost about
+  // three 128-byte lines each, where loading the MFMA fragments straight
+  // from memory (each load instruction spans 32 rows) costs 32 per load.
   for (int tt = k_lo; tt < k_lo + PP_NST - 2 && tt < n_kv; ++tt) PP_ISSUE(tt);
-  // This wave's 32 queries as MFMA B fragments: features 16 s + 8 lg .. +8;
-  // the rotary features (s >= 8) are rotated by the RoPE row of the position
-  bf16x8 qf[12];
   {
-    const int qrow = min(q0 + 32 * w + lr, p.T - 1);
-    const bf16_t* qp = p.q + ((rowbase + qrow) * HS + h) * 192 + 8 * lg;
+    // staged chunk i = 64 (12 w + d) + lane: row i / 24, 16-byte position
+    // i % 24, holding logical chunk (i % 24) ^ pp_qswz(row)
+    const u32x4 rq = pp_rsrc(p.q + (rowbase * HS + h) * 192, (long)p.T * HS * PP_QROW);
 #pragma unroll
-    for (int s = 0; s < 12; ++s) {
-      u32x4 v = *(const u32x4*)(qp + 16 * s);
-      if (s >= 8) v = rope8_bf16(v, p.rcos, p.rsin, p.P0 + qrow, 32, (16 * s + 8 * lg - 128) / 2);
-      qf[s] = __builtin_bit_cast(bf16x8, v);
+    for (int d = 0; d < PP_QST / 1024 / 8; ++d) {
+      const int i = 64 * (12 * w + d) + lane, row = i / 24, c = (i % 24) ^ pp_qswz(row);
+      pp_dma16(lds_base + PP_STG + 1024 * (12 * w + d), min(q0 + row, p.T - 1) * (int)HS * PP_QROW + 16 * c, rq);
     }
   }
+  const int qrow = min(q0 + 32 * w + lr, p.T - 1);
+  floatx4 rcs[4][2];  // RoPE (cos, sin) of the rotary fragments s = 8..11
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const long o = (long)(p.P0 + qrow) * 32 + (16 * s + 8 * lg) / 2;
+    rcs[s][0] = *(const floatx4*)(p.rcos + o);
+    rcs[s][1] = *(const floatx4*)(p.rsin + o);
+  }
+  bf16x8 qf[12];  // this wave's 32 queries as MFMA B fragments: features 16 s + 8 lg .. +8
 
   // ---- fragment offsets inside a stage (tile-invariant).
   // K fragment (s, mb): key row 32 mb + lr.  s < 8: content chunk 2 s + lg;
@@ -196,7 +213,7 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
 
 #define PP_QK(tt)                                                                            \
   do {                                                                                       \
-    const char* sb_ = lds + ((tt) % PP_NST) * PP_STG;                                        \
+    const char* sb_ = lds + (((tt) - k_lo) % PP_NST) * PP_STG;                               \
     _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                         \
       _Pragma("unroll") for (int e = 0; e < 16; ++e) S[mb][e] = 0.f;                         \
     constexpr int RQ = 6;                                                                    \
@@ -266,7 +283,7 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
         psum_ += pv_;                                                                        \
       }                                                                                      \
     l_run += psum_;                                                                          \
-    const char* sb_ = lds + ((tt) % PP_NST) * PP_STG;                                        \
+    const char* sb_ = lds + (((tt) - k_lo) % PP_NST) * PP_STG;                               \
     /* fragment y = 4 ks + d; a ring of 3 keeps the transposed reads 2 ahead */             \
     s16x4 tv_[3][2];                                                                         \
     _Pragma("unroll") for (int y = 0; y < 2; ++y) PP_VREAD(sb_, y, tv_[y]);                  \
@@ -298,6 +315,25 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
   // buffer whose last reader (PV of the second half) finished before it.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  {
+    // the rotary features (s >= 8) are rotated by the RoPE row of the position
+    const int r = 32 * w + lr;
+    const char* qs = lds + PP_STG + r * PP_QROW;
+#pragma unroll
+    for (int s = 0; s < 12; ++s) {
+      u32x4 v = *(const u32x4*)(qs + 16 * ((2 * s + lg) ^ pp_qswz(r)));
+      if (s >= 8) {
+        const floatx4 c = rcs[s - 8][0], sn = rcs[s - 8][1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = lo_bf(v[i]), bb = hi_bf(v[i]);
+          v[i] = pack2bf(a * c[i] - bb * sn[i], a * sn[i] + bb * c[i]);
+        }
+      }
+      qf[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  __syncthreads();  // every wave's queries read: slots 1 and 2 take key tiles now
   if (k_lo + PP_NST - 2 < n_kv) PP_ISSUE(k_lo + PP_NST - 2);
   for (int k = k_lo; k < n_kv; ++k) {
     // The fragment offsets are loop-invariant, and left alone the compiler
@@ -383,7 +419,9 @@ bool flash_prefill_fits(int T, int H) {
 bool flash_pp_ok(const FlashParams& p) {
   // per-key byte offsets (64 keys past the last tile included) stay below 2^31
   const long nk = (long)p.P0 + p.T + 64;
+  // the staged query rows' byte offsets stay below 2^31 too
   return p.P0 >= 0 && nk * p.kc_kb < 0x7fffffffL && nk * p.kr_kb < 0x7fffffffL &&
+         (long)p.T * p.H * PP_QROW < 0x7fffffffL &&
          nk * p.v_kb < 0x7fffffffL && p.kc_kb % 16 == 0 && p.kr_kb % 16 == 0 && p.v_kb % 16 == 0;
 }
 
