@@ -383,9 +383,14 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
     }
     return;
   }
-  if (qrow_l < p.T) {
-    const float inv = 1.f / l_tot;
-    bf16_t* op = p.out + (rowbase + qrow_l) * (HS * 128) + (long)h * 128 + 4 * lg;
+  // The normalised tile goes through the (now free) ring as 256 rows of
+  // 256 bytes, 16-byte chunk c of row r at c ^ (r & 15), and leaves as whole
+  // row segments, 16 bytes per lane (a lane's own outputs are 8-byte pieces
+  // of 32 different rows per store).
+  const float inv = 1.f / l_tot;
+  __syncthreads();  // every wave's last key tile read
+  {
+    const int r = 32 * w + lr;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -393,8 +398,15 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
         u32x2 v;
         v[0] = pack2bf(O[d][4 * i + 0] * inv, O[d][4 * i + 1] * inv);
         v[1] = pack2bf(O[d][4 * i + 2] * inv, O[d][4 * i + 3] * inv);
-        *(u32x2*)(op + 32 * d + 8 * i) = v;
+        *(u32x2*)(lds + r * 256 + 16 * ((4 * d + i) ^ (r & 15)) + 8 * lg) = v;
       }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < PP_BQ * 16 / 512; ++it) {
+    const int idx = tid + 512 * it, r = idx >> 4, c = idx & 15;
+    const u32x4 v = *(const u32x4*)(lds + r * 256 + 16 * (c ^ (r & 15)));
+    if (q0 + r < p.T) *(u32x4*)(p.out + (rowbase + q0 + r) * (HS * 128) + (long)h * 128 + 8 * c) = v;
   }
 }
 
