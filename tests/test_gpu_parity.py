@@ -90,6 +90,27 @@ def test_prefill_kimi_ragged_T2000_sampled_rows():
     assert_close(from_dev(got)[:, rows], want, TOL_BF16, "kimi prefill T=2000 sampled rows")
 
 
+def test_prefill_24_heads_T2300_sampled_rows():
+    """24 heads at T=2300: the q and kv up-projections have 9 x 18 and 9 x 24
+    tiles of 256 x 256, 378 in all with neither count a multiple of the 8
+    XCDs, so the persistent tile loop splits them unevenly over the XCDs and
+    its product-1 runs differ between XCDs (with Kimi widths every count is a
+    multiple of 8).  One sampled query row in every 256-row block, so a tile
+    computed twice or not at all shows up."""
+    od = ref.MLADims(d_model=7168, n_heads=24, q_lora_rank=1536, kv_lora_rank=512,
+                     qk_nope_dim=128, qk_rope_dim=64, v_head_dim=128)
+    B, T = 1, 2300
+    log(f"[prefill 24 heads] B={B} T={T} bf16")
+    x, w = synth.prefill_inputs(od, B, T, 1015, bf16=True)
+    rows = sorted(set([0, 255, 256, 511, 700, 1023, 1100, 1400, 1535, 1800, 2047, 2048, 2200, T - 1] +
+                      list(np.random.default_rng(8).choice(T, 8, replace=False))))
+    want = ref.mla_prefill(od, oracle_weights(w), x.astype(np.float64), rows=rows)
+    d = dims_of(mla, od, "bf16")
+    got = mla.mla_prefill(d, weights_to_dev(w, "bf16", DEV), to_dev(x, "bf16", DEV), _rope(od, T))
+    torch.cuda.synchronize()
+    assert_close(from_dev(got)[:, rows], want, TOL_BF16, "24-head prefill T=2300 sampled rows")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_prefill_writes_caches(dt):
     od = ref.TINY if dt == "f32" else KIMI_NARROW
