@@ -789,7 +789,7 @@ MLA_DEV void v224_stage_f32(const floatx16 (&acc)[2][4], float* cst, int rg, int
 
 template <int EPI>
 __global__ __launch_bounds__(512) void gemm_v224_kernel(GemmParams p) {
-  static_assert(EPI == EPI_BF16 || EPI == EPI_RESID, "bf16 and residual epilogues only");
+  static_assert(EPI == EPI_BF16 || EPI == EPI_RESID || EPI == EPI_F32, "bf16, residual and fp32-partial epilogues");
   __shared__ __attribute__((aligned(16))) char lds[V_LDS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -807,6 +807,9 @@ __global__ __launch_bounds__(512) void gemm_v224_kernel(GemmParams p) {
   const int within = lin - group * GM * p.tiles_n;
   const int tm = first_m + within % gm, tv = within / gm;
   const int m0 = tm * V_BM;
+  // K slice of this workgroup (grid.y: fp32-partial launches cut K into ksplit slices)
+  const int split = blockIdx.y;
+  const int k_begin = split * p.kchunk, k_end = min(p.K, k_begin + p.kchunk);
 
   floatx16 acc[2][4];
 #pragma unroll
@@ -827,7 +830,7 @@ __global__ __launch_bounds__(512) void gemm_v224_kernel(GemmParams p) {
     for (int d = 0; d < 4; ++d) {
       const int r = 8 * (4 * wv + d) + lane / 8;
       const int c = (lane % 8) ^ gemm_swz(r);
-      a_vo[d] = (min(m0 + r, p.M - 1) * (int)p.lda + 8 * c) * 2;
+      a_vo[d] = (min(m0 + r, p.M - 1) * (int)p.lda + k_begin + 8 * c) * 2;
     }
     const int b_dma0 = cg ? 16 + 3 * (wv - 4) : 4 * wv;
 #pragma unroll
@@ -836,13 +839,13 @@ __global__ __launch_bounds__(512) void gemm_v224_kernel(GemmParams p) {
       const int r = 8 * g + lane / 8;  // row of the B tile
       const int c = (lane % 8) ^ gemm_swz(r);
       const int src = min(v224_col(tv, min(g, 27) / 4, nt) + 8 * (g % 4) + lane / 8, p.N - 1);
-      b_vo[d] = (src * (int)p.ldb + 8 * c) * 2;
+      b_vo[d] = (src * (int)p.ldb + k_begin + 8 * c) * 2;
     }
     const u32x4 ra = gemm_rsrc(p.A), rb = gemm_rsrc(p.B);
     const unsigned lds_base = (unsigned)(unsigned long)(__attribute__((address_space(3))) char*)lds;
     const int sw = gemm_swz(lr);  // fragment rows are lr (mod 32)
     const int a_rd = (64 * rg + lr) * V_ROWB, b_rd = V_A_BYTES + (32 * s0 + lr) * V_ROWB;
-    const int nst = p.K / V_SK;
+    const int nst = (k_end - k_begin) / V_SK;
     if (cg == 0)
       v224_loop<4>(acc, lds, lds_base, nst, wv, a_vo, b_vo, b_dma0, ra, rb, a_rd, b_rd, sw, lg);
     else
@@ -873,6 +876,33 @@ __global__ __launch_bounds__(512) void gemm_v224_kernel(GemmParams p) {
       const int row = m0 + rl;
       if (row >= rows_M) continue;
       *(u32x4*)(C + (long)row * ldc + v224_col(tv, c8 >> 2, nt) + 8 * (c8 & 3)) = sv[it];
+    }
+  } else if constexpr (EPI == EPI_F32) {
+    // fp32 partial of this K slice, staged as the residual epilogue stages it
+    // (two passes of 128 rows), 8 columns per thread as two 16-byte stores
+    float* cst = (float*)lds;
+    float* Cf = (float*)p.C + (long)split * p.split_stride;
+    constexpr int NIT = 128 * CH8 / 512;  // 7
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      __syncthreads();  // LDS free: last K stage read (pass 0) or previous pass stored
+      const int rlo = 128 * pass;
+      if ((rg >> 1) == pass) {
+        if (cg == 0) v224_stage_f32<4>(acc, cst, rg, s0, lr, lg, rlo);
+        else v224_stage_f32<3>(acc, cst, rg, s0, lr, lg, rlo);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int idx = tid + it * 512, rl = idx / CH8, c8 = idx % CH8;
+        const int row = m0 + rlo + rl;
+        const floatx4 a = *(const floatx4*)&cst[v224_fidx(rl, 8 * c8)];
+        const floatx4 b = *(const floatx4*)&cst[v224_fidx(rl, 8 * c8 + 4)];
+        if (row >= rows_M) continue;
+        float* dst = Cf + (long)row * ldc + v224_col(tv, c8 >> 2, nt) + 8 * (c8 & 3);
+        *(floatx4*)dst = a;
+        *(floatx4*)(dst + 4) = b;
+      }
     }
   } else {
     // residual add in two passes of 128 rows (waves with rg < 2, then rg >= 2)
@@ -923,15 +953,23 @@ __global__ __launch_bounds__(512) void gemm_v224_kernel(GemmParams p) {
   }
 }
 
-// The 256 x 224 tiling applies to single bf16-output products whose width
-// is a multiple of 1792 (seven 256-column tiles) with no batch, K split or
-// second weight, when its whole waves beat the 256 x 256 tile's.
-static bool v224_ok(const GemmParams& p, int epi) {
-  if ((epi != EPI_BF16 && epi != EPI_RESID) || p.N % 1792 != 0 || p.batch != 1 || p.ksplit != 1 ||
-      p.b_split > 0 || p.B2 || p.K % V_SK != 0 || p.kchunk != p.K || p.M <= 0)
-    return false;
+// The 256 x 224 tiling applies to single products whose width is a multiple
+// of 1792 (seven 256-column tiles) with no batch or second weight: bf16 and
+// residual outputs over the whole K (chosen automatically when its whole
+// waves beat the 256 x 256 tile's), or fp32 partials of K slices (chosen by
+// the small-product plan).
+static bool v224_shape_ok(const GemmParams& p, int epi) {
+  if (epi != EPI_BF16 && epi != EPI_RESID && epi != EPI_F32) return false;
+  if (p.N % 1792 != 0 || p.batch != 1 || p.b_split > 0 || p.B2 || p.K % V_SK != 0 || p.M <= 0) return false;
+  if (epi != EPI_F32 && (p.ksplit != 1 || p.kchunk != p.K)) return false;
+  if (p.kchunk % V_SK != 0 || p.kchunk <= 0 || (long)p.ksplit * p.kchunk < p.K) return false;
+  if (epi == EPI_F32 && (p.bias || (p.ldc % 4) != 0)) return false;
   if ((long)p.M * p.lda * 2 >= 0x7fffffffL || (long)p.N * p.ldb * 2 >= 0x7fffffffL) return false;
-  if ((p.ldc % 8) != 0 || (epi == EPI_RESID && (p.ldr % 8) != 0)) return false;
+  if ((p.ldc % 8) != 0 && epi != EPI_F32) return false;
+  return epi != EPI_RESID || (p.ldr % 8) == 0;
+}
+static bool v224_ok(const GemmParams& p, int epi) {
+  if (epi == EPI_F32 || !v224_shape_ok(p, epi)) return false;
   const long tm = (p.M + 255) / 256;
   const long w256 = (tm * (p.N / 256) + 255) / 256, w224 = (tm * (p.N / 224) + 255) / 256;
   return w224 * 7 < w256 * 8;
@@ -941,8 +979,8 @@ template <int EPI>
 static hipError_t launch_v224(GemmParams p, hipStream_t s) {
   p.tiles_m = (p.M + 255) / 256;
   p.tiles_n = p.N / 224;
-  p.group_m = pick_group_m<256, 224>(p.tiles_m, p.tiles_n, 1);
-  hipLaunchKernelGGL(gemm_v224_kernel<EPI>, dim3(p.tiles_m * p.tiles_n), dim3(512), 0, s, p);
+  p.group_m = pick_group_m<256, 224>(p.tiles_m, p.tiles_n, p.ksplit);
+  hipLaunchKernelGGL(gemm_v224_kernel<EPI>, dim3(p.tiles_m * p.tiles_n, p.ksplit), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1373,15 +1411,17 @@ GemmPlan gemm_plan_small(int M, int N, int K, bool fp32_out, int max_split) {
   GemmPlan best{GEMM_CFG_128x128, 1, K};
   double best_t = 1e30;
   const int kb = (K + 63) / 64;
-  for (int cfg : {GEMM_CFG_256x256, GEMM_CFG_128x128}) {
-    const int b = cfg == GEMM_CFG_256x256 ? 256 : 128;
-    const long tiles = (long)((M + b - 1) / b) * ((N + b - 1) / b);
+  for (int cfg : {GEMM_CFG_256x256, GEMM_CFG_256x224, GEMM_CFG_128x128}) {
+    // 256 x 224 tiles (products 1792k wide) run at the 256 x 256 tile's per-CU rate
+    if (cfg == GEMM_CFG_256x224 && N % 1792 != 0) continue;
+    const int b = cfg == GEMM_CFG_128x128 ? 128 : 256, bn = cfg == GEMM_CFG_256x224 ? 224 : b;
+    const long tiles = (long)((M + b - 1) / b) * ((N + bn - 1) / bn);
     for (int S = 1; S <= max_split; ++S) {
       const int per = (kb + S - 1) / S;
       if (S > 1 && per < 8) break;  // keep >= 512 of K per split
       const int Sr = (kb + per - 1) / per;
       const long W = tiles * Sr;
-      const double fl = 2.0 * b * b * 64.0 * per;  // FLOPs of one tile
+      const double fl = 2.0 * b * bn * 64.0 * per;  // FLOPs of one tile
       double t;
       if (b == 256) t = (double)((W + 255) / 256) * (fl / 5.6e12 + 5e-6);
       else if (W <= 256) t = fl / 2.46e12 + 3e-6;
@@ -1424,6 +1464,11 @@ hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s) {
   if (p.kchunk <= 0) p.kchunk = p.K;
   if (cfg < 0 && v224_ok(p, epi))
     return epi == EPI_BF16 ? launch_v224<EPI_BF16>(p, s) : launch_v224<EPI_RESID>(p, s);
+  if (cfg == GEMM_CFG_256x224) {
+    if (!v224_shape_ok(p, epi)) return hipErrorInvalidValue;
+    if (epi == EPI_F32) return launch_v224<EPI_F32>(p, s);
+    return epi == EPI_BF16 ? launch_v224<EPI_BF16>(p, s) : launch_v224<EPI_RESID>(p, s);
+  }
   if (cfg < 0) cfg = gemm_pick_cfg(p.M, p.N, p.kchunk, p.batch * p.ksplit);
   switch (epi) {
     case EPI_F32: return launch_epi<EPI_F32>(p, cfg, s);

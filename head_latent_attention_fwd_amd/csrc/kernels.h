@@ -9,7 +9,8 @@ typedef uint16_t bf16_t;
 
 // ------------------------------------------------------------------ GEMM
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_RESID = 3, EPI_SWIGLU = 4 };
-enum { GEMM_CFG_AUTO = -1, GEMM_CFG_256x256 = 0, GEMM_CFG_128x128 = 1, GEMM_CFG_64x128 = 2 };
+enum { GEMM_CFG_AUTO = -1, GEMM_CFG_256x256 = 0, GEMM_CFG_128x128 = 1, GEMM_CFG_64x128 = 2,
+       GEMM_CFG_256x224 = 3 };  // 256x224: products 1792k columns wide (bf16, residual, fp32 K slices)
 
 struct GemmParams {
   const bf16_t* A;   // [M, K] row-major, leading dim lda

@@ -378,6 +378,9 @@ def test_ragged_decode_uniform_and_clamped(form):
     ("kimi_bf16_keysplit4", ref.KIMI_K2, 1, 200, 2000, 2200, "bf16", 116),
     ("kimi_bf16_keysplit2", ref.KIMI_K2, 1, 300, 1700, 2000, "bf16", 117),
     ("kimi_bf16_keysplit_one_token", ref.KIMI_K2, 2, 1, 4000, 4001, "bf16", 118),
+    # 512 rows: o_proj on 256 x 224 tiles in four fp32 K slices (256
+    # workgroups), summed by reduce_splits
+    ("kimi_bf16_T512", ref.KIMI_K2, 1, 512, 512, 1024, "bf16", 119),
 ])
 @pytest.mark.parametrize("form", ["full", "latent"])
 def test_prefill_chunk(case, form):
