@@ -369,17 +369,33 @@ __global__ __launch_bounds__(512) void flash_pp_kernel(FlashParams p) {
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (p.nsplit > 1) {
-    // split partial: unnormalised O^T columns and (m, l) of this query
-    if (qrow_l < p.T) {
+    // split partial: unnormalised O^T columns and (m, l) of this query.  The
+    // fp32 tile goes through the (now free) ring as 256 rows of 512 bytes,
+    // 16-byte chunk c of row r at c ^ (r & 31), and leaves as whole row
+    // records, 16 bytes per lane.
+    if (qrow_l < p.T && lg == 0) {
       const long rec = ((long)sp * p.B * p.T + rowbase + qrow_l) * HS + h;
-      float* op = p.opart + rec * 128 + 4 * lg;
+      *(floatx2*)(p.ostat + 2 * rec) = floatx2{m_run, l_tot};
+    }
+    __syncthreads();  // every wave's last key tile read
+    {
+      const int r = 32 * w + lr;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          *(floatx4*)(op + 32 * d + 8 * i) =
+          *(floatx4*)(lds + r * 512 + 16 * ((8 * d + 2 * i + lg) ^ (r & 31))) =
               floatx4{O[d][4 * i + 0], O[d][4 * i + 1], O[d][4 * i + 2], O[d][4 * i + 3]};
-      if (lg == 0) *(floatx2*)(p.ostat + 2 * rec) = floatx2{m_run, l_tot};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < PP_BQ * 32 / 512; ++it) {
+      const int idx = tid + 512 * it, r = idx >> 5, c = idx & 31;
+      const floatx4 v = *(const floatx4*)(lds + r * 512 + 16 * (c ^ (r & 31)));
+      if (q0 + r < p.T) {
+        const long rec = ((long)sp * p.B * p.T + rowbase + q0 + r) * HS + h;
+        *(floatx4*)(p.opart + rec * 128 + 4 * c) = v;
+      }
     }
     return;
   }
