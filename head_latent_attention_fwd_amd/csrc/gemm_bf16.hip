@@ -1465,9 +1465,13 @@ hipError_t gemm_bf16(GemmParams p, int epi, int cfg, hipStream_t s) {
   if (cfg < 0 && v224_ok(p, epi))
     return epi == EPI_BF16 ? launch_v224<EPI_BF16>(p, s) : launch_v224<EPI_RESID>(p, s);
   if (cfg == GEMM_CFG_256x224) {
-    if (!v224_shape_ok(p, epi)) return hipErrorInvalidValue;
-    if (epi == EPI_F32) return launch_v224<EPI_F32>(p, s);
-    return epi == EPI_BF16 ? launch_v224<EPI_BF16>(p, s) : launch_v224<EPI_RESID>(p, s);
+    // the plan's 256 x 224 choice; a product outside its shape takes the 256 x 256 tile
+    if (v224_shape_ok(p, epi)) {
+      if (epi == EPI_F32) return launch_v224<EPI_F32>(p, s);
+      if (epi == EPI_BF16 || epi == EPI_RESID)
+        return epi == EPI_BF16 ? launch_v224<EPI_BF16>(p, s) : launch_v224<EPI_RESID>(p, s);
+    }
+    cfg = GEMM_CFG_256x256;
   }
   if (cfg < 0) cfg = gemm_pick_cfg(p.M, p.N, p.kchunk, p.batch * p.ksplit);
   switch (epi) {
