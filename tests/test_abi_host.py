@@ -101,7 +101,8 @@ def test_null_pointers_rejected():
 def test_bad_shapes_rejected():
     L = _lib()
     d = tiny()
-    assert _prefill(L, d, B=0) == -2
+    assert _prefill(L, d, B=0) == -2              # empty inputs are refused, not a silent no-op
+    assert _prefill(L, d, T=0) == -2
     assert _prefill(L, d, T=-3) == -2
     assert _prefill(L, d, rows=15) == -2          # rope table shorter than T
     assert _prefill(L, d, kc=FAKE, vc=FAKE, L_cap=8) == -2   # cache smaller than T

@@ -45,6 +45,9 @@ def _rope(od, n):
     ("kimi_narrow_bf16", KIMI_NARROW, 2, 200, "bf16", 11),
     ("kimi_bf16_T130", ref.KIMI_K2, 1, 130, "bf16", 12),
     ("kimi_bf16_T20_small_rows", ref.KIMI_K2, 2, 20, "bf16", 13),
+    # a one-token prompt per sequence: every product has 3 rows, and the
+    # attention is one key per query
+    ("kimi_bf16_T1", ref.KIMI_K2, 3, 1, "bf16", 14),
 ])
 def test_prefill(case):
     name, od, B, T, dt, seed = case
