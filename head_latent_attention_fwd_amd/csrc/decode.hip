@@ -570,10 +570,25 @@ __global__ __launch_bounds__(256) void decode_latent_kernel(DecodeLatentParams p
   // the W_UV product)
   const long rec = (long)v * p.H + head;
   if (g4 == 0) *(floatx2*)(p.stats + 2 * rec) = floatx2{m_run, l_tot};
-  bf16_t* op = p.opart + rec * 512 + 4 * g4;
+  // o~ goes through the (drained) ring as 64 records of 1 KB, 16-byte chunk
+  // c of record r at c ^ (r & 63) (a lane's own values are 8-byte pieces of
+  // 16 records per store), and leaves as whole records, 16 bytes per lane
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every wave's last tile read
 #pragma unroll
-  for (int i = 0; i < 32; ++i)
-    *(u32x2*)(op + 16 * i) = u32x2{pack2bf(O[i][0], O[i][1]), pack2bf(O[i][2], O[i][3])};
+  for (int i = 0; i < 32; ++i) {
+    // features 16 i + 4 g4 .. + 3: chunk 2 i + (g4 >> 1), half g4 & 1
+    const int c = 2 * i + (g4 >> 1);
+    *(u32x2*)(lds + head * 1024 + 16 * (c ^ (head & 63)) + 8 * (g4 & 1)) =
+        u32x2{pack2bf(O[i][0], O[i][1]), pack2bf(O[i][2], O[i][3])};
+  }
+  __syncthreads();
+  bf16_t* ob = p.opart + (long)v * p.H * 512;
+#pragma unroll
+  for (int it = 0; it < 64 * 64 / 256; ++it) {
+    const int idx = tid + 256 * it, r = idx >> 6, c = idx & 63;
+    *(u32x4*)(ob + (long)r * 512 + 8 * c) = *(const u32x4*)(lds + r * 1024 + 16 * (c ^ (r & 63)));
+  }
 }
 
 // Merge of the split partials fused with the value up-projection: one
