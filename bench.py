@@ -110,6 +110,46 @@ def decode_traffic(form):
     return int(m.group(1))
 
 
+def achievable(torch, mla, dev, flush_buf):
+    """Second denominators measured on this machine in the same run: the HBM read
+    rate of the library's streaming-read yardstick over 1 GiB (four times the
+    256 MB Infinity Cache; 16-byte loads, sixteen in flight per thread) and the
+    bf16 dense rate of the vendor GEMM (hipBLASLt through torch.matmul) on an
+    8192^3 product, each after the same clock warm-up as the workloads.  For
+    reference, torch's own 1 GiB sum is timed too."""
+    st = torch.cuda.current_stream()
+
+    def rate(fn, reps):
+        warm(torch, fn, 3)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    nbytes = flush_buf.numel() * flush_buf.element_size()
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    t_rd = rate(lambda: mla.mla_read_sweep(flush_buf, sink), 20)
+    t_sum = rate(lambda: flush_buf.sum(), 20)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    n = 8192
+    a = torch.randn(n, n, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn(n, n, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    t_mm = rate(lambda: torch.matmul(a, b, out=c), 20)
+    del a, b, c
+    return {"hbm_read_gbs": nbytes / t_rd / 1e9,
+            "mfma_bf16_tflops": 2.0 * n ** 3 / t_mm / 1e12,
+            "torch_sum_read_gbs": nbytes / t_sum / 1e9,
+            "method": "HBM: mla_read_sweep over 1 GiB on the device (16-byte loads, 4096 workgroups), "
+                      "20 reps; MFMA: hipBLASLt bf16 8192 x 8192 x 8192 product via torch.matmul, "
+                      "20 reps; both after >= 0.25 s of warm-up, timed with HIP events"}
+
+
 def make_weights(torch, dev, k, seed):
     """Synthetic N(0, 0.02^2) weights with unit gains, drawn on the device."""
     import head_latent_attention_fwd_amd as mla
@@ -545,6 +585,21 @@ def main():
                 sec[name] = {"error": repr(e)}
             torch.cuda.empty_cache()
         line["secondary"] = sec
+    log("[bench] achievable rates (vendor yardsticks)")
+    ach = achievable(torch, mla, dev, flush_buf)
+    line["achievable"] = ach
+    roofline["frac_of_achievable"] = roofline["achieved"] / ach["mfma_bf16_tflops"]
+    line["mfma_frac_step_of_achievable"] = value / ach["mfma_bf16_tflops"]
+    for name, v in line.get("secondary", {}).items():
+        if not isinstance(v, dict):
+            continue
+        if "hbm_gbs" in v:
+            v["hbm_frac_of_achievable"] = v["hbm_gbs"] / ach["hbm_read_gbs"]
+        if "tflops" in v:
+            v["mfma_frac_of_achievable"] = v["tflops"] / ach["mfma_bf16_tflops"]
+        for pt in v.get("points", []):
+            if "hbm_gbs" in pt:
+                pt["hbm_frac_of_achievable"] = pt["hbm_gbs"] / ach["hbm_read_gbs"]
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle, float32)")
         line["cpu_baseline"] = cpu_baseline()

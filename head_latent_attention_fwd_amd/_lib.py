@@ -95,6 +95,8 @@ def load():
     L.dense_block_workspace_size.restype = _SZ
     L.dense_block_fwd.argtypes = [_DP, ctypes.POINTER(BlockWeights), _P, _I, _I, _P, _P, _I, _P, _P,
                                   _SZ, _P]
+    L.mla_read_sweep.argtypes = [_P, _SZ, _P, _P]
+    L.mla_read_sweep.restype = _I
     L.mla_profile_enable.argtypes = [_I]
     L.mla_profile_enable.restype = _I
     L.mla_profile_summary.argtypes = [ctypes.c_char_p, _SZ, ctypes.POINTER(_I)]
@@ -215,6 +217,21 @@ def mla_rope_table(n_pos, d_rope, base=10000.0, device="cuda"):
     _check(L.mla_rope_table(n_pos, d_rope, float(base), ctypes.c_void_p(cos.data_ptr()),
                             ctypes.c_void_p(sin.data_ptr()), _stream(device)))
     return cos, sin
+
+
+def mla_read_sweep(buf, sink=None):
+    """Read every byte of the device tensor buf once (the HBM read-rate
+    yardstick); returns the sink tensor (4096 int32 words whose XOR is the
+    XOR of every word read; allocated when not given)."""
+    L = load()
+    dev = buf.device
+    if not buf.is_contiguous():
+        raise MLAError(-2, "buf must be contiguous")
+    if sink is None:
+        sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    _check(L.mla_read_sweep(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                            ctypes.c_void_p(sink.data_ptr()), _stream(dev)))
+    return sink
 
 
 def prefill_workspace_size(d: Dims, B, T):

@@ -137,6 +137,10 @@ hipError_t rope_inplace_f32(float* x, long ldx, int M, int ncols, int head_dim, 
                             int rope_pos0, hipStream_t s, const int* seq_pos = nullptr,
                             int pos_max = 0);
 hipError_t swiglu_f32(const float* g, const float* u, float* h, long n, hipStream_t s);
+// streaming-read yardstick: reads bytes / 16 chunks of buf, one word per
+// workgroup into sink [nwg]
+constexpr int kReadSweepWG = 4096;
+hipError_t read_sweep(const void* buf, size_t bytes, unsigned* sink, int nwg, hipStream_t s);
 
 // Scatter the per-head keys/values of new tokens into the full cache.
 // kv [M][H][d_nope + d_v] (row m = b * T + t), kr [M][d_rope]; slot t + pos0,

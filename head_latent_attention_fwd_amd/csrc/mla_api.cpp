@@ -818,6 +818,16 @@ int mla_rope_table(int n_pos, int d_rope, double base, float* cos_out, float* si
   return MLA_OK;
 }
 
+int mla_read_sweep(const void* buf, size_t bytes, unsigned* sink, void* stream) {
+  g_err[0] = 0;
+  if (!buf || !sink) return fail(MLA_ERR_NULL, "buffer or sink is NULL");
+  if (int r = check_align({buf, sink}, "buffer / sink")) return r;
+  if (bytes == 0 || bytes % 16) return fail(MLA_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  hipStream_t st = (hipStream_t)stream;
+  LAUNCH("read_sweep", read_sweep(buf, bytes, sink, kReadSweepWG, st));
+  return MLA_OK;
+}
+
 size_t mla_prefill_workspace_size(const mla_dims* d, int B, int T) {
   if (check_dims(d, false) || B <= 0 || T <= 0) return 0;
   PrefillPlan pl;

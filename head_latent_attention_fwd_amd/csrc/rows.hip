@@ -425,4 +425,42 @@ template hipError_t reduce_splits<float>(const float*, int, long, int, int, floa
 template hipError_t reduce_splits<bf16_t>(const float*, int, long, int, int, bf16_t*, long,
                                           hipStream_t, const bf16_t*);
 
+// ---------------------------------------------------------------------------
+// Streaming-read yardstick: workgroup g reads the g-th of gridDim.x equal
+// contiguous ranges of a buffer in 16-byte chunks, sixteen loads in flight per
+// thread, and folds the values with XOR so the loads stay live; one word per
+// workgroup goes to `sink`.  It measures the HBM read rate this chip reaches
+// with plain vector loads, the second denominator next to the nominal 8 TB/s.
+// (A probe of the forms: contiguous ranges with 16 loads in flight read 1 GiB
+// at 6.2-6.3 TB/s from 2048 workgroups up; grid-stride loops over the whole
+// buffer reached 4.8-6.2 TB/s.)
+__global__ __launch_bounds__(256) void read_sweep_kernel(const u32x4* __restrict__ p, long n16,
+                                                         unsigned* __restrict__ sink) {
+  constexpr int U = 16;
+  const long per = (n16 + gridDim.x - 1) / gridDim.x;
+  const long b0 = (long)blockIdx.x * per, b1 = min(b0 + per, n16);
+  long i = b0 + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + (U - 1) * 256 < b1; i += U * 256) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = p[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
+  }
+  for (; i < b1; i += 256) acc ^= p[i];
+  const unsigned x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  __shared__ unsigned red[4];
+  const unsigned w = __reduce_xor_sync(~0ull, x);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+hipError_t read_sweep(const void* buf, size_t bytes, unsigned* sink, int nwg, hipStream_t s) {
+  hipLaunchKernelGGL(read_sweep_kernel, dim3(nwg), dim3(256), 0, s, (const u32x4*)buf, (long)(bytes / 16),
+                     sink);
+  return hipGetLastError();
+}
+
 }  // namespace mla

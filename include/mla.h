@@ -268,6 +268,18 @@ int dense_block_fwd(const mla_dims *dims, const mla_block_weights *w, const void
 int mla_profile_enable(int on);
 int mla_profile_summary(char *buf, size_t len, int *n_entries);
 
+/* ---- Measurement yardstick (not a step of the forward pass) ----
+ * Reads every byte of buf once with 16-byte vector loads (4096 workgroups,
+ * each a contiguous range, sixteen loads in flight per thread) so that the
+ * caller can time the HBM read rate this chip reaches: the achievable
+ * denominator next to the nominal 8 TB/s for the decode kernels' bandwidth.
+ * buf: device, bytes a multiple of 16 (a buffer much larger than the 256 MB
+ * Infinity Cache measures HBM); sink: device, 4096 unsigned ints whose XOR
+ * is the XOR of every 32-bit word read.
+ * MLA_ERR_NULL / MLA_ERR_SHAPE / MLA_ERR_UNSUPPORTED (alignment) on bad
+ * arguments; nothing is written to buf. */
+int mla_read_sweep(const void *buf, size_t bytes, unsigned *sink, void *stream);
+
 /* Static description of a status code, and the calling thread's last error
  * message (empty after a successful call). */
 const char *mla_status_string(int status);

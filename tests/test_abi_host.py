@@ -243,3 +243,15 @@ def test_misaligned_pointers_are_rejected():
     st = L.mla_decode_fullcache(ctypes.byref(d), ctypes.byref(w), FAKE, 2, 10, 16, FAKE, FAKE,
                                 FAKE, FAKE, 64, FAKE, odd, 1 << 40, None)
     assert st == -3
+
+
+def test_read_sweep_arguments_rejected():
+    """The measurement yardstick validates its arguments like the compute
+    calls: NULL pointers, sizes that are not a positive multiple of 16 bytes
+    and misaligned pointers are refused before any HIP call."""
+    L = _lib()
+    assert L.mla_read_sweep(None, 1024, FAKE, None) == -1
+    assert L.mla_read_sweep(FAKE, 1024, None, None) == -1
+    assert L.mla_read_sweep(FAKE, 0, FAKE, None) == -2
+    assert L.mla_read_sweep(FAKE, 1000, FAKE, None) == -2
+    assert L.mla_read_sweep(ctypes.c_void_p(0x1008), 1024, FAKE, None) == -3
