@@ -21,6 +21,12 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 # Kimi K2 widths with smaller model/latent widths, for fast oracle runs that
 # still exercise the bf16 kernels' fixed head shapes.
+# Widths that are multiples of 64 but not of 128 (d_model 960, query latent
+# 192): the decode projections with K = 960 or K = 192, and the joint
+# down-projection split at 192, leave the 128-k weight stream for the K-sliced
+# register-streamed kernel; the 960-wide outputs end in a partial tile.
+KIMI_ODD = ref.MLADims(d_model=960, n_heads=64, q_lora_rank=192, kv_lora_rank=512,
+                       qk_nope_dim=128, qk_rope_dim=64, v_head_dim=128, d_ff=1536)
 KIMI_NARROW = ref.MLADims(d_model=1024, n_heads=64, q_lora_rank=256, kv_lora_rank=512,
                           qk_nope_dim=128, qk_rope_dim=64, v_head_dim=128, d_ff=1536)
 
@@ -43,6 +49,7 @@ def _rope(od, n):
     ("tiny_config", ref.TINY, 1, 16, "f32", 1001),
     ("tiny_ragged", ref.TINY, 2, 37, "f32", 7),
     ("kimi_narrow_bf16", KIMI_NARROW, 2, 200, "bf16", 11),
+    ("odd_widths_bf16", KIMI_ODD, 1, 100, "bf16", 15),
     ("kimi_bf16_T130", ref.KIMI_K2, 1, 130, "bf16", 12),
     ("kimi_bf16_T20_small_rows", ref.KIMI_K2, 2, 20, "bf16", 13),
     # a one-token prompt per sequence: every product has 3 rows, and the
@@ -188,6 +195,7 @@ def _decode_full_case(od, B, P, L_cap, dt, seed, sample=None):
     ("tiny_f32", ref.TINY, 3, 20, 24, "f32", 51),
     ("tiny_f32_P0", ref.TINY, 2, 0, 4, "f32", 52),
     ("kimi_narrow_bf16", KIMI_NARROW, 3, 300, 320, "bf16", 53),
+    ("odd_widths_bf16", KIMI_ODD, 3, 150, 160, "bf16", 55),
     ("kimi_bf16_long", ref.KIMI_K2, 2, 5000, 5001, "bf16", 54),
 ])
 def test_decode_fullcache(case):
@@ -229,6 +237,7 @@ def _decode_latent_case(od, B, P, L_cap, dt, seed, sample=None):
     ("tiny_f32", ref.TINY, 3, 20, 24, "f32", 61),
     ("tiny_f32_P0", ref.TINY, 2, 0, 3, "f32", 62),
     ("kimi_narrow_bf16", KIMI_NARROW, 3, 700, 701, "bf16", 63),
+    ("odd_widths_bf16", KIMI_ODD, 4, 260, 300, "bf16", 65),
     ("kimi_bf16_ragged", ref.KIMI_K2, 5, 333, 400, "bf16", 64),
 ])
 def test_decode_latentcache(case):
