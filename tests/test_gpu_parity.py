@@ -27,6 +27,10 @@ DEV = "cuda:0"
 # register-streamed kernel; the 960-wide outputs end in a partial tile.
 KIMI_ODD = ref.MLADims(d_model=960, n_heads=64, q_lora_rank=192, kv_lora_rank=512,
                        qk_nope_dim=128, qk_rope_dim=64, v_head_dim=128, d_ff=1536)
+# the same with a 576-wide query latent: its decode up-projection takes two
+# 512-wide K slices whose fp32 partials a separate launch sums into bf16
+KIMI_ODD576 = ref.MLADims(d_model=960, n_heads=64, q_lora_rank=576, kv_lora_rank=512,
+                          qk_nope_dim=128, qk_rope_dim=64, v_head_dim=128, d_ff=1536)
 KIMI_NARROW = ref.MLADims(d_model=1024, n_heads=64, q_lora_rank=256, kv_lora_rank=512,
                           qk_nope_dim=128, qk_rope_dim=64, v_head_dim=128, d_ff=1536)
 
@@ -196,6 +200,7 @@ def _decode_full_case(od, B, P, L_cap, dt, seed, sample=None):
     ("tiny_f32_P0", ref.TINY, 2, 0, 4, "f32", 52),
     ("kimi_narrow_bf16", KIMI_NARROW, 3, 300, 320, "bf16", 53),
     ("odd_widths_bf16", KIMI_ODD, 3, 150, 160, "bf16", 55),
+    ("odd_widths_q576_bf16", KIMI_ODD576, 2, 90, 96, "bf16", 56),
     ("kimi_bf16_long", ref.KIMI_K2, 2, 5000, 5001, "bf16", 54),
 ])
 def test_decode_fullcache(case):
@@ -238,6 +243,7 @@ def _decode_latent_case(od, B, P, L_cap, dt, seed, sample=None):
     ("tiny_f32_P0", ref.TINY, 2, 0, 3, "f32", 62),
     ("kimi_narrow_bf16", KIMI_NARROW, 3, 700, 701, "bf16", 63),
     ("odd_widths_bf16", KIMI_ODD, 4, 260, 300, "bf16", 65),
+    ("odd_widths_q576_bf16", KIMI_ODD576, 3, 130, 140, "bf16", 66),
     ("kimi_bf16_ragged", ref.KIMI_K2, 5, 333, 400, "bf16", 64),
 ])
 def test_decode_latentcache(case):
