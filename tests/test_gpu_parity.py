@@ -271,6 +271,7 @@ def _pos_dev(positions):
 @pytest.mark.parametrize("case", [
     ("tiny_f32", ref.TINY, [0, 3, 20, 9], 24, "f32", 71),
     ("kimi_narrow_bf16", KIMI_NARROW, [0, 1, 300, 127, 319], 320, "bf16", 72),
+    ("odd_widths_bf16", KIMI_ODD, [3, 0, 150, 77], 160, "bf16", 74),
     ("kimi_bf16_splits", ref.KIMI_K2, [0, 4999, 2500], 5001, "bf16", 73),
 ])
 def test_decode_fullcache_ragged(case):
@@ -302,6 +303,7 @@ def test_decode_fullcache_ragged(case):
 @pytest.mark.parametrize("case", [
     ("tiny_f32", ref.TINY, [5, 0, 20], 24, "f32", 81),
     ("kimi_narrow_bf16", KIMI_NARROW, [0, 700, 31, 32], 701, "bf16", 82),
+    ("odd_widths_bf16", KIMI_ODD, [0, 259, 64, 129], 300, "bf16", 85),
     ("kimi_bf16_splits", ref.KIMI_K2, [8192, 5, 4000], 8193, "bf16", 83),
     # 40 sequences, most of them a few tiles long and one of 94 tiles: the
     # split plan gives the long one many workgroups and leaves some idle;
@@ -388,6 +390,7 @@ def test_ragged_decode_uniform_and_clamped(form):
 @pytest.mark.parametrize("case", [
     ("tiny_f32", ref.TINY, 2, 5, 9, 16, "f32", 111),
     ("kimi_narrow_bf16", KIMI_NARROW, 2, 100, 150, 300, "bf16", 112),
+    ("odd_widths_bf16", KIMI_ODD, 1, 120, 170, 300, "bf16", 120),
     ("kimi_bf16", ref.KIMI_K2, 1, 300, 700, 1024, "bf16", 113),
     ("kimi_bf16_P0_0", ref.KIMI_K2, 1, 130, 0, 200, "bf16", 114),
     ("kimi_bf16_one_token", ref.KIMI_K2, 2, 1, 777, 800, "bf16", 115),
@@ -442,6 +445,7 @@ def _with_biases(w, od, seed, bf16):
 @pytest.mark.parametrize("case", [
     ("tiny_f32", ref.TINY, 2, 37, "f32", 101),
     ("kimi_narrow_bf16", KIMI_NARROW, 2, 200, "bf16", 102),
+    ("odd_widths_bf16", KIMI_ODD, 1, 90, "bf16", 104),
     ("kimi_bf16_T130", ref.KIMI_K2, 1, 130, "bf16", 103),
 ])
 def test_prefill_attention_bias(case):
@@ -752,6 +756,7 @@ def test_prefill_last_row_equals_decode(dt):
 @pytest.mark.parametrize("case", [
     ("tiny_f32", ref.TINY, 2, 19, "f32", 91),
     ("kimi_narrow_bf16", KIMI_NARROW, 1, 150, "bf16", 92),
+    ("odd_widths_bf16", KIMI_ODD, 1, 140, "bf16", 93),
 ])
 def test_dense_block(case):
     name, od, B, T, dt, seed = case
