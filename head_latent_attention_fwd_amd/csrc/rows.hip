@@ -76,7 +76,7 @@ MLA_DEV float down_bias(const LatentNormParams<T>& p, int c) {
 // norm, y = 1 the kv latent, its norm and the rotary key.
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T> p) {
-  extern __shared__ float row[];  // [q_lora + kv_lora + d_rope]
+  extern __shared__ __attribute__((aligned(16))) float row[];  // [q_lora + kv_lora + d_rope]
   __shared__ float red[NT / 64];
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
@@ -122,10 +122,25 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
       else if (c < p.q_lora + p.kv_lora) skv += v * v;
     }
   }
+  // bf16 outputs four columns at a time (8-byte gain loads and stores, one
+  // 16-byte LDS read) when the widths and leading dimensions allow it
+  constexpr bool BF = sizeof(T) == 2;
+  const bool v4 = BF && p.q_lora % 4 == 0 && p.kv_lora % 4 == 0 && p.ld_cq % 4 == 0 && p.ld_ckv % 4 == 0 &&
+                  (p.kv_lora + p.d_rope) % 4 == 0;
   if (do_q) {
     const float rq = 1.0f / sqrtf(block_sum<NT>(sq, red) / (float)p.q_lora + p.eps);
-    for (int c = tid; c < p.q_lora; c += NT)
-      p.cq[(long)m * p.ld_cq + c] = from_f<T>(to_f<T>(p.g_q[c]) * (row[c] * rq));
+    if (v4) {
+      for (int c4 = tid; c4 < p.q_lora / 4; c4 += NT) {
+        const u32x2 g = *(const u32x2*)(p.g_q + 4 * c4);
+        const floatx4 x = *(const floatx4*)(row + 4 * c4);
+        *(u32x2*)(p.cq + (long)m * p.ld_cq + 4 * c4) =
+            u32x2{pack2bf(lo_bf(g[0]) * (x[0] * rq), hi_bf(g[0]) * (x[1] * rq)),
+                  pack2bf(lo_bf(g[1]) * (x[2] * rq), hi_bf(g[1]) * (x[3] * rq))};
+      }
+    } else {
+      for (int c = tid; c < p.q_lora; c += NT)
+        p.cq[(long)m * p.ld_cq + c] = from_f<T>(to_f<T>(p.g_q[c]) * (row[c] * rq));
+    }
   }
   if (!do_kv) return;
   const float rkv = 1.0f / sqrtf(block_sum<NT>(skv, red) / (float)p.kv_lora + p.eps);
@@ -137,10 +152,21 @@ __global__ __launch_bounds__(NT) void latent_norm_rope_kernel(LatentNormParams<T
                ? p.latent_cache + ((long)bseq * p.L_cap + pos) * (p.kv_lora + p.d_rope)
                : nullptr;
 
-  for (int c = tid; c < p.kv_lora; c += NT) {
-    T y = from_f<T>(to_f<T>(p.g_kv[c]) * (row[p.q_lora + c] * rkv));
-    p.ckv[(long)m * p.ld_ckv + c] = y;
-    if (lat) lat[c] = y;
+  if (v4) {
+    for (int c4 = tid; c4 < p.kv_lora / 4; c4 += NT) {
+      const u32x2 g = *(const u32x2*)(p.g_kv + 4 * c4);
+      const floatx4 x = *(const floatx4*)(row + p.q_lora + 4 * c4);
+      const u32x2 y = {pack2bf(lo_bf(g[0]) * (x[0] * rkv), hi_bf(g[0]) * (x[1] * rkv)),
+                       pack2bf(lo_bf(g[1]) * (x[2] * rkv), hi_bf(g[1]) * (x[3] * rkv))};
+      *(u32x2*)(p.ckv + (long)m * p.ld_ckv + 4 * c4) = y;
+      if (lat) *(u32x2*)(lat + 4 * c4) = y;
+    }
+  } else {
+    for (int c = tid; c < p.kv_lora; c += NT) {
+      T y = from_f<T>(to_f<T>(p.g_kv[c]) * (row[p.q_lora + c] * rkv));
+      p.ckv[(long)m * p.ld_ckv + c] = y;
+      if (lat) lat[c] = y;
+    }
   }
   const int npairs = p.d_rope / 2;
   const float* kp = row + p.q_lora + p.kv_lora;
