@@ -189,9 +189,10 @@ def warm(torch, fn, warmup, min_s=WARM_S):
     torch.cuda.synchronize()
 
 
-def timed(torch, fn, steps, warmup, flush=None):
+def timed(torch, fn, steps, warmup, flush=None, samples=None):
     """Warm up, then time `steps` calls with HIP events on the current stream
-    (per-step events when a cache flush runs between steps)."""
+    (per-step events when a cache flush runs between steps; their times are
+    appended to `samples` when a list is given)."""
     if warmup > 0:
         warm(torch, fn, warmup)
     torch.cuda.synchronize()
@@ -217,16 +218,20 @@ def timed(torch, fn, steps, warmup, flush=None):
         fn()
         b.record(st)
         torch.cuda.synchronize()
-        tot += a.elapsed_time(b)
+        e = a.elapsed_time(b)
+        tot += e
+        if samples is not None:
+            samples.append(e)
     return tot / steps, time.perf_counter() - t0
 
 
-def timed_profiled(torch, mla, fn, steps, flush=None):
+def timed_profiled(torch, mla, fn, steps, flush=None, samples=None):
     """Time `steps` steps as they run (no per-kernel events), then time them
     again with the library's per-launch HIP events on the launch stream for
     the kernel table.  Returns (ms_per_step, wall_s, kernel_table,
-    ms_per_step_with_events)."""
-    ms, wall = timed(torch, fn, steps, 0, flush)
+    ms_per_step_with_events); with a flush, the first pass's per-step times
+    go to `samples`."""
+    ms, wall = timed(torch, fn, steps, 0, flush, samples)
     mla.mla_profile_summary()                  # drop anything recorded so far
     mla.mla_profile_enable(True)
     ms_ev, _ = timed(torch, fn, steps, 0, flush)
@@ -279,6 +284,21 @@ def bench_prefill_bias(torch, mla, dev, d, w, steps, warmup, k=KIMI, B=1, T=2048
             "tflops": flops / (ms * 1e-3) / 1e12, "kernels": kern}
 
 
+def decode_extras(torch, fn, steps, samples, B):
+    """Per-step statistics of the flushed steps, and the same step timed back
+    to back with the Infinity Cache left as the previous step leaves it
+    (labelled un-flushed: weights and part of the cache may hit in it)."""
+    ex = {}
+    if samples:
+        v = sorted(samples)
+        ex["ms_per_step_median"] = v[len(v) // 2]
+        ex["ms_per_step_min"] = v[0]
+    ms_warm, _ = timed(torch, fn, steps, 0)
+    ex["ms_per_step_unflushed"] = ms_warm
+    ex["tokens_per_s_unflushed"] = B / (ms_warm * 1e-3)
+    return ex
+
+
 def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000):
     k = KIMI
     L_cap = P + 1
@@ -293,7 +313,9 @@ def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000)
     ws = torch.empty(mla.decode_workspace_size(d, B, L_cap), dtype=torch.uint8, device=dev)
     fn = lambda: mla.mla_decode_fullcache(d, w, x, P, kc, vc, rope, out=out, workspace=ws)  # noqa: E731
     warm(torch, fn, warmup)
-    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush)
+    samples = []
+    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush, samples)
+    extras = decode_extras(torch, fn, steps, samples, B)
     L = P + 1
     cache_bytes = B * H * L * (192 + 128) * 2
     nbytes = cache_bytes + mla_param_count() * 2 + B * H * 320 * 2 + 2 * B * k["d_model"] * 2
@@ -306,7 +328,7 @@ def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000)
     return {"workload": f"MLA decode, full cache, bf16, B={B}, P={P} (L={L} keys)",
             "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev, "tokens_per_s": B / (ms * 1e-3),
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None}
+            "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None, **extras}
 
 
 def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=8192):
@@ -321,7 +343,9 @@ def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=819
     ws = torch.empty(mla.decode_workspace_size(d, B, L_cap), dtype=torch.uint8, device=dev)
     fn = lambda: mla.mla_decode_latentcache(d, w, x, P, cc, rope, out=out, workspace=ws)  # noqa: E731
     warm(torch, fn, warmup)
-    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush)
+    samples = []
+    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush, samples)
+    extras = decode_extras(torch, fn, steps, samples, B)
     L = P + 1
     cache_bytes = B * L * 576 * 2
     nbytes = cache_bytes + mla_param_count() * 2 + B * 576 * 2 + 2 * B * k["d_model"] * 2
@@ -333,7 +357,7 @@ def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=819
     return {"workload": f"MLA decode, absorbed latent cache, bf16, B={B}, P={P} (L={L} keys)",
             "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev, "tokens_per_s": B / (ms * 1e-3),
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None}
+            "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None, **extras}
 
 
 def bench_decode_latent_ragged(torch, mla, dev, d, w, steps, warmup, flush, B=32, P_max=8192):
@@ -354,7 +378,9 @@ def bench_decode_latent_ragged(torch, mla, dev, d, w, steps, warmup, flush, B=32
     ws = torch.empty(mla.decode_workspace_size(d, B, L_cap), dtype=torch.uint8, device=dev)
     fn = lambda: mla.mla_decode_latentcache_ragged(d, w, x, pos, P_max, cc, rope, out=out, workspace=ws)  # noqa: E731
     warm(torch, fn, warmup)
-    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush)
+    samples = []
+    ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush, samples)
+    extras = decode_extras(torch, fn, steps, samples, B)
     keys = int(pos_host.sum()) + B
     cache_bytes = keys * 576 * 2
     nbytes = cache_bytes + mla_param_count() * 2 + B * 576 * 2 + 2 * B * k["d_model"] * 2
@@ -364,7 +390,7 @@ def bench_decode_latent_ragged(torch, mla, dev, d, w, steps, warmup, flush, B=32
                         f"in [0, {P_max}] (mean {pos_host.mean():.0f}, {keys} keys in all)",
             "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev, "tokens_per_s": B / (ms * 1e-3),
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None}
+            "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None, **extras}
 
 
 SWEEP_P = (1000, 4096, 8192, 16384)
@@ -384,11 +410,13 @@ def bench_decode_sweep(torch, mla, dev, d, w, steps, warmup, flush):
                 kname = "decode_full" if form == "full" else "decode_latent"
                 rows.append({"form": form, "B": B, "P": P, "ms_per_step": r["ms_per_step"],
                              "tokens_per_s": r["tokens_per_s"], "hbm_gbs": r["hbm_gbs"],
-                             "hbm_frac": r["hbm_frac"],
+                             "hbm_frac": r["hbm_frac"], "ms_per_step_median": r.get("ms_per_step_median"),
+                             "ms_per_step_unflushed": r.get("ms_per_step_unflushed"),
                              "attention_kernel_gbs": r["kernels"].get(kname, {}).get("gbs")})
                 torch.cuda.empty_cache()
     return {"workload": "MLA decode step over P in " + str(list(SWEEP_P)) + ", B in " + str(list(SWEEP_B)) +
-                        ", both cache forms, bf16, Infinity Cache flushed before each step",
+                        ", both cache forms, bf16, Infinity Cache flushed before each step "
+                        "(ms_per_step_unflushed: the same step back to back)",
             "points": rows}
 
 
