@@ -239,6 +239,20 @@ def timed_profiled(torch, mla, fn, steps, flush=None, samples=None):
     return ms, wall, kernel_table(mla, steps), ms_ev
 
 
+def per_step_stats(torch, fn, steps):
+    """Median and minimum of `steps` steps, each bracketed by its own pair of
+    HIP events on the current stream (a pass of its own, after the timed one)."""
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    v = sorted(a.elapsed_time(b) for a, b in ev)
+    return v[len(v) // 2], v[0]
+
+
 def kernel_table(mla, steps):
     prof = mla.mla_profile_summary()
     return {n: {"launches": c, "avg_ms": ms / c} for n, (c, ms) in prof.items()}
@@ -253,13 +267,15 @@ def bench_prefill(torch, mla, dev, steps, warmup, k=KIMI, B=1, T=2048):
     fn = lambda: mla.mla_prefill(d, w, x, rope, out=out, workspace=ws)  # noqa: E731
     warm(torch, fn, warmup)
     ms, wall, kern, ms_ev = timed_profiled(torch, mla, fn, steps)
+    med, mn = per_step_stats(torch, fn, steps)
     flops = prefill_kernel_flops(B, T, k)
     for n, v in kern.items():
         if n in flops:
             v["gflop"] = flops[n] / 1e9
             v["tflops"] = flops[n] / (v["avg_ms"] * 1e-3) / 1e12
     total = sum(v for n, v in flops.items() if n != "gemm_qkv_up")
-    return {"ms": ms, "ms_with_kernel_events": ms_ev, "wall_s": wall, "flops": total, "kernels": kern, "w": w, "d": d}
+    return {"ms": ms, "ms_with_kernel_events": ms_ev, "ms_median": med, "ms_min": mn, "wall_s": wall,
+            "flops": total, "kernels": kern, "w": w, "d": d}
 
 
 def bench_prefill_bias(torch, mla, dev, d, w, steps, warmup, k=KIMI, B=1, T=2048):
@@ -594,6 +610,7 @@ def main():
         "mfma_frac_step": value / MFMA_BF16_PEAK_TFS,
         "roofline": roofline,
         "ms_per_step_with_kernel_events": r["ms_with_kernel_events"],
+        "ms_per_step_median": r["ms_median"], "ms_per_step_min": r["ms_min"],
         "kernels": kern,
     }
     if not args.no_secondary:
