@@ -89,19 +89,27 @@ def measured_traffic(kernel):
     return int(m.group(1))
 
 
+def decode_source_hash():
+    """First 16 hex digits of the SHA-256 of the decode attention kernels'
+    sources (decode.hip, then latent_body.h)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode.hip", "latent_body.h"):
+        h.update(open(os.path.join(ROOT, "head_latent_attention_fwd_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def decode_traffic(form):
     """HBM bytes per launch of the decode attention kernel (read + write)
     from the committed rocprofv3 counter summary of that workload, or None
-    when decode.hip changed since the counters were taken."""
-    import hashlib
+    when the decode kernels' sources changed since the counters were taken."""
     import re
     name = {"full": "decode_fullcache_B64_P1000_hbm_traffic.md",
             "latent": "decode_latentcache_B32_P8192_hbm_traffic.md"}[form]
     kern = {"full": "decode_full", "latent": "decode_latent"}[form]
-    src = os.path.join(ROOT, "head_latent_attention_fwd_amd", "csrc", "decode.hip")
     try:
         text = open(os.path.join(ROOT, "profiles", name)).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = decode_source_hash()
     except OSError:
         return None
     m = re.search(rf"{kern} traffic_bytes_per_launch=(\d+) decode_source_sha256_16=([0-9a-f]+)", text)
@@ -347,7 +355,9 @@ def bench_decode_full(torch, mla, dev, d, w, steps, warmup, flush, B=64, P=1000)
             "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None, **extras}
 
 
-def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=8192):
+def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=8192, persistent=False):
+    """Latent-cache decode step; persistent=True times the same step run as
+    one cooperative kernel (mla_decode_latentcache_persistent)."""
     k = KIMI
     L_cap = P + 1
     g = torch.Generator(device=dev)
@@ -357,7 +367,8 @@ def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=819
     rope = mla.mla_rope_table(L_cap, 64, 10000.0, dev)
     out = torch.empty_like(x)
     ws = torch.empty(mla.decode_workspace_size(d, B, L_cap), dtype=torch.uint8, device=dev)
-    fn = lambda: mla.mla_decode_latentcache(d, w, x, P, cc, rope, out=out, workspace=ws)  # noqa: E731
+    step = mla.mla_decode_latentcache_persistent if persistent else mla.mla_decode_latentcache
+    fn = lambda: step(d, w, x, P, cc, rope, out=out, workspace=ws)  # noqa: E731
     warm(torch, fn, warmup)
     samples = []
     ms, _, kern, ms_ev = timed_profiled(torch, mla, fn, steps, flush, samples)
@@ -370,7 +381,8 @@ def bench_decode_latent(torch, mla, dev, d, w, steps, warmup, flush, B=32, P=819
         kern["decode_latent"]["algorithmic_bytes"] = cache_bytes
         if (B, P) == (32, 8192):
             kern["decode_latent"]["traffic"] = decode_traffic("latent")
-    return {"workload": f"MLA decode, absorbed latent cache, bf16, B={B}, P={P} (L={L} keys)",
+    form = ", one persistent cooperative kernel" if persistent else ""
+    return {"workload": f"MLA decode, absorbed latent cache, bf16, B={B}, P={P} (L={L} keys){form}",
             "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_ev, "tokens_per_s": B / (ms * 1e-3),
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": nbytes, "kernels": kern, "mall_flushed": flush is not None, **extras}
@@ -537,7 +549,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode_full", "decode_latent", "decode_latent_ragged",
+    ap.add_argument("--only", choices=["prefill", "decode_full", "decode_latent", "decode_latent_persistent",
+                                       "decode_latent_ragged",
                                        "prefill_bias", "chunk_full", "chunk_latent", "block", "decode_sweep",
                                        "copy"])
     args = ap.parse_args()
@@ -576,6 +589,8 @@ def main():
         d, w, _ = make_weights(torch, dev, KIMI, 1002)
         fn = {"decode_full": lambda: bench_decode_full(torch, mla, dev, d, w, args.steps, args.warmup, flush),
               "decode_latent": lambda: bench_decode_latent(torch, mla, dev, d, w, args.steps, args.warmup, flush),
+              "decode_latent_persistent": lambda: bench_decode_latent(torch, mla, dev, d, w, args.steps, args.warmup,
+                                                                      flush, persistent=True),
               "decode_latent_ragged": lambda: bench_decode_latent_ragged(torch, mla, dev, d, w, args.steps,
                                                                          args.warmup, flush),
               "prefill_bias": lambda: bench_prefill_bias(torch, mla, dev, d, w, args.steps, args.warmup),
@@ -617,6 +632,7 @@ def main():
         sec = {}
         for name, fn in (("decode_fullcache", lambda: bench_decode_full(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
                          ("decode_latentcache", lambda: bench_decode_latent(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
+                         ("decode_latentcache_persistent", lambda: bench_decode_latent(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush, persistent=True)),
                          ("decode_latentcache_ragged", lambda: bench_decode_latent_ragged(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, flush)),
                          ("prefill_attention_bias", lambda: bench_prefill_bias(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3)),
                          ("prefill_chunk_fullcache", lambda: bench_prefill_chunk(torch, mla, dev, r["d"], r["w"], max(5, args.steps // 2), 3, "full")),

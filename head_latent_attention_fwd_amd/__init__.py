@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     mla_prefill_chunk_latentcache,
     decode_workspace_size, dense_block_fwd, load, make_dims, mla_decode_fullcache,
     mla_decode_fullcache_ragged, mla_decode_latentcache, mla_decode_latentcache_noalloc,
+    mla_decode_latentcache_persistent, mla_decode_latentcache_persistent_status,
     mla_decode_latentcache_ragged, mla_prefill, NOALLOC_SCRATCH_BYTES,
     mla_profile_enable, mla_profile_summary, mla_read_sweep, mla_rope_table, prefill_workspace_size, weight_shapes,
 )

@@ -81,6 +81,9 @@ def load():
                                          _I, _P, _P, _SZ, _P]
     L.mla_decode_latentcache_noalloc.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _I, _I, _P, _P,
                                                  _P, _I, _P, _P]
+    L.mla_decode_latentcache_persistent.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _I, _I, _P, _P,
+                                                    _P, _I, _P, _P, _SZ, _P]
+    L.mla_decode_latentcache_persistent_status.argtypes = [_DP, _I, _I, _P, ctypes.POINTER(_I)]
     L.mla_decode_fullcache_ragged.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _P, _I, _I, _P,
                                               _P, _P, _P, _I, _P, _P, _SZ, _P]
     L.mla_decode_latentcache_ragged.argtypes = [_DP, ctypes.POINTER(Weights), _P, _I, _P, _I, _I,
@@ -106,7 +109,8 @@ def load():
     L.mla_last_error.argtypes = []
     L.mla_last_error.restype = ctypes.c_char_p
     for name in ("mla_rope_table", "mla_prefill", "mla_decode_fullcache",
-                 "mla_decode_latentcache", "mla_decode_latentcache_noalloc", "mla_decode_fullcache_ragged",
+                 "mla_decode_latentcache", "mla_decode_latentcache_noalloc", "mla_decode_latentcache_persistent",
+                 "mla_decode_latentcache_persistent_status", "mla_decode_fullcache_ragged",
                  "mla_decode_latentcache_ragged", "mla_prefill_chunk_fullcache",
                  "mla_prefill_chunk_latentcache", "dense_block_fwd"):
         getattr(L, name).restype = _I
@@ -320,6 +324,38 @@ def mla_decode_latentcache(d: Dims, w: dict, x, P, latent_cache, rope, out=None,
                                     ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
                                     ws.numel(), _stream(dev)))
     return out
+
+
+def mla_decode_latentcache_persistent(d: Dims, w: dict, x, P, latent_cache, rope, out=None, workspace=None):
+    """mla_decode_latentcache as one persistent cooperative kernel (bf16,
+    B <= 64): same arguments and workspace."""
+    L = load()
+    dev = x.device
+    B = x.shape[0]
+    _tensor(x, "x", (B, d.d_model), d.torch_dtype, dev)
+    L_cap = latent_cache.shape[1]
+    lc = _tensor(latent_cache, "latent_cache", (B, L_cap, d.kv_lora_rank + d.qk_rope_dim), d.torch_dtype, dev)
+    wt = _weights(d, w, dev)
+    rc, rs, rows = _rope(rope, P + 1, d, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _tensor(out, "out", x.shape, d.torch_dtype, dev)
+    ws = _ws(decode_workspace_size(d, B, L_cap), dev, workspace)
+    _check(L.mla_decode_latentcache_persistent(ctypes.byref(d), ctypes.byref(wt), ctypes.c_void_p(x.data_ptr()),
+                                               B, int(P), L_cap, lc, rc, rs, rows,
+                                               ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                               ws.numel(), _stream(dev)))
+    return out
+
+
+def mla_decode_latentcache_persistent_status(d: Dims, B, L_cap, workspace):
+    """1 if a grid barrier of the last persistent step in `workspace` gave up,
+    else 0 (synchronous: call after the step's stream has finished)."""
+    L = load()
+    st = ctypes.c_int(-1)
+    _check(L.mla_decode_latentcache_persistent_status(ctypes.byref(d), int(B), int(L_cap),
+                                                      ctypes.c_void_p(workspace.data_ptr()), ctypes.byref(st)))
+    return st.value
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES of include/mla.h

@@ -273,4 +273,25 @@ struct AbsorbParams {
 };
 hipError_t absorb_q_bf16(const AbsorbParams& p, hipStream_t s);
 
+// The whole bf16 latent-cache decode step (uniform position, M <= 64 rows) as
+// one cooperative launch: down-projection weight stream, latent norms with
+// RoPE and the cache write, q up-projection weight stream, query absorption,
+// split-L attention, merge fused with W_UV, o_proj weight stream and its split
+// sum, with a grid-wide barrier between consecutive phases.  Each phase runs
+// the same device body as its own kernel in the multi-launch step, over the
+// same plans (StreamInfo of each stream, the attention's splits).
+struct PersistLatentParams {
+  GemmParams down; StreamInfo down_si; float* down_part;   // partials summed by the norms
+  LatentNormParams<bf16_t> norm;
+  GemmParams qup; StreamInfo qup_si; float* qup_part;      // partials summed by the absorption
+  AbsorbParams ab;
+  DecodeLatentParams at;
+  GemmParams oproj; StreamInfo oproj_si; float* oproj_part;
+  // barrier state: [0] arrivals, [1] generation, [2] status (1: a barrier
+  // wait gave up); 16 bytes of device memory, zeroed on the stream before the
+  // launch
+  unsigned* sync;
+};
+hipError_t decode_latent_persistent_bf16(const PersistLatentParams& p, hipStream_t s);
+
 }  // namespace mla

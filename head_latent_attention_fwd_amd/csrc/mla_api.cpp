@@ -348,6 +348,32 @@ bool gemm_stream_deferred(const char* name, const GemmParams& g, void* part, siz
   return true;
 }
 
+// Parameters of the bf16 latent norms over the down-projection's partials
+// (b.part: b.S fp32 K slices, or the weight stream's blocks when si is
+// given): rows m at position m % rowsT + pos0 (or seq_pos[m], clamped into
+// [0, pos_max]), with the optional latent-cache write.
+LatentNormParams<bf16_t> latent_norm_params(const mla_dims* d, const mla_weights* w, const ProjBufs& b, int M,
+                                            int rowsT, int pos0, const float* rc, const float* rs,
+                                            const StreamInfo* si, void* latent_cache, int L_cap,
+                                            const int* seq_pos, int pos_max) {
+  const int ql = d->q_lora_rank, kl = d->kv_lora_rank, dr = d->qk_rope_dim, N1 = ql + kl + dr;
+  LatentNormParams<bf16_t> n;
+  memset(&n, 0, sizeof n);
+  n.part = (const float*)b.part; n.nsplit = b.S;
+  n.split_stride = (long)M * N1; n.ld_part = N1;
+  n.stream = si ? 1 : 0;
+  if (si) n.si = *si;
+  n.seq_pos = seq_pos; n.pos_max = pos_max;
+  n.bias_q = (const bf16_t*)w->b_dq; n.bias_kvr = (const bf16_t*)w->b_dkvr;
+  n.M = M; n.q_lora = ql; n.kv_lora = kl; n.d_rope = dr;
+  n.g_q = (const bf16_t*)w->g_q; n.g_kv = (const bf16_t*)w->g_kv; n.eps = d->rms_eps;
+  n.cq = (bf16_t*)b.cq; n.ld_cq = ql; n.ckv = (bf16_t*)b.ckv; n.ld_ckv = kl;
+  n.kr = (bf16_t*)b.kr; n.ld_kr = dr;
+  n.rcos = rc; n.rsin = rs; n.n_pairs = dr / 2; n.rope_T = rowsT; n.rope_pos0 = pos0;
+  n.latent_cache = (bf16_t*)latent_cache; n.L_cap = L_cap;
+  return n;
+}
+
 // ---------------------------------------------------- shared launch steps
 // Down-projections, latent norms and RoPE, query up-projection (roped) and,
 // if kv is given, the kv up-projection.  Rows m = b*rowsT + t at position
@@ -392,19 +418,8 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
       g.kchunk = b.kchunk;
       LAUNCH("gemm_down", gemm_bf16(g, EPI_F32, b.cfg, st));
     }
-    LatentNormParams<bf16_t> n;
-    memset(&n, 0, sizeof n);
-    n.part = (const float*)b.part; n.nsplit = b.S;
-    n.split_stride = (long)M * N1; n.ld_part = N1;
-    n.stream = streamed ? 1 : 0; n.si = si;
-    n.seq_pos = seq_pos; n.pos_max = pos_max;
-    n.bias_q = (const bf16_t*)w->b_dq; n.bias_kvr = (const bf16_t*)w->b_dkvr;
-    n.M = M; n.q_lora = ql; n.kv_lora = kl; n.d_rope = dr;
-    n.g_q = (const bf16_t*)w->g_q; n.g_kv = (const bf16_t*)w->g_kv; n.eps = d->rms_eps;
-    n.cq = (bf16_t*)b.cq; n.ld_cq = ql; n.ckv = (bf16_t*)b.ckv; n.ld_ckv = kl;
-    n.kr = (bf16_t*)b.kr; n.ld_kr = dr;
-    n.rcos = rc; n.rsin = rs; n.n_pairs = dr / 2; n.rope_T = rowsT; n.rope_pos0 = pos0;
-    n.latent_cache = (bf16_t*)latent_cache; n.L_cap = L_cap;
+    const LatentNormParams<bf16_t> n = latent_norm_params(d, w, b, M, rowsT, pos0, rc, rs, streamed ? &si : nullptr,
+                                                         latent_cache, L_cap, seq_pos, pos_max);
     LAUNCH("latent_norm_rope", latent_norm_rope<bf16_t>(n, st));
     GemmParams q = gp_base();
     q.A = (const bf16_t*)b.cq; q.lda = ql;
@@ -638,6 +653,7 @@ struct DecodePlan {
   void* opart;      // o_proj split partials ([S2][B][d], or the stream GEMM's blocks)
   size_t opart_floats;
   int S2, kchunk2;
+  void* sync;       // 256 bytes: the persistent latent decode's barrier words
 };
 
 // Full-cache attention splits.  The kernel holds six workgroups per CU
@@ -727,6 +743,7 @@ size_t decode_layout(const mla_dims* d, int B, int L_cap, int form, void* ws, De
   }
   pl->opart = c.take(of * 4);
   pl->opart_floats = of;
+  pl->sync = c.take(256);
   return c.off + 256;
 }
 
@@ -1153,6 +1170,42 @@ static int decode_latent_check(const mla_dims* d, const mla_weights* w, const vo
   return MLA_OK;
 }
 
+// Parameters of the bf16 query absorption ([q~ | roped q^R] per head, q
+// summed from the q up-projection's weight-stream partials when qsi.G > 0)
+// and of the split-L attention with its merge (o~ W_UV into b.o).  Uniform
+// position P with `splits` workgroups per sequence, or (seq_pos) the device
+// plan over pl.nsplit workgroups.
+static void latent_attn_params(const mla_dims* d, const mla_weights* w, const DecodePlan& pl, int B, int P,
+                               const int* seq_pos, int splits, int L_cap, const void* latent_cache,
+                               const float* rc, const float* rs, const StreamInfo& qsi, AbsorbParams* abp,
+                               DecodeLatentParams* ap) {
+  const int H = d->n_heads;
+  const ProjBufs& b = pl.pb;
+  AbsorbParams& ab = *abp;
+  memset(&ab, 0, sizeof ab);
+  ab.q = (const bf16_t*)b.q;
+  ab.qpart = qsi.G > 0 ? (const float*)b.upart : nullptr; ab.qsi = qsi;
+  ab.w_ukv = (const bf16_t*)w->w_ukv; ab.qa = (bf16_t*)pl.q_abs;
+  ab.rcos = rc; ab.rsin = rs; ab.B = B; ab.H = H; ab.L = P + 1; ab.seq_pos = seq_pos;
+  // the attention's split plan, then its records: fp32 (m, l) and bf16 o~
+  int* plan = (int*)pl.apart;
+  char* recs = (char*)pl.apart + ((size_t)(3 * pl.ns_cap + 2 * B) * sizeof(int) + 255) / 256 * 256;
+  ab.plan = seq_pos ? plan : nullptr; ab.G = pl.nsplit;
+  DecodeLatentParams& a = *ap;
+  memset(&a, 0, sizeof a);
+  a.q_abs = (const bf16_t*)pl.q_abs;
+  a.cache = (const bf16_t*)latent_cache;
+  a.stats = (float*)recs;
+  a.opart = (bf16_t*)(recs + (size_t)pl.ns_cap * H * 2 * sizeof(float));
+  a.plan = ab.plan; a.splits = splits;
+  a.rcos = rc; a.rsin = rs;
+  a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.G = pl.nsplit;
+  a.scale_log2 = scale_of(d) * kLog2e;
+  a.seq_pos = seq_pos;
+  // merge of the splits fused with O_h = o~_h W_UV,h^T
+  a.w_ukv = (const bf16_t*)w->w_ukv; a.out = (bf16_t*)b.o;
+}
+
 static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
                               const int* seq_pos, int L_cap, void* latent_cache, const float* rc,
                               const float* rs, int rope_rows, void* out, void* ws, size_t ws_bytes,
@@ -1180,29 +1233,10 @@ static int decode_latent_impl(const mla_dims* d, const mla_weights* w, const voi
                            d->dtype == MLA_BF16 ? def : nullptr, seq_pos, P)))
     return r;
   if (d->dtype == MLA_BF16) {
-    // [q~ | roped q^R] per head
     AbsorbParams ab;
-    ab.q = (const bf16_t*)b.q;
-    ab.qpart = def[0].G > 0 ? (const float*)b.upart : nullptr; ab.qsi = def[0];
-    ab.w_ukv = (const bf16_t*)w->w_ukv; ab.qa = (bf16_t*)pl.q_abs;
-    ab.rcos = rc; ab.rsin = rs; ab.B = B; ab.H = H; ab.L = P + 1; ab.seq_pos = seq_pos;
-    // the attention's split plan, then its records: fp32 (m, l) and bf16 o~
-    int* plan = (int*)pl.apart;
-    char* recs = (char*)pl.apart + ((size_t)(3 * pl.ns_cap + 2 * B) * sizeof(int) + 255) / 256 * 256;
-    ab.plan = seq_pos ? plan : nullptr; ab.G = pl.nsplit;
-    LAUNCH("absorb_q", absorb_q_bf16(ab, st));
     DecodeLatentParams a;
-    a.q_abs = (const bf16_t*)pl.q_abs;
-    a.cache = (const bf16_t*)latent_cache;
-    a.stats = (float*)recs;
-    a.opart = (bf16_t*)(recs + (size_t)pl.ns_cap * H * 2 * sizeof(float));
-    a.plan = ab.plan; a.splits = splits;
-    a.rcos = rc; a.rsin = rs;
-    a.B = B; a.H = H; a.L = P + 1; a.L_cap = L_cap; a.G = pl.nsplit;
-    a.scale_log2 = scale_of(d) * kLog2e;
-    a.seq_pos = seq_pos;
-    // merge of the splits fused with O_h = o~_h W_UV,h^T
-    a.w_ukv = (const bf16_t*)w->w_ukv; a.out = (bf16_t*)b.o;
+    latent_attn_params(d, w, pl, B, P, seq_pos, splits, L_cap, latent_cache, rc, rs, def[0], &ab, &a);
+    LAUNCH("absorb_q", absorb_q_bf16(ab, st));
     LAUNCH("decode_latent", decode_latent_bf16(a, st));
   } else {
     GemmF32Params g;
@@ -1260,6 +1294,75 @@ int mla_decode_latentcache(const mla_dims* d, const mla_weights* w, const void* 
   g_err[0] = 0;
   return decode_latent_impl(d, w, x, B, P, nullptr, L_cap, latent_cache, rc, rs, rope_rows, out, ws,
                             ws_bytes, stream);
+}
+
+int mla_decode_latentcache_persistent(const mla_dims* d, const mla_weights* w, const void* x, int B, int P,
+                                      int L_cap, void* latent_cache, const float* rc, const float* rs,
+                                      int rope_rows, void* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int r = decode_latent_check(d, w, x, B, P, L_cap, latent_cache, rc, rs, rope_rows, out);
+  if (r) return r;
+  if (d->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "the persistent latent decode is bf16 only");
+  if (B > 64) return fail(MLA_ERR_UNSUPPORTED, "the persistent latent decode serves batches of up to 64 sequences");
+  if (!ws) return fail(MLA_ERR_NULL, "workspace is NULL");
+  if ((r = check_align({ws}, "workspace"))) return r;
+  DecodePlan pl;
+  const size_t need = decode_layout(d, B, L_cap, 1, nullptr, &pl);
+  if (ws_bytes < need) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  decode_layout(d, B, L_cap, 1, ws, &pl);
+  const int splits = plan_latent_splits(B, P + 1);
+  pl.nsplit = B * splits;
+  if (pl.nsplit > pl.ns_cap) return fail(MLA_ERR_HIP, "internal: split plan exceeds workspace");
+  const ProjBufs& b = pl.pb;
+  const int H = d->n_heads, dqk = d->qk_nope_dim + d->qk_rope_dim, ql = d->q_lora_rank;
+  const int N1 = ql + d->kv_lora_rank + d->qk_rope_dim, D = d->d_model, K = H * d->v_head_dim;
+  PersistLatentParams pp;
+  memset(&pp, 0, sizeof pp);
+  // the multi-launch step's products and plans (run_projections, decode_latent_impl, run_oproj)
+  GemmParams& g = pp.down;
+  g = gp_base();
+  g.A = (const bf16_t*)x; g.lda = D;
+  g.B = (const bf16_t*)w->w_dq; g.B2 = (const bf16_t*)w->w_dkvr; g.ldb = D; g.b_split = ql;
+  g.C = b.part; g.ldc = N1; g.M = B; g.N = N1; g.K = D; g.split_stride = (long)B * N1;
+  GemmParams& q = pp.qup;
+  q = gp_base();
+  q.A = (const bf16_t*)b.cq; q.lda = ql; q.B = (const bf16_t*)w->w_uqr; q.ldb = ql;
+  q.C = b.q; q.ldc = (long)H * dqk; q.M = B; q.N = H * dqk; q.K = ql;
+  GemmParams& o = pp.oproj;
+  o = gp_base();
+  o.A = (const bf16_t*)b.o; o.lda = K; o.B = (const bf16_t*)w->w_o; o.ldb = K;
+  o.C = out; o.ldc = D; o.M = B; o.N = D; o.K = K; o.bias = (const bf16_t*)w->b_o;
+  if (!b.decode || !stream_ok(g) || !stream_ok(q) || !stream_ok(o))
+    return fail(MLA_ERR_UNSUPPORTED, "the persistent latent decode needs the weight-streaming shapes of every projection");
+  pp.down_si = stream_info(B, N1, D);
+  pp.qup_si = stream_info(B, q.N, q.K);
+  pp.oproj_si = stream_info(B, D, K);
+  pp.down_part = (float*)b.part;
+  pp.qup_part = (float*)b.upart;
+  pp.oproj_part = (float*)pl.opart;
+  if (!b.upart || stream_part_floats(pp.qup_si) > b.upart_floats || stream_part_floats(pp.oproj_si) > pl.opart_floats)
+    return fail(MLA_ERR_HIP, "internal: weight-stream partial buffers too small");
+  pp.norm = latent_norm_params(d, w, b, B, 1, P, rc, rs, &pp.down_si, latent_cache, L_cap, nullptr, P);
+  latent_attn_params(d, w, pl, B, P, nullptr, splits, L_cap, latent_cache, rc, rs, pp.qup_si, &pp.ab, &pp.at);
+  pp.sync = (unsigned*)pl.sync;
+  hipStream_t st = (hipStream_t)stream;
+  LAUNCH("decode_latent_persistent", decode_latent_persistent_bf16(pp, st));
+  return MLA_OK;
+}
+
+int mla_decode_latentcache_persistent_status(const mla_dims* d, int B, int L_cap, const void* ws, int* status) {
+  g_err[0] = 0;
+  if (!d || !ws || !status) return fail(MLA_ERR_NULL, "dims, workspace or status is NULL");
+  int r = check_dims(d, false);
+  if (r) return r;
+  if (B <= 0 || L_cap <= 0) return fail(MLA_ERR_SHAPE, "B and L_cap must be positive");
+  DecodePlan pl;
+  decode_layout(d, B, L_cap, 1, const_cast<void*>(ws), &pl);
+  unsigned v = 0;
+  const hipError_t e = hipMemcpy(&v, (const unsigned*)pl.sync + 2, sizeof v, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipMemcpy: %s", hipGetErrorString(e));
+  *status = v ? 1 : 0;
+  return MLA_OK;
 }
 
 int mla_decode_latentcache_ragged(const mla_dims* d, const mla_weights* w, const void* x, int B,

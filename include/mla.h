@@ -197,6 +197,36 @@ int mla_decode_latentcache_noalloc(const mla_dims *dims, const mla_weights *w, c
                                    const float *rope_cos, const float *rope_sin, int rope_rows,
                                    void *out, void *stream);
 
+/* ---- Latent-cache decode as one persistent kernel ----
+ * The step of mla_decode_latentcache ([MP] decode mode, [KV] Why and
+ * Explanation) as a single cooperative launch: one workgroup per CU runs the
+ * down-projection, the latent norms with the cache write, the q
+ * up-projection, the query absorption, the split-L attention, the merge
+ * with W_UV and o_proj in turn, with a grid-wide barrier between phases,
+ * instead of eight kernel launches.  Same arguments, workspace size and
+ * rules as mla_decode_latentcache; the result equals it up to the latent
+ * norms' reduction order (within the bf16 tolerance, not bit for bit).
+ *   - Shapes: bf16 only, B <= 64, 64 heads and kv_lora 512 (else
+ *     MLA_ERR_UNSUPPORTED before any HIP call).
+ *   - Launch: hipLaunchCooperativeKernel, preceded by a 16-byte
+ *     hipMemsetAsync of the workspace's barrier words; a device that cannot
+ *     keep one workgroup per CU resident returns MLA_ERR_HIP.  Not for HIP
+ *     graph capture (the memset).
+ *   - A barrier wait that sees no progress for about a second gives up (the
+ *     kernel always ends) and marks the workspace; the step's output is then
+ *     undefined, and mla_decode_latentcache_persistent_status reports it. */
+int mla_decode_latentcache_persistent(const mla_dims *dims, const mla_weights *w, const void *x,
+                                      int B, int P, int L_cap, void *latent_cache,
+                                      const float *rope_cos, const float *rope_sin, int rope_rows,
+                                      void *out, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+/* Diagnostic: *status = 1 if a barrier of the last persistent step run in
+ * this workspace (same dims, B, L_cap) gave up, else 0.  Synchronous: it
+ * copies 4 bytes to the host with hipMemcpy, so call it after the step's
+ * stream has finished.  MLA_ERR_NULL / MLA_ERR_SHAPE for bad arguments. */
+int mla_decode_latentcache_persistent_status(const mla_dims *dims, int B, int L_cap,
+                                             const void *workspace, int *status);
+
 /* ---- Decode over a ragged batch (both cache forms) ----
  * As mla_decode_fullcache / mla_decode_latentcache, but sequence b's new
  * token sits at its own position positions[b] ([MP]'s decode mode per

@@ -255,3 +255,34 @@ def test_read_sweep_arguments_rejected():
     assert L.mla_read_sweep(FAKE, 0, FAKE, None) == -2
     assert L.mla_read_sweep(FAKE, 1000, FAKE, None) == -2
     assert L.mla_read_sweep(ctypes.c_void_p(0x1008), 1024, FAKE, None) == -3
+
+
+def test_persistent_latent_decode_arguments_rejected():
+    """The persistent latent decode checks as the multi-launch form does, and
+    serves bf16 batches of up to 64 sequences; every case fails before a HIP
+    call."""
+    L = _lib()
+    d = kimi()
+
+    def call(d, B=2, P=3, L_cap=16, lc=FAKE, x=FAKE, out=FAKE, ws=FAKE, wsb=1 << 40):
+        return L.mla_decode_latentcache_persistent(ctypes.byref(d), ctypes.byref(_w()), x, B, P, L_cap, lc,
+                                                   FAKE, FAKE, 16, out, ws, wsb, None)
+
+    assert call(d, lc=None) == -1
+    assert call(d, x=None) == -1
+    assert call(d, ws=None) == -1
+    assert call(d, P=16) == -2                      # P outside [0, L_cap)
+    assert call(d, B=0) == -2
+    assert call(d, B=65) == -3 and "64" in L.mla_last_error().decode()
+    assert call(tiny()) == -3 and "bf16" in L.mla_last_error().decode()
+    d2 = kimi()
+    d2.kv_lora_rank = 448
+    assert call(d2) == -3
+    assert call(d, wsb=1) == -4                     # everything else valid: workspace too small
+    odd = mla.make_dims(960, 64, 192, 512, 128, 64, 128, dtype="bf16")
+    assert call(odd) == -3                          # d_model 960: no weight-stream form (K % 128)
+    assert "weight-streaming" in L.mla_last_error().decode()
+    st = ctypes.c_int(7)
+    assert L.mla_decode_latentcache_persistent_status(ctypes.byref(d), 2, 16, FAKE, None) == -1
+    assert L.mla_decode_latentcache_persistent_status(ctypes.byref(d), 0, 16, FAKE, ctypes.byref(st)) == -2
+    assert st.value == 7

@@ -225,12 +225,12 @@ def test_decode_fullcache_kimi_full_size_sampled():
     assert_close(got, want, TOL_BF16, "decode full B=64 P=1000 sampled")
 
 
-def _decode_latent_case(od, B, P, L_cap, dt, seed, sample=None):
+def _decode_latent_case(od, B, P, L_cap, dt, seed, sample=None, fn=None):
     x, w, cc = synth.decode_latent_inputs(od, B, P, L_cap, seed, bf16=(dt == "bf16"))
     d = dims_of(mla, od, dt)
     cd = bits_to_dev(cc, dt, DEV)
-    got = mla.mla_decode_latentcache(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), P, cd,
-                                     _rope(od, P + 1))
+    got = (fn or mla.mla_decode_latentcache)(d, weights_to_dev(w, dt, DEV), to_dev(x, dt, DEV), P, cd,
+                                              _rope(od, P + 1))
     torch.cuda.synchronize()
     bs = list(range(B)) if sample is None else sample
     cf = synth.as_f32(cc[bs], dt == "bf16").astype(np.float64)
@@ -261,6 +261,55 @@ def test_decode_latentcache_kimi_full_size_sampled():
     log("[decode latent kimi] B=32 P=8192 bf16")
     got, want, *_ = _decode_latent_case(od, 32, 8192, 8193, "bf16", 1004, sample=[0, 13, 31])
     assert_close(got, want, TOL_BF16, "decode latent B=32 P=8192 sampled")
+
+
+# ---------------------------------------------- persistent latent decode
+@pytest.mark.parametrize("case", [
+    ("kimi_narrow", KIMI_NARROW, 3, 700, 701, 81, None),
+    ("kimi_narrow_P0", KIMI_NARROW, 2, 0, 3, 82, None),
+    ("kimi", ref.KIMI_K2, 5, 333, 400, 85, None),
+    ("kimi_B33", ref.KIMI_K2, 33, 70, 96, 86, [0, 16, 31, 32]),   # 64-row weight-stream tiles
+    ("kimi_B64", ref.KIMI_K2, 64, 40, 41, 87, [0, 31, 32, 63]),
+])
+def test_decode_latentcache_persistent(case):
+    """The latent-cache decode as one persistent cooperative kernel: output
+    and written cache slot against the oracle (sampled sequences for the
+    large batches), no grid barrier gave up, a second call in the same
+    workspace reproduces the output bit for bit, and the multi-launch step
+    agrees within the bf16 tolerance (only the latent norms' reduction order
+    differs)."""
+    name, od, B, P, L_cap, seed, sample = case
+    log(f"[decode latent persistent {name}] B={B} P={P} L_cap={L_cap} bf16")
+    x, w, cc = synth.decode_latent_inputs(od, B, P, L_cap, seed, bf16=True)
+    d = dims_of(mla, od, "bf16")
+    wd, xd, rope = weights_to_dev(w, "bf16", DEV), to_dev(x, "bf16", DEV), _rope(od, P + 1)
+    ws = torch.empty(mla.decode_workspace_size(d, B, L_cap), dtype=torch.uint8, device=DEV)
+    cd = bits_to_dev(cc, "bf16", DEV)
+    got = mla.mla_decode_latentcache_persistent(d, wd, xd, P, cd, rope, workspace=ws)
+    torch.cuda.synchronize()
+    assert mla.mla_decode_latentcache_persistent_status(d, B, L_cap, ws) == 0
+    bs = list(range(B)) if sample is None else sample
+    cf = synth.as_f32(cc[bs], True).astype(np.float64)
+    want, cc2 = ref.mla_decode_latentcache(od, oracle_weights(w), x[bs].astype(np.float64), P, cf)
+    assert_close(from_dev(got)[bs], want, TOL_BF16, name)
+    assert_close(from_dev(cd[bs, P]), cc2[:, P], TOL_BF16, "latent cache slot P")
+    got2 = mla.mla_decode_latentcache_persistent(d, wd, xd, P, cd, rope, workspace=ws)
+    torch.cuda.synchronize()
+    assert mla.mla_decode_latentcache_persistent_status(d, B, L_cap, ws) == 0
+    assert torch.equal(got, got2), "second persistent call differs"
+    multi = mla.mla_decode_latentcache(d, wd, xd, P, bits_to_dev(cc, "bf16", DEV), rope)
+    torch.cuda.synchronize()
+    assert_close(from_dev(got), from_dev(multi).astype(np.float64), TOL_BF16, "persistent vs multi-launch")
+
+
+def test_decode_latentcache_persistent_kimi_full_size_sampled():
+    """The latent-cache decode workload (B=32, P=8192, L=8193, bf16) through
+    the persistent kernel, oracle on sampled sequences."""
+    od = ref.KIMI_K2
+    log("[decode latent persistent kimi] B=32 P=8192 bf16")
+    got, want, *_ = _decode_latent_case(od, 32, 8192, 8193, "bf16", 1004, sample=[0, 13, 31],
+                                        fn=mla.mla_decode_latentcache_persistent)
+    assert_close(got, want, TOL_BF16, "persistent decode latent B=32 P=8192 sampled")
 
 
 # ------------------------------------------------------------ ragged decode
