@@ -287,9 +287,9 @@ struct PersistLatentParams {
   AbsorbParams ab;
   DecodeLatentParams at;
   GemmParams oproj; StreamInfo oproj_si; float* oproj_part;
-  // barrier state: [0] arrivals, [1] generation, [2] status (1: a barrier
-  // wait gave up); 16 bytes of device memory, zeroed on the stream before the
-  // launch
+  // barrier state (24 words, zeroed on the stream before the launch): [0]
+  // XCD arrivals, [1] generation, [2] status (1: a barrier wait gave up), [3]
+  // XCDs holding workgroups, [8 + x] arrivals and [16 + x] workgroups of XCD x
   unsigned* sync;
 };
 hipError_t decode_latent_persistent_bf16(const PersistLatentParams& p, hipStream_t s);

@@ -208,7 +208,7 @@ int mla_decode_latentcache_noalloc(const mla_dims *dims, const mla_weights *w, c
  * norms' reduction order (within the bf16 tolerance, not bit for bit).
  *   - Shapes: bf16 only, B <= 64, 64 heads and kv_lora 512 (else
  *     MLA_ERR_UNSUPPORTED before any HIP call).
- *   - Launch: hipLaunchCooperativeKernel, preceded by a 16-byte
+ *   - Launch: hipLaunchCooperativeKernel, preceded by a 96-byte
  *     hipMemsetAsync of the workspace's barrier words; a device that cannot
  *     keep one workgroup per CU resident returns MLA_ERR_HIP.  Not for HIP
  *     graph capture (the memset).
