@@ -78,7 +78,7 @@ typedef enum {
   MLA_OK = 0,
   MLA_ERR_NULL = -1,        /* a required pointer is NULL                     */
   MLA_ERR_SHAPE = -2,       /* a size is non-positive or inconsistent          */
-  MLA_ERR_UNSUPPORTED = -3, /* valid, but not a shape/dtype this build serves  */
+  MLA_ERR_UNSUPPORTED = -3, /* valid, but not a shape/dtype the library serves */
   MLA_ERR_WORKSPACE = -4,   /* workspace smaller than the *_workspace_size     */
   MLA_ERR_HIP = -5          /* a HIP launch failed                             */
 } mla_status;
