@@ -535,6 +535,26 @@ def test_prefill_attention_bias_kimi_T1100_sampled_rows():
     assert_close(from_dev(got)[:, rows], want, TOL_BF16, "kimi prefill with biases T=1100 sampled rows")
 
 
+def test_decode_latentcache_persistent_attention_bias():
+    """The persistent latent decode with the attention_bias biases (q_a, kv_a
+    and o_proj): the down-projection biases enter where the norm phase sums
+    the row, b_o in the final split sum."""
+    od = KIMI_NARROW
+    B, P, L_cap, seed = 3, 30, 40, 108
+    log(f"[decode bias persistent bf16] B={B} P={P}")
+    d = dims_of(mla, od, "bf16")
+    x, w, cc = synth.decode_latent_inputs(od, B, P, L_cap, seed, bf16=True)
+    w = _with_biases(w, od, seed + 1, True)
+    ws = torch.empty(mla.decode_workspace_size(d, B, L_cap), dtype=torch.uint8, device=DEV)
+    got = mla.mla_decode_latentcache_persistent(d, weights_to_dev(w, "bf16", DEV), to_dev(x, "bf16", DEV), P,
+                                                bits_to_dev(cc, "bf16", DEV), _rope(od, P + 1), workspace=ws)
+    torch.cuda.synchronize()
+    assert mla.mla_decode_latentcache_persistent_status(d, B, L_cap, ws) == 0
+    want, _ = ref.mla_decode_latentcache(od, oracle_weights(w), x.astype(np.float64), P,
+                                         synth.as_f32(cc, True).astype(np.float64))
+    assert_close(from_dev(got), want, TOL_BF16, "decode bias persistent bf16")
+
+
 @pytest.mark.parametrize("form", ["full", "latent"])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_decode_attention_bias(form, dt):
